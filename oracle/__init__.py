@@ -1,0 +1,11 @@
+"""fp64 CPU oracle for the attention forward pass.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check in __graft_entry__ and by the
+CPU-baseline leg of bench.py, never by the HIP path.  It shares no code with that path.
+"""
+from .attention import (MASKS, allowed, allowed_pair_count, attention, attention_blocked,
+                        decode_bf16, doc_index, scores)
+from .tiles import tile_class_counts, tile_table
+
+__all__ = ["MASKS", "allowed", "allowed_pair_count", "attention", "attention_blocked",
+           "decode_bf16", "doc_index", "scores", "tile_class_counts", "tile_table"]
