@@ -1,0 +1,198 @@
+"""Benchmark of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one attn_fwd call over one batch of seeded synthetic input already resident in HBM:
+the V transpose-pack kernel, the block-table kernel (masked kinds) and the forward kernel.
+W untimed steps, then exactly K timed steps bracketed by a device synchronisation on both
+sides, timed with HIP events on the stream the kernels run on.  Prints one JSON line.
+
+Default workload: causal attention, B=1, H=32, N=16384, d=128 (the configuration the
+throughput target is quoted on).  The metric counts only unmasked FLOPs: 4*d per allowed
+(query, key) pair (2d for Q K^T, 2d for P V).
+
+The "roofline" object is for the forward kernel alone: algorithmic FLOPs per launch divided by
+its average duration, measured with a HIP event pair the library records around that kernel on
+the same stream, against the published dense bf16 MFMA peak of MI355X.
+
+The "cpu_baseline" object times the fp64 CPU oracle (a plain, untuned reference) on the host
+cores on a bounded sample of the same workload, in the same unit.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
+METRIC = "attention fwd TFLOP/s (unmasked FLOPs) and % of MFMA peak, 1 MI355X"
+DEFAULT_WORKLOAD = "causal_h32_n16384_d128"
+KERNEL_SOURCES = ["exact_io_aware_21_amd/csrc/fwd.hip", "exact_io_aware_21_amd/csrc/tiles.h",
+                  "exact_io_aware_21_amd/csrc/launch.h"]
+
+
+def allowed_pairs(w, doc_offsets=None):
+    """Allowed (query, key) pairs over all batch entries and heads, in closed form."""
+    N = w.N
+    if w.mask == "none":
+        per = [N * N] * w.B
+    elif w.mask == "causal":
+        per = [N * (N + 1) // 2] * w.B
+    elif w.mask == "window":
+        W = w.window
+        m = min(W, N)
+        per = [m * (m + 1) // 2 + (N - m) * W] * w.B
+    else:
+        per = []
+        for row in doc_offsets:
+            o = [int(x) for x in row]
+            per.append(sum((o[r + 1] - o[r]) * (o[r + 1] - o[r] + 1) // 2 for r in range(len(o) - 1)))
+    return sum(per) * w.H
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per launch of the forward kernel from committed rocprofv3 counter runs,
+    or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_fwd_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s=25.0, chunk=2048):
+    """The fp64 oracle on host cores: one head, query rows in chunks of `chunk` until the head is
+    done or `budget_s` has elapsed.  Throughput in the metric's unit (unmasked TFLOP/s)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i["num_threads"] for i in threadpool_info() if i["user_api"] == "blas"]
+                      or [1])
+    except Exception:
+        threads = 1
+    q = oracle.decode_bf16(inp["q"][:1, :1])
+    k = oracle.decode_bf16(inp["k"][:1, :1])
+    v = oracle.decode_bf16(inp["v"][:1, :1])
+    offs = None if inp["doc_offsets"] is None else inp["doc_offsets"][:1]
+    slopes = inp["slopes"]
+    t0 = time.perf_counter()
+    rows_done = 0
+    pairs = 0
+    while rows_done < w.N and time.perf_counter() - t0 < budget_s:
+        rows = np.arange(rows_done, min(rows_done + chunk, w.N))
+        oracle.attention(q, k, v, float(inp["scale"]), mask=w.mask, window=w.window,
+                         softcap=float(w.softcap), slopes=slopes, doc_offsets=offs, rows=rows)
+        pairs += int(oracle.allowed(rows, np.arange(w.N), w.N, w.mask, w.window,
+                                    None if offs is None else offs[0]).sum())
+        rows_done = rows[-1] + 1
+    dt = time.perf_counter() - t0
+    return {"value": 4.0 * w.d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 oracle, head (b=0,h=0), query rows 0..{rows_done - 1} of {w.N} "
+                      f"(all keys), {dt:.1f} s wall, {pairs} allowed pairs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the forward pass here runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from exact_io_aware_21_amd import attn, inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    inp = inputs.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    o = torch.empty(w.B, w.H, w.N, w.d, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    slopes = None if inp["slopes"] is None else torch.from_numpy(inp["slopes"]).to(dev)
+    offs = None if inp["doc_offsets"] is None else torch.from_numpy(inp["doc_offsets"]).to(dev)
+    var = attn.variant_bits(w.mask, w.alibi, w.softcap > 0)
+    ws = attn.alloc_workspace(w.B, w.H, w.N, w.d, var, dev)
+    kw = dict(window=w.window, softcap=w.softcap, alibi_slopes=slopes, doc_offsets=offs,
+              workspace=ws)
+
+    for _ in range(args.warmup):
+        attn.attn_fwd(q, k, v, o, lse, inp["scale"], var, **kw)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        attn.attn_fwd(q, k, v, o, lse, inp["scale"], var, timing_events=kev[i], **kw)
+    end.record()
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / K
+    kern_ms = sum(a.elapsed_time(b) for a, b in kev) / K
+
+    flops = 4.0 * w.d * allowed_pairs(w, inp["doc_offsets"])
+    hbm_bytes = w.B * w.H * w.N * (4 * w.d * 2 + 4)  # Q, K, V read; O (bf16) and L written
+    value = flops / (step_ms * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    traffic = traffic_from_profile(w.name)
+    mfma_bound = flops / hbm_bytes > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic}
+    else:
+        gbs = hbm_bytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0, sigma^2) Q/K/V rounded to bf16)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
+                   "window": w.window, "alibi": w.alibi, "softcap": w.softcap,
+                   "unmasked_gflop": round(flops / 1e9, 3),
+                   "fwd_kernel_ms": round(kern_ms, 4)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+"""Thin Python binding of libattn.so (include/attn.h): argument marshalling only.
+
+Every step of the forward pass runs in the library's HIP kernels.  torch is used only to hold
+device memory and to name the current HIP stream.  There is no fallback: if the library is not
+built, or the device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+# variant bits and codes, as in include/attn.h
+ATTN_MASK_NONE = 0
+ATTN_MASK_CAUSAL = 1
+ATTN_MASK_SLIDING_WINDOW = 2
+ATTN_MASK_DOCUMENT = 3
+ATTN_MOD_ALIBI = 1 << 4
+ATTN_MOD_SOFTCAP = 1 << 5
+ATTN_O_BF16 = 0
+ATTN_O_F32 = 1
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = -1
+ATTN_ERR_UNSUPPORTED_DEVICE = -2
+ATTN_ERR_LAUNCH = -3
+ATTN_ERR_WORKSPACE = -4
+
+MASK_BITS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
+             "window": ATTN_MASK_SLIDING_WINDOW, "document": ATTN_MASK_DOCUMENT}
+
+EXPORTS = ("attn_fwd", "attn_workspace_size", "attn_tile_shape", "attn_block_table",
+           "attn_block_table_host", "attn_strerror", "attn_last_error")
+
+
+class attn_params(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("softcap", ctypes.c_float),
+                ("alibi_slopes", ctypes.c_void_p), ("doc_offsets", ctypes.c_void_p),
+                ("max_docs", ctypes.c_int32), ("o_dtype", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("timing_events", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code, detail):
+        self.code = code
+        super().__init__(f"{detail} (code {code})")
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               f"(or make -C exact_io_aware_21_amd/csrc)")
+        L = ctypes.CDLL(LIB_PATH)
+        c_int, c_u32, c_vp, c_f = ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_float
+        P = ctypes.POINTER(attn_params)
+        L.attn_fwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_f,
+                               c_u32, P, c_vp]
+        L.attn_fwd.restype = c_int
+        L.attn_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_u32]
+        L.attn_workspace_size.restype = ctypes.c_size_t
+        L.attn_tile_shape.argtypes = [c_int, c_u32, ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
+        L.attn_tile_shape.restype = c_int
+        L.attn_block_table.argtypes = [c_int, c_int, c_int, c_int, c_u32, P, c_vp, c_vp, c_vp, c_vp]
+        L.attn_block_table.restype = c_int
+        L.attn_block_table_host.argtypes = [c_int, c_int, c_int, c_int, c_u32, P, c_vp, c_vp, c_vp]
+        L.attn_block_table_host.restype = c_int
+        L.attn_strerror.argtypes = [c_int]
+        L.attn_strerror.restype = ctypes.c_char_p
+        L.attn_last_error.argtypes = []
+        L.attn_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != ATTN_OK:
+        L = lib()
+        raise AttnError(rc, f"{L.attn_strerror(rc).decode()}: {L.attn_last_error().decode()}")
+
+
+def variant_bits(mask="none", alibi=False, softcap=False) -> int:
+    v = MASK_BITS[mask]
+    if alibi:
+        v |= ATTN_MOD_ALIBI
+    if softcap:
+        v |= ATTN_MOD_SOFTCAP
+    return v
+
+
+def attn_tile_shape(d: int, variant: int):
+    Br, Bc = ctypes.c_int(), ctypes.c_int()
+    _check(lib().attn_tile_shape(d, variant, ctypes.byref(Br), ctypes.byref(Bc)))
+    return Br.value, Bc.value
+
+
+def attn_workspace_size(B: int, H: int, N: int, d: int, variant: int) -> int:
+    return int(lib().attn_workspace_size(B, H, N, d, variant))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_params(window=0, softcap=0.0, alibi_slopes=None, doc_offsets=None, o_dtype=ATTN_O_BF16,
+                workspace=None):
+    p = attn_params()
+    p.window = int(window)
+    p.softcap = float(softcap)
+    p.alibi_slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
+    if doc_offsets is not None:
+        p.doc_offsets = doc_offsets.data_ptr()
+        p.max_docs = doc_offsets.shape[-1] - 1
+    p.o_dtype = int(o_dtype)
+    if workspace is not None:
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    return p
+
+
+def alloc_workspace(B, H, N, d, variant, device="cuda"):
+    """A workspace tensor of the size attn_fwd needs (allocated by torch, outside any call)."""
+    import torch
+    n = attn_workspace_size(B, H, N, d, variant)
+    if n == 0:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "invalid shape for attn_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def attn_fwd(q, k, v, o, lse, scale, variant, window=0, softcap=0.0, alibi_slopes=None,
+             doc_offsets=None, workspace=None, stream=None, timing_events=None):
+    """Calls attn_fwd on torch tensors q, k, v ([B,H,N,d] bf16), o (bf16 or fp32), lse (fp32 or
+    None).  alibi_slopes: fp32 [H]; doc_offsets: int32 [B, max_docs+1]; workspace: uint8 tensor
+    of at least attn_workspace_size bytes (allocated here when None); timing_events: optional
+    pair of torch.cuda.Event(enable_timing=True) recorded around the main kernel."""
+    import torch
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{name} must be a contiguous bf16 [B,H,N,d] tensor")
+    if o.dtype not in (torch.bfloat16, torch.float32) or not o.is_contiguous() \
+            or tuple(o.shape) != (B, H, N, d):
+        raise ValueError("o must be a contiguous bf16/fp32 [B,H,N,d] tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, H, N)):
+        raise ValueError("lse must be a contiguous fp32 [B,H,N] tensor")
+    if workspace is None:
+        workspace = alloc_workspace(B, H, N, d, variant, q.device)
+    p = make_params(window, softcap, alibi_slopes, doc_offsets,
+                    ATTN_O_F32 if o.dtype == torch.float32 else ATTN_O_BF16, workspace)
+    ev = None
+    if timing_events is not None:
+        ev = (ctypes.c_void_p * 2)(timing_events[0].cuda_event, timing_events[1].cuda_event)
+        p.timing_events = ctypes.cast(ev, ctypes.c_void_p)
+    _check(lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                          float(scale), variant, ctypes.byref(p), _stream(stream)))
+    return o, lse
+
+
+def attn_block_table(B, H, N, d, variant, cls, kv_cnt, kv_list, window=0, doc_offsets=None,
+                     stream=None):
+    """Device block table into torch tensors cls (int8), kv_cnt (int32), kv_list (int32)."""
+    p = make_params(window=window, doc_offsets=doc_offsets)
+    _check(lib().attn_block_table(B, H, N, d, variant, ctypes.byref(p), _ptr(cls), _ptr(kv_cnt),
+                                  _ptr(kv_list), _stream(stream)))
+
+
+def attn_block_table_host(B, H, N, d, variant, window=0, doc_offsets=None):
+    """The same table computed on the host by the library; returns numpy arrays."""
+    import numpy as np
+    Br, Bc = attn_tile_shape(d, variant)
+    n_qt, n_kt = -(-N // Br), -(-N // Bc)
+    Bm = B if (variant & 0xF) == ATTN_MASK_DOCUMENT else 1
+    cls = np.zeros((Bm, n_qt, n_kt), dtype=np.int8)
+    cnt = np.zeros((Bm, n_qt), dtype=np.int32)
+    lst = np.zeros((Bm, n_qt, n_kt), dtype=np.int32)
+    p = attn_params()
+    p.window = int(window)
+    offs = None
+    if doc_offsets is not None:
+        offs = np.ascontiguousarray(doc_offsets, dtype=np.int32)
+        p.doc_offsets = offs.ctypes.data
+        p.max_docs = offs.shape[-1] - 1
+    _check(lib().attn_block_table_host(B, H, N, d, variant, ctypes.byref(p), cls.ctypes.data,
+                                       cnt.ctypes.data, lst.ctypes.data))
+    return cls, cnt, lst

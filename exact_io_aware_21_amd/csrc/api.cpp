@@ -1,0 +1,288 @@
+// C-ABI layer of libattn.so: argument validation, device check, workspace layout and dispatch.
+// Declarations and the contract of each entry point are in include/attn.h.
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+constexpr uint32_t kKnownBits = 0xFu | ATTN_MOD_ALIBI | ATTN_MOD_SOFTCAP;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Shape {
+  int B, H, N, d, n_qt, n_kt, Npad, Bm;
+  uint32_t kind;
+};
+
+// Validates the shape and variant bits; fills s.  No HIP call.
+int check_shape(int B, int H, int N, int d, uint32_t variant, Shape &s) {
+  if (B < 1 || H < 1 || N < 1) return fail(ATTN_ERR_INVALID_ARG, "B, H and N must be >= 1");
+  if (N > (1 << 24)) return fail(ATTN_ERR_INVALID_ARG, "N must be <= 2^24");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_INVALID_ARG, "d must be 64 or 128");
+  if (variant & ~kKnownBits) return fail(ATTN_ERR_INVALID_ARG, "unknown variant bits");
+  s.kind = variant & 0xFu;
+  if (s.kind > ATTN_MASK_DOCUMENT) return fail(ATTN_ERR_INVALID_ARG, "unknown mask kind");
+  s.B = B;
+  s.H = H;
+  s.N = N;
+  s.d = d;
+  s.n_qt = (N + attn::kBr - 1) / attn::kBr;
+  s.n_kt = (N + attn::kBc - 1) / attn::kBc;
+  s.Npad = s.n_kt * attn::kBc;
+  s.Bm = s.kind == ATTN_MASK_DOCUMENT ? B : 1;
+  if ((long long)B * H * s.n_qt >= (1ll << 31))
+    return fail(ATTN_ERR_INVALID_ARG, "B*H*ceil(N/Br) must be < 2^31");
+  return ATTN_OK;
+}
+
+// Validates the params fields the variant uses.  No HIP call.
+int check_params(const Shape &s, uint32_t variant, const attn_params *p, bool need_ws) {
+  if (!p) {
+    if (need_ws || s.kind == ATTN_MASK_SLIDING_WINDOW || s.kind == ATTN_MASK_DOCUMENT ||
+        (variant & (ATTN_MOD_ALIBI | ATTN_MOD_SOFTCAP)))
+      return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+    return ATTN_OK;
+  }
+  if (s.kind == ATTN_MASK_SLIDING_WINDOW && p->window < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "window must be >= 1");
+  if (s.kind == ATTN_MASK_DOCUMENT) {
+    if (!p->doc_offsets) return fail(ATTN_ERR_INVALID_ARG, "doc_offsets is NULL");
+    if (p->max_docs < 1) return fail(ATTN_ERR_INVALID_ARG, "max_docs must be >= 1");
+    if ((uintptr_t)p->doc_offsets % 4) return fail(ATTN_ERR_INVALID_ARG, "doc_offsets misaligned");
+  }
+  if (variant & ATTN_MOD_SOFTCAP) {
+    if (!(p->softcap > 0.f) || !std::isfinite(p->softcap))
+      return fail(ATTN_ERR_INVALID_ARG, "softcap must be finite and > 0");
+  }
+  if (variant & ATTN_MOD_ALIBI) {
+    if (!p->alibi_slopes) return fail(ATTN_ERR_INVALID_ARG, "alibi_slopes is NULL");
+    if ((uintptr_t)p->alibi_slopes % 4) return fail(ATTN_ERR_INVALID_ARG, "alibi_slopes misaligned");
+  }
+  if (p->o_dtype != ATTN_O_BF16 && p->o_dtype != ATTN_O_F32)
+    return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_O_BF16 or ATTN_O_F32");
+  return ATTN_OK;
+}
+
+struct WsLayout {
+  size_t vt, cls, cnt, list, total;
+};
+
+WsLayout ws_layout(const Shape &s) {
+  WsLayout w{};
+  size_t off = 0;
+  w.vt = off;
+  off = align256(off + (size_t)s.B * s.H * s.d * s.Npad * 2);
+  if (s.kind != ATTN_MASK_NONE) {
+    const size_t rows = (size_t)s.Bm * s.n_qt;
+    w.cls = off;
+    off = align256(off + rows * s.n_kt);
+    w.cnt = off;
+    off = align256(off + rows * 4);
+    w.list = off;
+    off = align256(off + rows * s.n_kt * 4);
+  }
+  w.total = off;
+  return w;
+}
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "no HIP device available");
+  }
+  if (dev < kMaxDevices) {
+    const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return ATTN_OK;
+    if (c == -1) return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "cannot query device %d", dev);
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+  if (!ok) return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  return ATTN_OK;
+}
+
+attn::MaskDesc mask_desc(const Shape &s, const attn_params *p) {
+  attn::MaskDesc m{};
+  m.kind = (int)s.kind;
+  m.N = s.N;
+  m.window = (p && s.kind == ATTN_MASK_SLIDING_WINDOW) ? p->window : 0;
+  m.offs = nullptr;
+  m.max_docs = (p && s.kind == ATTN_MASK_DOCUMENT) ? p->max_docs : 0;
+  return m;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    default: return "unknown error code";
+  }
+}
+
+const char *attn_last_error(void) { return g_err; }
+
+int attn_tile_shape(int d, uint32_t variant, int *Br, int *Bc) {
+  if (d != 64 && d != 128) return fail(ATTN_ERR_INVALID_ARG, "d must be 64 or 128");
+  if (variant & ~kKnownBits || (variant & 0xFu) > ATTN_MASK_DOCUMENT)
+    return fail(ATTN_ERR_INVALID_ARG, "unknown variant bits");
+  if (!Br || !Bc) return fail(ATTN_ERR_INVALID_ARG, "Br/Bc output pointer is NULL");
+  *Br = attn::kBr;
+  *Bc = attn::kBc;
+  return ATTN_OK;
+}
+
+size_t attn_workspace_size(int B, int H, int N, int d, uint32_t variant) {
+  Shape s;
+  if (check_shape(B, H, N, d, variant, s) != ATTN_OK) return 0;
+  return ws_layout(s).total;
+}
+
+int attn_block_table_host(int B, int H, int N, int d, uint32_t variant, const attn_params *params,
+                          int8_t *cls, int32_t *kv_cnt, int32_t *kv_list) {
+  Shape s;
+  int rc = check_shape(B, H, N, d, variant, s);
+  if (rc) return rc;
+  // the table depends only on the mask kind: score modifications are not validated here
+  if ((rc = check_params(s, variant & 0xFu, params, false))) return rc;
+  if (!cls || !kv_cnt || !kv_list) return fail(ATTN_ERR_INVALID_ARG, "output pointer is NULL");
+  attn::MaskDesc m = mask_desc(s, params);
+  for (int bm = 0; bm < s.Bm; ++bm) {
+    if (s.kind == ATTN_MASK_DOCUMENT) m.offs = params->doc_offsets + (size_t)bm * (m.max_docs + 1);
+    for (int qt = 0; qt < s.n_qt; ++qt) {
+      const size_t row = (size_t)bm * s.n_qt + qt;
+      kv_cnt[row] = attn::tile_row(m, qt, s.n_kt, attn::kBr, attn::kBc, cls + row * s.n_kt,
+                                   kv_list + row * s.n_kt);
+    }
+  }
+  return ATTN_OK;
+}
+
+int attn_block_table(int B, int H, int N, int d, uint32_t variant, const attn_params *params,
+                     int8_t *cls, int32_t *kv_cnt, int32_t *kv_list, void *stream) {
+  Shape s;
+  int rc = check_shape(B, H, N, d, variant, s);
+  if (rc) return rc;
+  // the table depends only on the mask kind: score modifications are not validated here
+  if ((rc = check_params(s, variant & 0xFu, params, false))) return rc;
+  if (!cls || !kv_cnt || !kv_list) return fail(ATTN_ERR_INVALID_ARG, "output pointer is NULL");
+  if (((uintptr_t)kv_cnt | (uintptr_t)kv_list) & 3u)
+    return fail(ATTN_ERR_INVALID_ARG, "kv_cnt/kv_list misaligned");
+  if ((rc = check_device())) return rc;
+  const attn::MaskDesc m = mask_desc(s, params);
+  const int32_t *offs = s.kind == ATTN_MASK_DOCUMENT ? params->doc_offsets : nullptr;
+  if (attn::launch_block_table(m, offs, s.Bm, s.n_qt, s.n_kt, cls, kv_cnt, kv_list,
+                               (hipStream_t)stream) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "block table kernel launch failed");
+  return ATTN_OK;
+}
+
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
+             int d, float scale, uint32_t variant, const attn_params *params, void *stream) {
+  Shape s;
+  int rc = check_shape(B, H, N, d, variant, s);
+  if (rc) return rc;
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (lse && ((uintptr_t)lse & 3u)) return fail(ATTN_ERR_INVALID_ARG, "lse misaligned");
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+  if ((rc = check_params(s, variant, params, true))) return rc;
+  const WsLayout wl = ws_layout(s);
+  if (!params->workspace || ((uintptr_t)params->workspace & 255u))
+    return fail(ATTN_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (params->workspace_bytes < wl.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", params->workspace_bytes,
+                wl.total);
+  if ((rc = check_device())) return rc;
+
+  const hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)params->workspace;
+  uint16_t *vt = (uint16_t *)(ws + wl.vt);
+  if (attn::launch_vt_pack((const uint16_t *)v, vt, B * H, N, s.Npad, d, st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "V transpose kernel launch failed");
+
+  attn::FwdArgs a{};
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.vt = vt;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.Npad = s.Npad;
+  a.n_qt = s.n_qt;
+  a.n_kt = s.n_kt;
+  const float log2e = 1.4426950408889634f;
+  a.c = scale * log2e;
+  if (variant & ATTN_MOD_SOFTCAP) {
+    a.cap_c1 = 2.f * scale * log2e / params->softcap;
+    a.capL = params->softcap * log2e;
+  }
+  a.slopes = (variant & ATTN_MOD_ALIBI) ? params->alibi_slopes : nullptr;
+  a.kind = (int)s.kind;
+  a.window = s.kind == ATTN_MASK_SLIDING_WINDOW ? params->window : 0;
+  a.max_docs = s.kind == ATTN_MASK_DOCUMENT ? params->max_docs : 0;
+  a.offs = s.kind == ATTN_MASK_DOCUMENT ? params->doc_offsets : nullptr;
+  if (s.kind != ATTN_MASK_NONE) {
+    a.cls = (const int8_t *)(ws + wl.cls);
+    a.cnt = (const int32_t *)(ws + wl.cnt);
+    a.list = (const int32_t *)(ws + wl.list);
+    if (attn::launch_block_table(mask_desc(s, params), a.offs, s.Bm, s.n_qt, s.n_kt,
+                                 (int8_t *)(ws + wl.cls), (int32_t *)(ws + wl.cnt),
+                                 (int32_t *)(ws + wl.list), st) != hipSuccess)
+      return fail(ATTN_ERR_LAUNCH, "block table kernel launch failed");
+  }
+  attn::FwdInstance in{};
+  in.d = d;
+  in.alibi = (variant & ATTN_MOD_ALIBI) != 0;
+  in.softcap = (variant & ATTN_MOD_SOFTCAP) != 0;
+  in.pos_scale = !in.alibi && !in.softcap && scale > 0.f;
+  in.out_f32 = params->o_dtype == ATTN_O_F32;
+  void *const *ev = params->timing_events;
+  if (ev && hipEventRecord((hipEvent_t)ev[0], st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "timing event record failed");
+  if (attn::launch_fwd(in, a, st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "forward kernel launch failed");
+  if (ev && hipEventRecord((hipEvent_t)ev[1], st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "timing event record failed");
+  return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,408 @@
+// gfx950 kernels of the FlashAttention forward pass.
+//
+// The tiled forward pass with the online softmax follows page "FlashAttention/es" (marovi.ai),
+// section "El algoritmo FlashAttention": Q is split into blocks of Br rows that stay on chip,
+// K and V are streamed block by block (Bc keys) through on-chip memory, each score block is
+// formed and reduced while the running maximum m and normaliser l are carried along, the output
+// is rescaled by e^{m_old - m_new} when the maximum moves, and at the end O is divided by l and
+// L = m + ln(l) is written.  The loop order (outer over query blocks, one workgroup each; inner
+// over key blocks) is the one the section "Variantes y sucesores" credits to the second version.
+// The N x N score matrix never leaves registers.
+//
+// gfx950 mapping (one workgroup = 4 wave64s = Br = 128 query rows, 32 per wave):
+//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K is the A operand
+//    read from LDS, Q^T the B operand held in VGPRs for the whole kernel.  In the 32x32 result
+//    each lane owns one query (lane % 32) and 16 keys, so a row maximum is an in-lane max plus a
+//    single exchange with lane ^ 32, and the running m, l live in one VGPR per lane.
+//  * K rows are stored in LDS with key bits 2 and 3 swapped.  After that permutation the 16
+//    score registers of a lane hold keys {16*(r/8) + 8*(lane/32) + r%8}, i.e. two runs of 8
+//    consecutive keys, which is exactly the B-operand layout of the P V product: P^T feeds
+//    O^T = V^T P^T straight from registers, with no LDS round trip.
+//  * V^T (d rows, keys contiguous) is the A operand of that product.  A small pack kernel
+//    writes V^T into the workspace once per call, with the d rows of each 32-block permuted so
+//    that each lane's 16 accumulator registers hold 16 consecutive output columns.
+//  * K and V^T tiles are double-buffered in LDS and prefetched into VGPRs one tile ahead; LDS
+//    rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads are bank-conflict free.
+//  * Scores are kept in base-2 units (scale * log2 e folded in), so each probability costs one
+//    v_exp_f32; L is converted back to natural log in the epilogue.
+//  * The running maximum is only moved when a tile's maximum exceeds it by more than 8 (base 2):
+//    the output and l are then rescaled, otherwise probabilities are formed against the older
+//    maximum and stay below 2^8.  Both are exact rewritings of the same sums.
+//  * Fully masked tiles never reach the kernel: it walks the per-q-tile list of non-empty tiles
+//    from the block table, and evaluates the element mask only on partial tiles.
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kTau = 8.0f;
+
+// Key permutation inside a 64-key tile: swap bits 2 and 3 (an involution).
+__device__ __forceinline__ int pi_key(int x) {
+  return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// Output-column permutation inside a 32-block of d: accumulator row i = 8a + 4h + b of the
+// 32x32 MFMA result (a = i>>3, h = (i>>2)&1, b = i&3) holds column 16h + 4a + b.
+__host__ __device__ constexpr int sigma_d(int i) {
+  return (((i >> 2) & 1) << 4) | ((i >> 3) << 2) | (i & 3);
+}
+
+// 16-byte-chunk XOR swizzle of an LDS row with NCH chunks.  Any 8 consecutive rows map a given
+// logical chunk to 8 distinct 16-byte slots within 128 bytes, and any 16 consecutive rows to 16
+// distinct slots within 256 bytes.
+template <int NCH>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (NCH >= 16)
+    return row & 15;
+  else
+    return (row & 7) ^ ((row >> 3) & 1);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------------------
+// V [BH][N][D] -> V^T [BH][D][Npad]: keys contiguous, zero beyond N, d rows permuted by sigma_d.
+template <int D>
+__global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t *__restrict__ v,
+                                                      uint16_t *__restrict__ vt, int N, int Npad) {
+  constexpr int RS = D + 2;  // padded LDS row, in elements
+  __shared__ uint16_t t[64 * RS];
+  const int kt = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const uint16_t *src = v + (size_t)bh * N * D;
+  for (int c = tid; c < 64 * D / 8; c += 256) {
+    const int key = c / (D / 8), ch = c % (D / 8);
+    const int j = kt * 64 + key;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (j < N) x = *(const u32x4 *)(src + (size_t)j * D + ch * 8);
+    uint32_t *dst = (uint32_t *)(t + key * RS + ch * 8);
+    dst[0] = x[0];
+    dst[1] = x[1];
+    dst[2] = x[2];
+    dst[3] = x[3];
+  }
+  __syncthreads();
+  uint16_t *out = vt + (size_t)bh * D * Npad + (size_t)kt * 64;
+  for (int c = tid; c < D * 8; c += 256) {
+    const int p = c >> 3, e = c & 7;
+    const int dcol = (p & ~31) | sigma_d(p & 31);
+    u32x4 x;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = t[(e * 8 + 2 * w) * RS + dcol];
+      const uint32_t hi = t[(e * 8 + 2 * w + 1) * RS + dcol];
+      x[w] = lo | (hi << 16);
+    }
+    *(u32x4 *)(out + (size_t)p * Npad + e * 8) = x;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// One thread per (table row bm, q-tile qt).
+__global__ __launch_bounds__(256) void block_table_kernel(MaskDesc m, const int32_t *offs_all,
+                                                          int Bm, int n_qt, int n_kt, int8_t *cls,
+                                                          int32_t *cnt, int32_t *list) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= Bm * n_qt) return;
+  const int bm = idx / n_qt, qt = idx - bm * n_qt;
+  MaskDesc mm = m;
+  if (offs_all) mm.offs = offs_all + (size_t)bm * (m.max_docs + 1);
+  cnt[idx] = tile_row(mm, qt, n_kt, kBr, kBc, cls + (size_t)idx * n_kt, list + (size_t)idx * n_kt);
+}
+
+// ---------------------------------------------------------------------------------------------
+template <int D, bool ALIBI, bool SOFTCAP, bool POS, bool OUTF32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
+    FwdArgs a) {
+  constexpr int KCH = D / 8;             // 16-byte chunks per K row
+  constexpr int VCH = kBc / 8;           // 16-byte chunks per V^T row
+  constexpr int KLD = kBc * KCH / 256;   // K chunks loaded per thread per tile
+  constexpr int VLD = D * VCH / 256;     // V^T chunks loaded per thread per tile
+  constexpr int NKS = D / 16;            // k-steps of the score product
+  constexpr int NDB = D / 32;            // 32-column blocks of O
+  static_assert(kBr == 128 && kBc == 64, "kernel is written for 128 x 64 tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBc * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * kBc];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+
+  // Workgroups are dispatched round-robin over the 8 XCDs; remap so that consecutive logical
+  // blocks (the q-tiles of one head, sharing K and V) run on the same XCD and its L2.
+  const int nblk = gridDim.x, w = blockIdx.x;
+  const int n8 = nblk & ~7;
+  const int lb = (w < n8) ? (w & 7) * (n8 >> 3) + (w >> 3) : w;
+  const int bh = lb / a.n_qt;
+  const int qx = lb - bh * a.n_qt;
+  // Masked kinds have longer key lists for later q-tiles: start those first.
+  const int qt = (a.kind != kMaskNone) ? a.n_qt - 1 - qx : qx;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int N = a.N;
+
+  const int qrow = qt * kBr + wave * 32 + l32;
+  const bool q_ok = qrow < N;
+  const MaskDesc md{a.kind, N, a.window, a.offs ? a.offs + (size_t)b * (a.max_docs + 1) : nullptr,
+                    a.max_docs};
+  int lo = 1, hi = 0;  // empty interval for rows beyond N
+  if (q_ok) {
+    lo = row_lo(md, qrow);
+    hi = row_hi(md, qrow);
+  }
+
+  // Q^T fragments (B operand): lane holds Q[qrow][16*ks + 8*hf .. +7].
+  bf16x8 qf[NKS];
+  {
+    const uint16_t *qp = a.q + ((size_t)bh * N + (q_ok ? qrow : 0)) * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (q_ok) x = *(const u32x4 *)(qp + ks * 16);
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  int cnt;
+  const int32_t *lst = nullptr;
+  const int8_t *clsr = nullptr;
+  if (a.cls) {
+    const int bm = (a.kind == kMaskDocument) ? b : 0;
+    const size_t row = (size_t)bm * a.n_qt + qt;
+    cnt = a.cnt[row];
+    lst = a.list + row * a.n_kt;
+    clsr = a.cls + row * a.n_kt;
+  } else {
+    cnt = a.n_kt;
+  }
+  const bool q_full = (qt + 1) * kBr <= N;
+
+  const uint16_t *kbase = a.k + (size_t)bh * N * D;
+  const uint16_t *vbase = a.vt + (size_t)bh * D * a.Npad;
+  u32x4 kpre[KLD], vpre[VLD];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < KLD; ++u) {
+      const int c = tid + 256 * u, key = c / KCH, ch = c % KCH, j = kt * kBc + key;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (j < N) x = *(const u32x4 *)(kbase + (size_t)j * D + ch * 8);
+      kpre[u] = x;
+    }
+#pragma unroll
+    for (int u = 0; u < VLD; ++u) {
+      const int c = tid + 256 * u, row = c / VCH, ch = c % VCH;
+      vpre[u] = *(const u32x4 *)(vbase + (size_t)row * a.Npad + (size_t)kt * kBc + ch * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < KLD; ++u) {
+      const int c = tid + 256 * u, key = c / KCH, ch = c % KCH, r = pi_key(key);
+      *(u32x4 *)&sK[buf][r * D + ((ch ^ swz<KCH>(r)) * 8)] = kpre[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VLD; ++u) {
+      const int c = tid + 256 * u, row = c / VCH, ch = c % VCH;
+      *(u32x4 *)&sV[buf][row * kBc + ((ch ^ swz<VCH>(row)) * 8)] = vpre[u];
+    }
+  };
+
+  const float c = a.c;
+  const float slopeL = ALIBI ? a.slopes[h] * 1.4426950408889634f : 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+
+  if (cnt > 0) {
+    gload(lst ? lst[0] : 0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < cnt; ++it) {
+    const int buf = it & 1;
+    const int kt = lst ? lst[it] : it;
+    const int cls = clsr ? clsr[kt] : ((q_full && (kt + 1) * kBc <= N) ? 2 : 1);
+    const bool has_next = it + 1 < cnt;
+    if (has_next) gload(lst ? lst[it + 1] : it + 1);
+
+    // S^T = K Q^T, two 32-key blocks.
+    f32x16 s[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      s[blk] = f32x16{};
+      const int row = blk * 32 + l32;
+      const uint16_t *kr = &sK[buf][row * D];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 kf = *(const bf16x8 *)(kr + (((2 * ks + hf) ^ swz<KCH>(row)) * 8));
+        s[blk] = mfma32(kf, qf[ks], s[blk]);
+      }
+    }
+
+    // Score modifications, in base-2 units.  Register r of block blk is key
+    // kt*Bc + 32*blk + 16*(r/8) + 8*hf + r%8.
+    const int kb = kt * kBc + 8 * hf;
+    if constexpr (!POS) {
+      const float abase = ALIBI ? slopeL * (float)(kb - qrow) : 0.f;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = s[blk][r];
+          float t;
+          if constexpr (SOFTCAP) {
+            const float e = __builtin_amdgcn_exp2f(x * a.cap_c1);
+            t = fmaf(-2.f * a.capL, __builtin_amdgcn_rcpf(1.f + e), a.capL);
+          } else {
+            t = x * c;
+          }
+          if constexpr (ALIBI) t += fmaf(slopeL, (float)(32 * blk + 16 * (r >> 3) + (r & 7)), abase);
+          s[blk][r] = t;
+        }
+      }
+    }
+    if (cls == 1) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = kb + 32 * blk + 16 * (r >> 3) + (r & 7);
+          if (j < lo || j > hi) s[blk][r] = -INFINITY;
+        }
+      }
+    }
+
+    // Tile row maximum (in-lane over 32 keys, then across the lane pair sharing the query).
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_tile = POS ? mx * c : mx;
+
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kTau)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+    // Probabilities (fp32 for l, bf16 for the product), four 8-key groups.
+    bf16x8 pb[4];
+    float psum[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x8 pv;
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = s[g >> 1][8 * (g & 1) + e];
+        const float p = POS ? __builtin_amdgcn_exp2f(fmaf(x, c, -m_use))
+                            : __builtin_amdgcn_exp2f(x - m_use);
+        pv[e] = p;
+        acc += p;
+      }
+      psum[g] = acc;
+      pb[g] = __builtin_convertvector(pv, bf16x8);
+    }
+    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+
+    // O^T += V^T P^T over the 4 groups of 16 keys.
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int row = db * 32 + l32;
+      const uint16_t *vr = &sV[buf][row * kBc];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 vf = *(const bf16x8 *)(vr + (((2 * kk + hf) ^ swz<VCH>(row)) * 8));
+        oacc[db] = mfma32(vf, pb[kk], oacc[db]);
+      }
+    }
+
+    if (has_next) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: O = O / l, L = (m + log2 l) * ln 2.
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (q_ok) {
+    const size_t obase = ((size_t)bh * N + qrow) * D + 16 * hf;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const f32x16 o = oacc[db] * inv;
+      if constexpr (OUTF32) {
+        float *op = (float *)a.o + obase + 32 * db;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *(f32x4 *)(op + 4 * i) = f32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+      } else {
+        uint16_t *op = (uint16_t *)a.o + obase + 32 * db;
+        const f32x8 o0 = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+        const f32x8 o1 = {o[8], o[9], o[10], o[11], o[12], o[13], o[14], o[15]};
+        *(bf16x8 *)op = __builtin_convertvector(o0, bf16x8);
+        *(bf16x8 *)(op + 8) = __builtin_convertvector(o1, bf16x8);
+      }
+    }
+    if (a.lse && hf == 0)
+      a.lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, bool ALIBI, bool SOFTCAP, bool POS>
+hipError_t launch_out(bool out_f32, const FwdArgs &a, dim3 grid, hipStream_t s) {
+  if (out_f32)
+    fwd_kernel<D, ALIBI, SOFTCAP, POS, true><<<grid, 256, 0, s>>>(a);
+  else
+    fwd_kernel<D, ALIBI, SOFTCAP, POS, false><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdInstance &in, const FwdArgs &a, dim3 grid, hipStream_t s) {
+  if (in.alibi && in.softcap) return launch_out<D, true, true, false>(in.out_f32, a, grid, s);
+  if (in.alibi) return launch_out<D, true, false, false>(in.out_f32, a, grid, s);
+  if (in.softcap) return launch_out<D, false, true, false>(in.out_f32, a, grid, s);
+  if (in.pos_scale) return launch_out<D, false, false, true>(in.out_f32, a, grid, s);
+  return launch_out<D, false, false, false>(in.out_f32, a, grid, s);
+}
+
+}  // namespace
+
+hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Npad, int d,
+                          hipStream_t stream) {
+  dim3 grid(Npad / 64, BH);
+  if (d == 128)
+    vt_pack_kernel<128><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
+  else
+    vt_pack_kernel<64><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_table(MaskDesc m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,
+                              int8_t *cls, int32_t *cnt, int32_t *list, hipStream_t stream) {
+  const int n = Bm * n_qt;
+  block_table_kernel<<<(n + 255) / 256, 256, 0, stream>>>(m, offs_all, Bm, n_qt, n_kt, cls, cnt,
+                                                          list);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdInstance &in, const FwdArgs &a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.n_qt * (unsigned)(a.B * a.H));
+  if (in.d == 128) return launch_d<128>(in, a, grid, stream);
+  return launch_d<64>(in, a, grid, stream);
+}
+
+}  // namespace attn

@@ -1,0 +1,44 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the kernels (fwd.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tiles.h"
+
+namespace attn {
+
+struct FwdArgs {
+  const uint16_t *q;   // bf16 [BH][N][D]
+  const uint16_t *k;   // bf16 [BH][N][D]
+  const uint16_t *vt;  // bf16 [BH][D][Npad], key-contiguous, d rows permuted (see fwd.hip)
+  void *o;             // bf16 or fp32 [BH][N][D]
+  float *lse;          // fp32 [BH][N] or null
+  int B, H, N, Npad, n_qt, n_kt;
+  float c;       // scale * log2(e): scores are kept in base-2 units
+  float cap_c1;  // soft-cap: 2 * scale * log2(e) / cap
+  float capL;    // soft-cap: cap * log2(e)
+  const float *slopes;  // ALiBi slopes [H] or null
+  int kind, window, max_docs;
+  const int32_t *offs;   // [B][max_docs + 1] or null
+  const int8_t *cls;     // block table (null for the unmasked kind)
+  const int32_t *cnt;
+  const int32_t *list;
+};
+
+// Variant switches that select a kernel instance.
+struct FwdInstance {
+  int d;         // 64 or 128
+  bool alibi;
+  bool softcap;
+  bool pos_scale;  // scale > 0 and no score modification: max is taken on raw scores
+  bool out_f32;
+};
+
+hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Npad, int d,
+                          hipStream_t stream);
+hipError_t launch_block_table(MaskDesc m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,
+                              int8_t *cls, int32_t *cnt, int32_t *list, hipStream_t stream);
+hipError_t launch_fwd(const FwdInstance &inst, const FwdArgs &a, hipStream_t stream);
+
+}  // namespace attn

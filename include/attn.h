@@ -1,0 +1,138 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) FlashAttention forward library (libattn.so).
+ *
+ * What it computes.  For every batch entry b and head h, with Q, K, V in R^{N x d}:
+ *     O = softmax(S) V,   S_ij = modified score of query i and key j,
+ *     L_i = m_i + ln(l_i) (natural log), m_i = max_j S_ij, l_i = sum_j e^{S_ij - m_i},
+ * exactly as the plain definition (page "FlashAttention/es", sections "Por qué la atención
+ * estándar es lenta" and "El truco del softmax en línea"), evaluated by the tiled forward pass
+ * with the online softmax (same page, section "El algoritmo FlashAttention"): Q is walked in
+ * blocks of Br rows, K and V in blocks of Bc rows, the running maximum and normaliser stay in
+ * registers, and no N x N matrix is ever written to device memory.  L is the log-sum-exp the
+ * same section writes beside O.
+ *
+ * Score modifications and masks (named on page "El FlexAttention de PyTorch con
+ * FlashAttention-4 ...", opening paragraph), applied in this order to s = scale * q_i . k_j:
+ *     ATTN_MOD_SOFTCAP : s <- cap * tanh(s / cap)
+ *     ATTN_MOD_ALIBI   : s <- s - slope[h] * (i - j)
+ *     mask             : disallowed pairs get s = -inf
+ * with the mask kind (low 4 bits of `variant`):
+ *     ATTN_MASK_NONE            every key
+ *     ATTN_MASK_CAUSAL          j <= i
+ *     ATTN_MASK_SLIDING_WINDOW  i - window < j <= i
+ *     ATTN_MASK_DOCUMENT        j <= i and doc(i) == doc(j), doc(x) = r with off[r] <= x < off[r+1]
+ * Tiles of Br x Bc scores with no allowed pair are skipped entirely (block sparsity, page
+ * "El FlexAttention ...", section "Limitaciones actuales"): a per-tile class table is built on
+ * the device from the variant (see attn_block_table) and the kernel walks only non-empty tiles.
+ *
+ * Memory.  Every pointer is caller-owned device memory unless stated otherwise.  The library
+ * allocates nothing on any call and keeps no per-call state; the only state it keeps is a
+ * per-device cache of the architecture check.  All launches are asynchronous on `stream`
+ * (a hipStream_t, NULL = the default stream); a kernel fault surfaces at the caller's next
+ * synchronisation.  Entry points are reentrant; calls that share a workspace must not overlap.
+ *
+ * Errors.  Every entry point returns an int (ATTN_OK or a negative code) and never throws.
+ * All arguments are validated before any HIP call.  attn_strerror(code) names a code;
+ * attn_last_error() returns a thread-local message naming the offending argument.
+ * A device that is not gfx950 gives ATTN_ERR_UNSUPPORTED_DEVICE: there is no fallback path.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* variant bits */
+enum {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_CAUSAL = 1,
+  ATTN_MASK_SLIDING_WINDOW = 2,
+  ATTN_MASK_DOCUMENT = 3, /* mask kind: bits 0-3 */
+  ATTN_MOD_ALIBI = 1u << 4,
+  ATTN_MOD_SOFTCAP = 1u << 5
+};
+
+/* return codes */
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1,        /* a pointer, size, alignment or variant field is invalid */
+  ATTN_ERR_UNSUPPORTED_DEVICE = -2, /* no HIP device, or the current device is not gfx950 */
+  ATTN_ERR_LAUNCH = -3,             /* a kernel launch was rejected by the runtime */
+  ATTN_ERR_WORKSPACE = -4           /* workspace missing, misaligned or smaller than needed */
+};
+
+/* output dtype of O */
+enum { ATTN_O_BF16 = 0, ATTN_O_F32 = 1 };
+
+typedef struct {
+  int32_t window;              /* SLIDING_WINDOW: W >= 1; key j allowed iff i - W < j <= i */
+  float softcap;               /* SOFTCAP: cap, finite and > 0 */
+  const float *alibi_slopes;   /* ALIBI: device, H floats, finite; slope of head h */
+  const int32_t *doc_offsets;  /* DOCUMENT: device, [B][max_docs + 1] int32, per batch entry
+                                  0 = off[0] < off[1] < ... < off[n] = N, then padded with N.
+                                  Contents are not validated: invalid offsets give unspecified
+                                  values in O and L but no out-of-bounds access. */
+  int32_t max_docs;            /* DOCUMENT: >= 1, row length of doc_offsets minus one */
+  int32_t o_dtype;             /* ATTN_O_BF16 (default) or ATTN_O_F32 */
+  void *workspace;             /* device, 256-byte aligned, >= attn_workspace_size() bytes */
+  size_t workspace_bytes;
+  void *const *timing_events;  /* optional instrumentation: NULL, or two caller-created
+                                  hipEvent_t recorded on `stream` right before and right after
+                                  the main forward kernel (not the transpose or table kernels) */
+} attn_params;
+
+/*
+ * attn_fwd -- the forward pass.
+ *   q, k, v : device, bf16, [B][H][N][d] row-major (d contiguous), 16-byte aligned.
+ *   o       : device, [B][H][N][d], bf16 or fp32 per params->o_dtype, 16-byte aligned.
+ *   lse     : device, fp32 [B][H][N], the natural-log L; NULL skips it.
+ *   B, H, N : >= 1, N <= 2^24, B*H*ceil(N/Br) < 2^31.
+ *   d       : 64 or 128.
+ *   scale   : finite (1/sqrt(d) for the standard scaling).
+ *   variant : one mask kind, optionally OR-ed with ATTN_MOD_ALIBI and/or ATTN_MOD_SOFTCAP.
+ *   params  : required (it carries the workspace).
+ * A query row with no allowed key (impossible for the masks above with valid arguments) gets
+ * O = 0 and L = -inf.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
+             int d, float scale, uint32_t variant, const attn_params *params, void *stream);
+
+/* Bytes of workspace attn_fwd needs for this shape and variant (0 on invalid arguments).
+   It holds a key-transposed copy of V and the block table. */
+size_t attn_workspace_size(int B, int H, int N, int d, uint32_t variant);
+
+/* Tile shape (Br query rows x Bc keys) the forward kernel uses for (d, variant); the block table
+   is defined on this shape.  Returns ATTN_OK or ATTN_ERR_INVALID_ARG. */
+int attn_tile_shape(int d, uint32_t variant, int *Br, int *Bc);
+
+/*
+ * attn_block_table -- the per-tile class table attn_fwd builds and walks, written to caller
+ * buffers (device).  With (Br, Bc) = attn_tile_shape(d, variant), n_qt = ceil(N/Br),
+ * n_kt = ceil(N/Bc), Bm = B for ATTN_MASK_DOCUMENT and 1 otherwise:
+ *   cls[Bm][n_qt][n_kt]     int8 : 0 no allowed in-range pair, 2 all Br*Bc pairs in range and
+ *                                  allowed, 1 otherwise;
+ *   kv_cnt[Bm][n_qt]        int32: number of tiles with class != 0 in the row;
+ *   kv_list[Bm][n_qt][n_kt] int32: their kt in ascending order, then zeros.
+ * H is unused (the mask does not depend on the head) but validated like attn_fwd's.
+ * params may be NULL for NONE/CAUSAL; its workspace fields are ignored.
+ */
+int attn_block_table(int B, int H, int N, int d, uint32_t variant, const attn_params *params,
+                     int8_t *cls, int32_t *kv_cnt, int32_t *kv_list, void *stream);
+
+/* Same table computed on the host by the same closed-form tile predicates the device uses.
+   Here params->doc_offsets and the three outputs are HOST pointers.  No HIP call is made. */
+int attn_block_table_host(int B, int H, int N, int d, uint32_t variant, const attn_params *params,
+                          int8_t *cls, int32_t *kv_cnt, int32_t *kv_list);
+
+const char *attn_strerror(int code);
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

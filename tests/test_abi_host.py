@@ -1,0 +1,189 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared symbol, validates its
+arguments before any HIP call, and its host-compiled tile predicates reproduce the oracle's
+brute-force block table bit for bit.  No compute call reaches a GPU here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_io_aware_21_amd import attn, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = attn.lib()
+    names = declared_functions()
+    assert set(names) == set(attn.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror_and_tile_shape():
+    L = attn.lib()
+    assert L.attn_strerror(0) == b"ok"
+    for code in (-1, -2, -3, -4):
+        assert L.attn_strerror(code) != b"unknown error code"
+    assert attn.attn_tile_shape(128, attn.ATTN_MASK_CAUSAL) == (128, 64)
+    assert attn.attn_tile_shape(64, attn.ATTN_MASK_DOCUMENT | attn.ATTN_MOD_SOFTCAP) == (128, 64)
+    with pytest.raises(attn.AttnError):
+        attn.attn_tile_shape(96, 0)
+    with pytest.raises(attn.AttnError):
+        attn.attn_tile_shape(64, 1 << 7)
+
+
+def test_workspace_size():
+    # V^T (B*H*d*Npad bf16) plus, for masked kinds, the table; each part 256-byte aligned.
+    al = lambda x: (x + 255) // 256 * 256
+    assert attn.attn_workspace_size(1, 1, 256, 64, 0) == al(1 * 64 * 256 * 2)
+    B, H, N, d = 2, 3, 1000, 128
+    npad = 16 * 64
+    rows = 8  # ceil(1000/128)
+    exp = al(B * H * d * npad * 2) + al(rows * 16) + al(rows * 4) + al(rows * 16 * 4)
+    assert attn.attn_workspace_size(B, H, N, d, attn.ATTN_MASK_CAUSAL) == exp
+    rows_doc = B * rows
+    exp_doc = al(B * H * d * npad * 2) + al(rows_doc * 16) + al(rows_doc * 4) + al(rows_doc * 64)
+    assert attn.attn_workspace_size(B, H, N, d, attn.ATTN_MASK_DOCUMENT) == exp_doc
+    assert attn.attn_workspace_size(1, 1, 0, 64, 0) == 0
+    assert attn.attn_workspace_size(1, 1, 16, 80, 0) == 0
+
+
+def _call_fwd(q=16, k=16, v=16, o=16, lse=None, B=1, H=1, N=64, d=64, scale=0.125, variant=0,
+              params="default"):
+    L = attn.lib()
+    p = attn.attn_params()
+    p.workspace = 256
+    p.workspace_bytes = 1 << 40
+    p.window = 4
+    p.softcap = 30.0
+    p.alibi_slopes = 4096
+    p.doc_offsets = 4096
+    p.max_docs = 2
+    pp = ctypes.byref(p) if params == "default" else params
+    return L.attn_fwd(q, k, v, o, lse, B, H, N, d, scale, variant, pp, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, attn.ATTN_ERR_INVALID_ARG),
+    ({"o": None}, attn.ATTN_ERR_INVALID_ARG),
+    ({"k": 8}, attn.ATTN_ERR_INVALID_ARG),  # misaligned
+    ({"lse": 2}, attn.ATTN_ERR_INVALID_ARG),
+    ({"N": 0}, attn.ATTN_ERR_INVALID_ARG),
+    ({"B": -1}, attn.ATTN_ERR_INVALID_ARG),
+    ({"N": (1 << 24) + 1}, attn.ATTN_ERR_INVALID_ARG),
+    ({"d": 32}, attn.ATTN_ERR_INVALID_ARG),
+    ({"scale": float("inf")}, attn.ATTN_ERR_INVALID_ARG),
+    ({"scale": float("nan")}, attn.ATTN_ERR_INVALID_ARG),
+    ({"variant": 4}, attn.ATTN_ERR_INVALID_ARG),
+    ({"variant": 1 << 8}, attn.ATTN_ERR_INVALID_ARG),
+    ({"params": None}, attn.ATTN_ERR_INVALID_ARG),
+    ({"B": 40000, "H": 40000, "N": 1000}, attn.ATTN_ERR_INVALID_ARG),
+])
+def test_fwd_rejects_invalid_arguments(kw, code):
+    assert _call_fwd(**kw) == code
+    assert attn.lib().attn_last_error() != b""
+
+
+def test_fwd_rejects_bad_params():
+    L = attn.lib()
+
+    def call(variant, **fields):
+        p = attn.attn_params()
+        p.workspace, p.workspace_bytes = 256, 1 << 40
+        p.window, p.softcap, p.alibi_slopes, p.doc_offsets, p.max_docs = 4, 30.0, 4096, 4096, 2
+        for f, val in fields.items():
+            setattr(p, f, val)
+        return L.attn_fwd(16, 16, 16, 16, None, 1, 1, 64, 64, 0.125, variant, ctypes.byref(p), None)
+
+    E, W = attn.ATTN_ERR_INVALID_ARG, attn.ATTN_ERR_WORKSPACE
+    assert call(attn.ATTN_MASK_SLIDING_WINDOW, window=0) == E
+    assert call(attn.ATTN_MASK_DOCUMENT, doc_offsets=None) == E
+    assert call(attn.ATTN_MASK_DOCUMENT, max_docs=0) == E
+    assert call(attn.ATTN_MOD_SOFTCAP, softcap=0.0) == E
+    assert call(attn.ATTN_MOD_SOFTCAP, softcap=float("inf")) == E
+    assert call(attn.ATTN_MOD_ALIBI, alibi_slopes=None) == E
+    assert call(0, o_dtype=2) == E
+    assert call(0, workspace=None) == W
+    assert call(0, workspace=128) == W  # not 256-byte aligned
+    assert call(0, workspace_bytes=100) == W
+
+
+def test_block_table_rejects_invalid_arguments():
+    L = attn.lib()
+    assert L.attn_block_table(1, 1, 64, 64, 1, None, None, 16, 16, None) == attn.ATTN_ERR_INVALID_ARG
+    assert L.attn_block_table(1, 1, 64, 64, 3, None, 16, 16, 16, None) == attn.ATTN_ERR_INVALID_ARG
+    assert L.attn_block_table(1, 1, 64, 64, 1, None, 16, 18, 16, None) == attn.ATTN_ERR_INVALID_ARG
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_present(), reason="only meaningful on a host without a GPU")
+def test_valid_call_without_gpu_reports_unsupported_device():
+    # All arguments valid: validation passes, then the device check fails (no GPU here).
+    assert _call_fwd() == attn.ATTN_ERR_UNSUPPORTED_DEVICE
+
+
+# --- host-compiled closed-form table vs the oracle's brute force ----------------------------
+TABLE_CASES = [
+    (1, 64, "none", 0), (17, 64, "none", 0), (300, 128, "none", 0),
+    (1, 64, "causal", 0), (100, 64, "causal", 0), (255, 128, "causal", 0), (1000, 64, "causal", 0),
+    (2048, 128, "causal", 0),
+    (1, 64, "window", 1), (200, 64, "window", 1), (300, 64, "window", 63), (300, 64, "window", 64),
+    (300, 64, "window", 65), (1000, 128, "window", 128), (1000, 128, "window", 5000),
+    (8192, 128, "window", 1024),
+]
+
+
+@pytest.mark.parametrize("N,d,mask,W", TABLE_CASES)
+def test_host_table_matches_oracle(N, d, mask, W):
+    v = attn.variant_bits(mask)
+    Br, Bc = attn.attn_tile_shape(d, v)
+    ours = attn.attn_block_table_host(1, 1, N, d, v, window=W)
+    ref = oracle.tile_table(N, Br, Bc, mask, W)
+    for a, b in zip(ours, ref):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_host_table_document_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    B = 3
+    N = int(rng.integers(1, 700))
+    lens = []
+    for b in range(B):
+        lo, hi = [(1, 1), (1, 40), (100, 300)][(seed + b) % 3]
+        lens.append(inputs.draw_doc_lengths(N, lo, hi, (seed, b)))
+    off = inputs.doc_offsets(lens, N)
+    v = attn.variant_bits("document")
+    Br, Bc = attn.attn_tile_shape(64, v)
+    ours = attn.attn_block_table_host(B, 2, N, 64, v, doc_offsets=off)
+    ref = oracle.tile_table(N, Br, Bc, "document", 0, off)
+    for a, b in zip(ours, ref):
+        assert np.array_equal(a, b)
+
+
+def test_host_table_document_workload():
+    w = inputs.WORKLOADS["doc_softcap30_h16_n16384_d64"]
+    off = inputs.make_inputs(w, with_qkv=False)["doc_offsets"]
+    v = attn.variant_bits("document", softcap=True)
+    Br, Bc = attn.attn_tile_shape(w.d, v)
+    ours = attn.attn_block_table_host(w.B, w.H, w.N, w.d, v, doc_offsets=off)
+    ref = oracle.tile_table(w.N, Br, Bc, "document", 0, off)
+    for a, b in zip(ours, ref):
+        assert np.array_equal(a, b)

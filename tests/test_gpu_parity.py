@@ -1,0 +1,287 @@
+"""GPU parity of the HIP forward pass (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances (from the stated targets for bf16 inputs): max|O - O_ref| <= 1e-2 and
+max|L - L_ref| <= 1e-3.  A bf16 store of O alone can exceed 1e-2 once |O| >= 4 (half an ulp
+there is 0.0156), so the 1e-2 bound is applied to the kernel's arithmetic, read out with an fp32
+O; the bf16 output of the same kernel must then equal the round-to-nearest-even bf16 of that fp32
+output bit for bit, and must lie within 1e-2 plus half a bf16 ulp of O_ref.  The integer block
+table must match the oracle's brute force exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_21_amd import attn, inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_O, TOL_L = 1e-2, 1e-3
+DEV = "cuda:0"
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def run_gpu(inp, w, out_f32, workspace=None, q_override=None, v_override=None):
+    B, H, N, d = w.B, w.H, w.N, w.d
+    q = dev_bf16(inp["q"] if q_override is None else q_override)
+    k = dev_bf16(inp["k"])
+    v = dev_bf16(inp["v"] if v_override is None else v_override)
+    o = torch.full((B, H, N, d), float("nan"), device=DEV,
+                   dtype=torch.float32 if out_f32 else torch.bfloat16)
+    lse = torch.full((B, H, N), float("nan"), device=DEV, dtype=torch.float32)
+    slopes = None if inp["slopes"] is None else torch.from_numpy(inp["slopes"]).to(DEV)
+    offs = None if inp["doc_offsets"] is None else torch.from_numpy(inp["doc_offsets"]).to(DEV)
+    var = attn.variant_bits(w.mask, w.alibi, w.softcap > 0)
+    print(f"[gpu] {w.name} B={B} H={H} N={N} d={d} var={var} out_f32={out_f32}", flush=True)
+    attn.attn_fwd(q, k, v, o, lse, inp["scale"], var, window=w.window, softcap=w.softcap,
+                  alibi_slopes=slopes, doc_offsets=offs, workspace=workspace)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def oracle_ref(inp, w, rows=None, heads=None, q_override=None, v_override=None):
+    q = oracle.decode_bf16(inp["q"] if q_override is None else q_override)
+    k = oracle.decode_bf16(inp["k"])
+    v = oracle.decode_bf16(inp["v"] if v_override is None else v_override)
+    return oracle.attention(q, k, v, float(inp["scale"]), mask=w.mask, window=w.window,
+                            softcap=float(w.softcap), slopes=inp["slopes"],
+                            doc_offsets=inp["doc_offsets"], rows=rows, heads=heads)
+
+
+def bf16_half_ulp(x):
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.maximum(ax, 1e-30)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 0.0)  # bf16 has 8 significant bits
+
+
+def check(w, inp, o32, lse32, o16, lse16, rows=None, heads=None):
+    """Compares the GPU outputs (torch, full arrays) with the oracle on the given rows/heads."""
+    Oref, Lref = oracle_ref(inp, w, rows, heads)
+    if heads is None:
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    rows = np.arange(w.N) if rows is None else np.asarray(rows)
+    o32 = o32.cpu().numpy()
+    l32 = lse32.cpu().numpy()
+    o16f = o16.float().cpu().numpy()
+    l16 = lse16.cpu().numpy()
+    # the bf16 output is the round-to-nearest-even of the fp32 output (same arithmetic)
+    o32_rne = torch.from_numpy(o32).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(o16f, o32_rne), "bf16 O differs from RNE of the fp32 O"
+    assert np.array_equal(l16, l32)
+    worst = np.zeros(4)
+    for b, h in heads:
+        ref = Oref[b, h]
+        e32 = np.abs(o32[b, h, rows] - ref)
+        eL = np.abs(l32[b, h, rows] - Lref[b, h])
+        e16 = np.abs(o16f[b, h, rows] - ref)
+        floor = np.abs(torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).double().numpy()
+                       - ref)
+        assert np.all(np.isfinite(o32[b, h, rows])) and np.all(np.isfinite(l32[b, h, rows]))
+        assert e32.max() <= TOL_O, f"{w.name} b={b} h={h}: max|O32-Oref|={e32.max():.3e}"
+        assert eL.max() <= TOL_L, f"{w.name} b={b} h={h}: max|L-Lref|={eL.max():.3e}"
+        assert np.all(e16 <= TOL_O + bf16_half_ulp(ref)), \
+            f"{w.name} b={b} h={h}: bf16 O beyond 1e-2 + half ulp (max {e16.max():.3e})"
+        worst = np.maximum(worst, [e32.max(), eL.max(), e16.max(), floor.max()])
+    print(f"[parity] {w.name}: max|O32-Oref|={worst[0]:.3e} max|L-Lref|={worst[1]:.3e} "
+          f"max|O16-Oref|={worst[2]:.3e} (bf16 rounding floor {worst[3]:.3e})", flush=True)
+    return worst
+
+
+# --- small and edge shapes: every row and head against the oracle -------------------------
+SMALL = [
+    # (name, B, H, N, d, mask, window, alibi, softcap, sigma)
+    ("n1_none_d64", 1, 2, 1, 64, "none", 0, False, 0.0, 1.0),
+    ("n17_none_d128", 2, 1, 17, 128, "none", 0, False, 0.0, 1.0),
+    ("n100_causal_d64", 1, 3, 100, 64, "causal", 0, False, 0.0, 1.0),
+    ("n255_causal_d128", 2, 2, 255, 128, "causal", 0, False, 0.0, 1.0),
+    ("n256_none_d64", 1, 1, 256, 64, "none", 0, False, 0.0, 1.0),
+    ("n300_none_d128", 1, 2, 300, 128, "none", 0, False, 0.0, 2.0),
+    ("n1000_causal_d128", 1, 2, 1000, 128, "causal", 0, False, 0.0, 1.0),
+    ("n1000_causal_d64_sig3", 1, 1, 1000, 64, "causal", 0, False, 0.0, 3.0),
+    ("w1_d64", 1, 2, 200, 64, "window", 1, False, 0.0, 1.0),
+    ("w63_d128", 1, 2, 300, 128, "window", 63, False, 0.0, 1.0),
+    ("w64_d64", 1, 2, 300, 64, "window", 64, False, 0.0, 1.0),
+    ("w65_d128", 1, 2, 300, 128, "window", 65, True, 0.0, 1.0),
+    ("w_ge_n_d64", 1, 2, 300, 64, "window", 303, True, 0.0, 1.0),
+    ("w100_alibi_d128", 2, 4, 700, 128, "window", 100, True, 0.0, 1.0),
+    ("causal_alibi_d64", 1, 8, 400, 64, "causal", 0, True, 0.0, 1.0),
+    ("none_alibi_d128", 1, 2, 200, 128, "none", 0, True, 0.0, 1.0),
+    ("causal_softcap_d128", 1, 2, 333, 128, "causal", 0, False, 5.0, 3.0),
+    ("none_softcap_alibi_d64", 1, 2, 150, 64, "none", 0, True, 2.0, 2.0),
+    ("doc_softcap_d64", 2, 2, 900, 64, "document", 0, False, 30.0, 2.0),
+    ("doc_d128", 3, 1, 500, 128, "document", 0, False, 0.0, 1.0),
+]
+
+
+def small_inputs(name, B, H, N, d, mask, window, alibi, softcap, sigma, seed):
+    w = inputs.Workload(name, B=B, H=H, N=N, d=d, sigma=sigma, mask=mask, window=window,
+                        alibi=alibi, softcap=softcap, seed=seed)
+    if mask == "document":
+        w = inputs.Workload(name, B=B, H=H, N=N, d=d, sigma=sigma, mask=mask, window=window,
+                            alibi=alibi, softcap=softcap, seed=seed, doc_len_range=(1, 130))
+    return w, inputs.make_inputs(w)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shapes(case):
+    w, inp = small_inputs(*case, seed=1000 + SMALL.index(case))
+    o32, l32 = run_gpu(inp, w, out_f32=True)
+    o16, l16 = run_gpu(inp, w, out_f32=False)
+    check(w, inp, o32, l32, o16, l16)
+
+
+def test_document_length_one_docs():
+    # every token its own document: each row attends to itself only, O = v, L = s_ii
+    B, H, N, d = 1, 2, 130, 64
+    w = inputs.Workload("doc_len1", B=B, H=H, N=N, d=d, mask="document", seed=77)
+    inp = inputs.make_inputs(w)
+    inp["doc_offsets"] = np.arange(N + 1, dtype=np.int32)[None]
+    o32, l32 = run_gpu(inp, w, out_f32=True)
+    o16, l16 = run_gpu(inp, w, out_f32=False)
+    check(w, inp, o32, l32, o16, l16)
+    v = oracle.decode_bf16(inp["v"])
+    assert np.max(np.abs(o32.cpu().numpy() - v)) <= 1e-6
+
+
+# --- the five workloads at full size, sampled rows -----------------------------------------
+def sample_rows(w, inp, rng):
+    N = w.N
+    rows = {0, 1, 2, 31, 32, 63, 64, 127, 128, 129, N // 2, N - 129, N - 128, N - 2, N - 1}
+    if inp["doc_offsets"] is not None:
+        for o in inp["doc_offsets"][0][1:-1]:
+            rows.update({int(o) - 1, int(o), int(o) + 1})
+    rows.update(int(x) for x in rng.integers(0, N, 24))
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+_cache = {}
+
+
+def workload_inputs(name):
+    if name not in _cache:
+        _cache.clear()
+        _cache[name] = inputs.make_inputs(inputs.WORKLOADS[name])
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", inputs.WORKLOAD_ORDER)
+def test_workload_full_size(name):
+    w = inputs.WORKLOADS[name]
+    inp = workload_inputs(name)
+    rng = np.random.default_rng(5)
+    rows = sample_rows(w, inp, rng)
+    heads = sorted({(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))})
+    o16, l16 = run_gpu(inp, w, out_f32=False)  # the launch the benchmark times
+    o32, l32 = run_gpu(inp, w, out_f32=True)
+    check(w, inp, o32, l32, o16, l16, rows=rows, heads=heads)
+
+
+@pytest.mark.parametrize("name", ["causal_b4h16_n2048_d128", "window1024_alibi_b2h32_n8192_d128",
+                                  "doc_softcap30_h16_n16384_d64", "causal_h32_n16384_d128"])
+def test_workload_zero_q_closed_form_all_rows(name):
+    # With Q = 0 every score is 0 (before ALiBi), so for every row of every head:
+    # L_i = ln n_i (or the ALiBi geometric sum) and O_i = the (weighted) mean of the allowed v_j.
+    w = inputs.WORKLOADS[name]
+    inp = workload_inputs(name)
+    q0 = np.zeros_like(inp["q"])
+    o32, l32 = run_gpu(inp, w, out_f32=True, q_override=q0)
+    o32 = o32.cpu().numpy()
+    l32 = l32.cpu().numpy()
+    N = w.N
+    i = np.arange(N)
+    if w.mask == "causal":
+        start = np.zeros(N, dtype=np.int64)
+    elif w.mask == "window":
+        start = np.maximum(0, i - w.window + 1)
+    else:
+        off = inp["doc_offsets"][0]
+        start = off[np.searchsorted(off, i, side="right") - 1]
+    n = i - start + 1
+    if not w.alibi:
+        assert np.max(np.abs(l32 - np.log(n))) <= TOL_L
+        v = oracle.decode_bf16(inp["v"])
+        for b in range(w.B):
+            for h in (0, w.H - 1):
+                cs = np.concatenate([np.zeros((1, w.d)), np.cumsum(v[b, h], axis=0)])
+                mean = (cs[i + 1] - cs[start]) / n[:, None]
+                assert np.max(np.abs(o32[b, h] - mean)) <= TOL_O
+    else:
+        for h in range(w.H):
+            a = float(inp["slopes"][h])
+            Z = -np.expm1(-a * n) / -np.expm1(-a)
+            assert np.max(np.abs(l32[:, h] - np.log(Z))) <= TOL_L, h
+
+
+# --- block table on the device: bit-exact against the brute force --------------------------
+TABLE_GPU = [
+    ("causal", 16384, 128, 0, None), ("causal", 2048, 128, 0, None), ("window", 8192, 128, 1024, None),
+    ("causal", 1000, 64, 0, None), ("window", 300, 64, 65, None), ("window", 300, 64, 1, None),
+    ("document", 16384, 64, 0, "doc_softcap30_h16_n16384_d64"), ("none", 300, 128, 0, None),
+]
+
+
+@pytest.mark.parametrize("mask,N,d,W,wl", TABLE_GPU)
+def test_block_table_gpu_matches_oracle(mask, N, d, W, wl):
+    off = None
+    B = 1
+    if mask == "document":
+        off = inputs.make_inputs(inputs.WORKLOADS[wl], with_qkv=False)["doc_offsets"]
+        B = off.shape[0]
+    v = attn.variant_bits(mask)
+    Br, Bc = attn.attn_tile_shape(d, v)
+    ref = oracle.tile_table(N, Br, Bc, mask, W, off)
+    cls = torch.full(ref[0].shape, -7, dtype=torch.int8, device=DEV)
+    cnt = torch.full(ref[1].shape, -7, dtype=torch.int32, device=DEV)
+    lst = torch.full(ref[2].shape, -7, dtype=torch.int32, device=DEV)
+    attn.attn_block_table(B, 1, N, d, v, cls, cnt, lst, window=W,
+                          doc_offsets=None if off is None else torch.from_numpy(off).to(DEV))
+    torch.cuda.synchronize()
+    for got, exp in zip((cls, cnt, lst), ref):
+        assert np.array_equal(got.cpu().numpy(), exp)
+
+
+# --- run-to-run determinism, no allocation, constant V ------------------------------------
+def test_deterministic_and_no_allocation():
+    w = inputs.WORKLOADS["causal_b4h16_n2048_d128"]
+    inp = workload_inputs(w.name)
+    var = attn.variant_bits(w.mask)
+    ws = attn.alloc_workspace(w.B, w.H, w.N, w.d, var)
+    o1, l1 = run_gpu(inp, w, out_f32=False, workspace=ws)
+    o1, l1 = o1.clone(), l1.clone()
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    attn.attn_fwd(q, k, v, o2, l2, inp["scale"], var, workspace=ws)
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    assert free0 == free1
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_constant_v():
+    w = inputs.Workload("constv", B=1, H=2, N=1000, d=128, mask="causal", seed=9, sigma=2.0)
+    inp = inputs.make_inputs(w)
+    c = inputs.f32_to_bf16_bits(np.random.default_rng(1).standard_normal((1, 2, 1, 128))
+                                .astype(np.float32))
+    vconst = np.broadcast_to(c, inp["v"].shape).copy()
+    o32, _ = run_gpu(inp, w, out_f32=True, v_override=vconst)
+    cv = inputs.bf16_bits_to_f32(c).astype(np.float64)
+    # P is rounded to bf16 for the product while l sums fp32 P: relative error ~ 2^-9
+    assert np.max(np.abs(o32.cpu().numpy() - cv)) <= 4e-3 * max(1.0, np.abs(cv).max())
+
+
+def test_gpu_rejects_bad_arguments():
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device=DEV)
+    o = torch.zeros_like(q)
+    with pytest.raises(attn.AttnError) as e:
+        attn.attn_fwd(q, q, q, o, None, 0.125, attn.ATTN_MASK_SLIDING_WINDOW, window=0)
+    assert e.value.code == attn.ATTN_ERR_INVALID_ARG
+    small_ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(attn.AttnError) as e:
+        attn.attn_fwd(q, q, q, o, None, 0.125, 0, workspace=small_ws)
+    assert e.value.code == attn.ATTN_ERR_WORKSPACE
