@@ -77,9 +77,37 @@ def traffic_from_profile(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, budget_s=25.0, chunk=2048):
-    """The fp64 oracle on host cores: one head, query rows in chunks of `chunk` until the head is
-    done or `budget_s` has elapsed.  Throughput in the metric's unit (unmasked TFLOP/s)."""
+def _pmc_avg(path, counter, kernel_prefix):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and r["Kernel_Name"].startswith(kernel_prefix)]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernel {kernel_prefix!r} in {path}")
+    return sum(vals) / len(vals)
+
+
+def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes):
+    """Turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) into HBM bytes per
+    launch of the forward kernel.  Each counter is scaled by the factor that makes it read the
+    known byte count of the microbenchmark's plain copy kernel (copy_bytes read and written)."""
+    fwd = "void attn::(anonymous namespace)::fwd_kernel"
+    copy = "copy_kernel"
+    f_scale = copy_bytes / (_pmc_avg(copy_fetch_csv, "FETCH_SIZE", copy) * 1024)
+    w_scale = copy_bytes / (_pmc_avg(copy_write_csv, "WRITE_SIZE", copy) * 1024)
+    rd = _pmc_avg(fetch_csv, "FETCH_SIZE", fwd) * 1024 * f_scale
+    wr = _pmc_avg(write_csv, "WRITE_SIZE", fwd) * 1024 * w_scale
+    rec = {"workload": workload, "kernel": "fwd_kernel", "source_sha256": kernel_source_hash(),
+           "fetch_scale": f_scale, "write_scale": w_scale, "read_bytes_per_launch": rd,
+           "write_bytes_per_launch": wr, "hbm_bytes_per_launch": rd + wr}
+    path = os.path.join(ROOT, "profiles", f"traffic_fwd_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def cpu_baseline(w, inp, budget_s=20.0, chunk=2048):
+    """The fp64 oracle on host cores, over whole heads in order (query rows in chunks of `chunk`)
+    until `budget_s` has elapsed.  Throughput in the metric's unit (unmasked TFLOP/s)."""
     import numpy as np
     import oracle
     try:
@@ -88,26 +116,33 @@ def cpu_baseline(w, inp, budget_s=25.0, chunk=2048):
                       or [1])
     except Exception:
         threads = 1
-    q = oracle.decode_bf16(inp["q"][:1, :1])
-    k = oracle.decode_bf16(inp["k"][:1, :1])
-    v = oracle.decode_bf16(inp["v"][:1, :1])
-    offs = None if inp["doc_offsets"] is None else inp["doc_offsets"][:1]
-    slopes = inp["slopes"]
+    cols = np.arange(w.N)
     t0 = time.perf_counter()
-    rows_done = 0
     pairs = 0
-    while rows_done < w.N and time.perf_counter() - t0 < budget_s:
-        rows = np.arange(rows_done, min(rows_done + chunk, w.N))
-        oracle.attention(q, k, v, float(inp["scale"]), mask=w.mask, window=w.window,
-                         softcap=float(w.softcap), slopes=slopes, doc_offsets=offs, rows=rows)
-        pairs += int(oracle.allowed(rows, np.arange(w.N), w.N, w.mask, w.window,
-                                    None if offs is None else offs[0]).sum())
-        rows_done = rows[-1] + 1
+    rows_done = 0
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    for b, h in heads:
+        q = oracle.decode_bf16(inp["q"][b:b + 1, h:h + 1])
+        k = oracle.decode_bf16(inp["k"][b:b + 1, h:h + 1])
+        v = oracle.decode_bf16(inp["v"][b:b + 1, h:h + 1])
+        offs = None if inp["doc_offsets"] is None else inp["doc_offsets"][b:b + 1]
+        slopes = None if inp["slopes"] is None else inp["slopes"][h:h + 1]
+        for r0 in range(0, w.N, chunk):
+            rows = np.arange(r0, min(r0 + chunk, w.N))
+            oracle.attention(q, k, v, float(inp["scale"]), mask=w.mask, window=w.window,
+                             softcap=float(w.softcap), slopes=slopes, doc_offsets=offs,
+                             rows=rows)
+            pairs += int(oracle.allowed(rows, cols, w.N, w.mask, w.window,
+                                        None if offs is None else offs[0]).sum())
+            rows_done += rows.size
+        if time.perf_counter() - t0 >= budget_s:
+            break
     dt = time.perf_counter() - t0
     return {"value": 4.0 * w.d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"fp64 oracle, head (b=0,h=0), query rows 0..{rows_done - 1} of {w.N} "
-                      f"(all keys), {dt:.1f} s wall, {pairs} allowed pairs"}
+            "sample": f"fp64 oracle on {rows_done // w.N} whole head(s) of {w.name} "
+                      f"({rows_done} query rows x {w.N} keys, {pairs} allowed pairs), "
+                      f"{dt:.1f} s wall"}
 
 
 def main():
@@ -117,7 +152,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH",
+                                                    "COPY_WRITE"),
+                    help="write profiles/traffic_fwd_<workload>.json from rocprofv3 counter CSVs")
     args = ap.parse_args()
+    if args.traffic:
+        write_traffic(args.workload, *args.traffic, copy_bytes=float(1 << 30))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the forward pass here runs on a single MI355X)", file=sys.stderr)
@@ -153,6 +194,9 @@ def main():
     K = args.steps
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
+    for a, b in kev:  # torch creates the underlying hipEvent on the first record
+        a.record()
+        b.record()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()

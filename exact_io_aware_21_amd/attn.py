@@ -145,7 +145,8 @@ def attn_fwd(q, k, v, o, lse, scale, variant, window=0, softcap=0.0, alibi_slope
     """Calls attn_fwd on torch tensors q, k, v ([B,H,N,d] bf16), o (bf16 or fp32), lse (fp32 or
     None).  alibi_slopes: fp32 [H]; doc_offsets: int32 [B, max_docs+1]; workspace: uint8 tensor
     of at least attn_workspace_size bytes (allocated here when None); timing_events: optional
-    pair of torch.cuda.Event(enable_timing=True) recorded around the main kernel."""
+    pair of torch.cuda.Event(enable_timing=True), each recorded once beforehand (torch creates
+    the underlying event on its first record), recorded again around the main kernel."""
     import torch
     B, H, N, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -163,6 +164,8 @@ def attn_fwd(q, k, v, o, lse, scale, variant, window=0, softcap=0.0, alibi_slope
                     ATTN_O_F32 if o.dtype == torch.float32 else ATTN_O_BF16, workspace)
     ev = None
     if timing_events is not None:
+        if not (timing_events[0].cuda_event and timing_events[1].cuda_event):
+            raise ValueError("timing events must have been recorded once before use")
         ev = (ctypes.c_void_p * 2)(timing_events[0].cuda_event, timing_events[1].cuda_event)
         p.timing_events = ctypes.cast(ev, ctypes.c_void_p)
     _check(lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,

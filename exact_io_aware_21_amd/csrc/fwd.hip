@@ -21,8 +21,15 @@
 //  * V^T (d rows, keys contiguous) is the A operand of that product.  A small pack kernel
 //    writes V^T into the workspace once per call, with the d rows of each 32-block permuted so
 //    that each lane's 16 accumulator registers hold 16 consecutive output columns.
-//  * K and V^T tiles are double-buffered in LDS and prefetched into VGPRs one tile ahead; LDS
-//    rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads are bank-conflict free.
+//  * The P V product runs on fp16 operands (v_mfma_f32_32x32x16_f16, the same rate as bf16):
+//    bf16 V converts to fp16 exactly inside the pack kernel, and P <= 2^8 (see below) keeps
+//    11 significant bits instead of bf16's 8.  With bf16 P the rounding of a dominant
+//    probability alone moves O by up to 2^-9 |v|, which exceeds 1e-2 for |v| near 8.
+//    Q K^T stays on bf16 operands, which are the exact input values.
+//  * K and V^T tiles are double-buffered in LDS and prefetched into VGPRs one tile ahead.  Each
+//    LDS row is padded by 16 bytes, so the 8 (or 16) lanes of one ds_read_b128 phase, which read
+//    the same column of 8 (16) consecutive rows, hit distinct banks, while every operand address
+//    stays lane base + compile-time offset (no per-read address arithmetic).
 //  * Scores are kept in base-2 units (scale * log2 e folded in), so each probability costs one
 //    v_exp_f32; L is converted back to natural log in the epilogue.
 //  * The running maximum is only moved when a tile's maximum exceeds it by more than 8 (base 2):
@@ -36,6 +43,7 @@ namespace attn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -55,23 +63,34 @@ __host__ __device__ constexpr int sigma_d(int i) {
   return (((i >> 2) & 1) << 4) | ((i >> 3) << 2) | (i & 3);
 }
 
-// 16-byte-chunk XOR swizzle of an LDS row with NCH chunks.  Any 8 consecutive rows map a given
-// logical chunk to 8 distinct 16-byte slots within 128 bytes, and any 16 consecutive rows to 16
-// distinct slots within 256 bytes.
-template <int NCH>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (NCH >= 16)
-    return row & 15;
-  else
-    return (row & 7) ^ ((row >> 3) & 1);
-}
+// LDS row pitch (elements) for a row of `len` 2-byte elements: 16 bytes of padding.  With a
+// 256-, 128- or 144-byte row (len 128 or 64), rows r = 0..15 start at 16 distinct 16-byte bank
+// slots modulo 256 bytes (and r = 0..7 at 8 distinct slots modulo 128 bytes).
+constexpr int pitch(int len) { return len + 8; }
+
+// Marks a wave-uniform branch body as having a side effect so the compiler keeps the branch
+// instead of speculating the body into straight-line selects (the element mask and the output
+// rescale are rare and must cost nothing when skipped).
+__device__ __forceinline__ void keep_branch() { __asm__ volatile("" ::); }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// bf16 bits -> fp16 bits; exact for |x| in [2^-14, 65504], saturating beyond (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_to_f16_bits(uint32_t b) {
+  float f = __uint_as_float(b << 16);
+  if (fabsf(f) > 65504.f) f = copysignf(65504.f, f);
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 // ---------------------------------------------------------------------------------------------
-// V [BH][N][D] -> V^T [BH][D][Npad]: keys contiguous, zero beyond N, d rows permuted by sigma_d.
+// V [BH][N][D] bf16 -> V^T [BH][D][Npad] fp16: keys contiguous, zero beyond N, d rows permuted
+// by sigma_d.
 template <int D>
 __global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t *__restrict__ v,
                                                       uint16_t *__restrict__ vt, int N, int Npad) {
@@ -98,8 +117,8 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t *__restrict
     u32x4 x;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = t[(e * 8 + 2 * w) * RS + dcol];
-      const uint32_t hi = t[(e * 8 + 2 * w + 1) * RS + dcol];
+      const uint32_t lo = bf16_to_f16_bits(t[(e * 8 + 2 * w) * RS + dcol]);
+      const uint32_t hi = bf16_to_f16_bits(t[(e * 8 + 2 * w + 1) * RS + dcol]);
       x[w] = lo | (hi << 16);
     }
     *(u32x4 *)(out + (size_t)p * Npad + e * 8) = x;
@@ -107,16 +126,40 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t *__restrict
 }
 
 // ---------------------------------------------------------------------------------------------
-// One thread per (table row bm, q-tile qt).
+// One workgroup per table row (bm, qt): 256 tiles are classified at a time and the non-empty
+// ones compacted in ascending kt with a wave ballot plus a 4-entry LDS prefix.
 __global__ __launch_bounds__(256) void block_table_kernel(MaskDesc m, const int32_t *offs_all,
-                                                          int Bm, int n_qt, int n_kt, int8_t *cls,
+                                                          int n_qt, int n_kt, int8_t *cls,
                                                           int32_t *cnt, int32_t *list) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= Bm * n_qt) return;
-  const int bm = idx / n_qt, qt = idx - bm * n_qt;
+  __shared__ int wave_tot[4];
+  const int row = blockIdx.x;
+  const int bm = row / n_qt, qt = row - bm * n_qt;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   MaskDesc mm = m;
   if (offs_all) mm.offs = offs_all + (size_t)bm * (m.max_docs + 1);
-  cnt[idx] = tile_row(mm, qt, n_kt, kBr, kBc, cls + (size_t)idx * n_kt, list + (size_t)idx * n_kt);
+  int8_t *crow = cls + (size_t)row * n_kt;
+  int32_t *lrow = list + (size_t)row * n_kt;
+  int base = 0;
+  for (int c0 = 0; c0 < n_kt; c0 += 256) {
+    const int kt = c0 + tid;
+    const int k = kt < n_kt ? tile_class(mm, qt, kt, kBr, kBc) : 0;
+    if (kt < n_kt) crow[kt] = (int8_t)k;
+    const uint64_t bal = __ballot(k != 0);
+    const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_tot[wave] = __popcll(bal);
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      woff += w < wave ? wave_tot[w] : 0;
+      tot += wave_tot[w];
+    }
+    if (k) lrow[base + woff + pre] = kt;
+    base += tot;
+    __syncthreads();
+  }
+  for (int kt = base + tid; kt < n_kt; kt += 256) lrow[kt] = 0;
+  if (tid == 0) cnt[row] = base;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -129,9 +172,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int VLD = D * VCH / 256;     // V^T chunks loaded per thread per tile
   constexpr int NKS = D / 16;            // k-steps of the score product
   constexpr int NDB = D / 32;            // 32-column blocks of O
+  constexpr int KP = pitch(D);           // LDS pitch of a K row (keys x D)
+  constexpr int VP = pitch(kBc);         // LDS pitch of a V^T row (D x keys)
   static_assert(kBr == 128 && kBc == 64, "kernel is written for 128 x 64 tiles");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBc * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * kBc];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBc * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VP];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
 
@@ -203,13 +248,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < KLD; ++u) {
-      const int c = tid + 256 * u, key = c / KCH, ch = c % KCH, r = pi_key(key);
-      *(u32x4 *)&sK[buf][r * D + ((ch ^ swz<KCH>(r)) * 8)] = kpre[u];
+      const int c = tid + 256 * u, key = c / KCH, ch = c % KCH;
+      *(u32x4 *)&sK[buf][pi_key(key) * KP + ch * 8] = kpre[u];
     }
 #pragma unroll
     for (int u = 0; u < VLD; ++u) {
       const int c = tid + 256 * u, row = c / VCH, ch = c % VCH;
-      *(u32x4 *)&sV[buf][row * kBc + ((ch ^ swz<VCH>(row)) * 8)] = vpre[u];
+      *(u32x4 *)&sV[buf][row * VP + ch * 8] = vpre[u];
     }
   };
 
@@ -238,11 +283,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       s[blk] = f32x16{};
-      const int row = blk * 32 + l32;
-      const uint16_t *kr = &sK[buf][row * D];
+      const uint16_t *kr = &sK[buf][(blk * 32 + l32) * KP + hf * 8];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kf = *(const bf16x8 *)(kr + (((2 * ks + hf) ^ swz<KCH>(row)) * 8));
+        const bf16x8 kf = *(const bf16x8 *)(kr + ks * 16);
         s[blk] = mfma32(kf, qf[ks], s[blk]);
       }
     }
@@ -270,6 +314,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     if (cls == 1) {
+      keep_branch();
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
@@ -290,6 +335,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float m_tile = POS ? mx * c : mx;
 
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kTau)) {
+      keep_branch();
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -299,8 +345,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-    // Probabilities (fp32 for l, bf16 for the product), four 8-key groups.
-    bf16x8 pb[4];
+    // Probabilities (fp32 for l, fp16 for the product), four 8-key groups.
+    f16x8 pb[4];
     float psum[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -315,18 +361,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         acc += p;
       }
       psum[g] = acc;
-      pb[g] = __builtin_convertvector(pv, bf16x8);
+      pb[g] = __builtin_convertvector(pv, f16x8);
     }
     l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
 
     // O^T += V^T P^T over the 4 groups of 16 keys.
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int row = db * 32 + l32;
-      const uint16_t *vr = &sV[buf][row * kBc];
+      const uint16_t *vr = &sV[buf][(db * 32 + l32) * VP + hf * 8];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 vf = *(const bf16x8 *)(vr + (((2 * kk + hf) ^ swz<VCH>(row)) * 8));
+        const f16x8 vf = *(const f16x8 *)(vr + kk * 16);
         oacc[db] = mfma32(vf, pb[kk], oacc[db]);
       }
     }
@@ -393,9 +438,7 @@ hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Np
 
 hipError_t launch_block_table(MaskDesc m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,
                               int8_t *cls, int32_t *cnt, int32_t *list, hipStream_t stream) {
-  const int n = Bm * n_qt;
-  block_table_kernel<<<(n + 255) / 256, 256, 0, stream>>>(m, offs_all, Bm, n_qt, n_kt, cls, cnt,
-                                                          list);
+  block_table_kernel<<<Bm * n_qt, 256, 0, stream>>>(m, offs_all, n_qt, n_kt, cls, cnt, list);
   return hipGetLastError();
 }
 

@@ -97,6 +97,9 @@ typedef struct {
  *   params  : required (it carries the workspace).
  * A query row with no allowed key (impossible for the masks above with valid arguments) gets
  * O = 0 and L = -inf.
+ * Precision: Q K^T is formed from the bf16 inputs with fp32 accumulation; probabilities and V
+ * enter the P V product as fp16 (V converted exactly for |v| in [2^-14, 65504]; larger
+ * magnitudes saturate to +-65504), accumulated in fp32; l is summed from fp32 probabilities.
  */
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
              int d, float scale, uint32_t variant, const attn_params *params, void *stream);
