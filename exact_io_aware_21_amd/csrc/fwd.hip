@@ -9,7 +9,8 @@
 // over key blocks) is the one the section "Variantes y sucesores" credits to the second version.
 // The N x N score matrix never leaves registers.
 //
-// gfx950 mapping (one workgroup = 4 wave64s = Br = 128 query rows, 32 per wave):
+// gfx950 mapping (one workgroup = 8 wave64s = Br = 256 query rows, 32 per wave; the two waves
+// on each SIMD alternate between matrix-core and vector phases, see fwd_kernel):
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K is the A operand
 //    read from LDS, Q^T the B operand held in VGPRs for the whole kernel.  In the 32x32 result
 //    each lane owns one query (lane % 32) and 16 keys, so a row maximum is an in-lane max plus a
@@ -26,7 +27,7 @@
 //    11 significant bits instead of bf16's 8.  With bf16 P the rounding of a dominant
 //    probability alone moves O by up to 2^-9 |v|, which exceeds 1e-2 for |v| near 8.
 //    Q K^T stays on bf16 operands, which are the exact input values.
-//  * K and V^T tiles are double-buffered in LDS and prefetched into VGPRs one tile ahead.  Each
+//  * K and V^T tiles are double-buffered in LDS and prefetched into VGPRs two phases ahead.  Each
 //    LDS row is padded by 16 bytes, so the 8 (or 16) lanes of one ds_read_b128 phase, which read
 //    the same column of 8 (16) consecutive rows, hit distinct banks, while every operand address
 //    stays lane base + compile-time offset (no per-read address arithmetic).
@@ -48,8 +49,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const int32_t const_i32;
 
 constexpr float kLn2 = 0.69314718055994531f;
+// s_getreg operand for HW_ID.SIMD_ID: register 4, bit offset 4, 2 bits.
+constexpr int kHwRegSimdId = (4) | (4 << 6) | ((2 - 1) << 11);
 constexpr float kTau = 8.0f;
 
 // Key permutation inside a 64-key tile: swap bits 2 and 3 (an involution).
@@ -72,6 +76,20 @@ constexpr int pitch(int len) { return len + 8; }
 // instead of speculating the body into straight-line selects (the element mask and the output
 // rescale are rare and must cost nothing when skipped).
 __device__ __forceinline__ void keep_branch() { __asm__ volatile("" ::); }
+
+// max / sum of x over the lane pair (l, l ^ 32) that holds the two halves of one query's keys,
+// with v_permlane32_swap (no LDS round trip).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -163,22 +181,42 @@ __global__ __launch_bounds__(256) void block_table_kernel(MaskDesc m, const int3
 }
 
 // ---------------------------------------------------------------------------------------------
+// The forward kernel.  One workgroup = 8 wave64s over Br = 256 query rows (32 rows per wave).
+// Waves w and w + 4 run on the same SIMD; they form two groups (w < 4 and w >= 4) that work one
+// phase apart:
+//   M-phase of tile t : O^T += V_{t-1}^T P_{t-1}^T, then S_t^T = K_t Q^T   (MFMA + LDS reads)
+//   V-phase of tile t : mask, row max, lazy rescale, P_t = exp2(S_t - m)   (VALU)
+// Slot s (between two barriers) runs the M-phase of group (s & 1) and the V-phase of the other,
+// so on every SIMD one wave keeps the matrix core busy while the other does the softmax.
+// K_t and V_{t-1} are the LDS tiles read in slots 2t and 2t+1; K_{t+1} and V_t are fetched into
+// VGPRs at the start of slot 2t and written to the idle LDS buffers at the end of slot 2t+1.
 template <int D, bool ALIBI, bool SOFTCAP, bool POS, bool OUTF32>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     FwdArgs a) {
+  constexpr int NT = 512;                // threads per workgroup
   constexpr int KCH = D / 8;             // 16-byte chunks per K row
   constexpr int VCH = kBc / 8;           // 16-byte chunks per V^T row
-  constexpr int KLD = kBc * KCH / 256;   // K chunks loaded per thread per tile
-  constexpr int VLD = D * VCH / 256;     // V^T chunks loaded per thread per tile
+  constexpr int KLD = kBc * KCH / NT;    // K chunks loaded per thread per tile
+  constexpr int VLD = D * VCH / NT;      // V^T chunks loaded per thread per tile
   constexpr int NKS = D / 16;            // k-steps of the score product
   constexpr int NDB = D / 32;            // 32-column blocks of O
   constexpr int KP = pitch(D);           // LDS pitch of a K row (keys x D)
   constexpr int VP = pitch(kBc);         // LDS pitch of a V^T row (D x keys)
-  static_assert(kBr == 128 && kBc == 64, "kernel is written for 128 x 64 tiles");
+  static_assert(kBr == 256 && kBc == 64, "kernel is written for 256 x 64 tiles");
+  static_assert(KLD >= 1 && VLD >= 1, "tile loads must cover the workgroup");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBc * KP];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VP];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  // Phase group: of the two waves the dispatcher placed on a SIMD, the lower-numbered one is
+  // group 0 and the other group 1 (SIMD id from the HW_ID register).  Correctness does not
+  // depend on this choice, only the overlap of matrix-core and vector work does.
+  __shared__ int simd_of[8];
+  if (lane == 0) simd_of[wave] = __builtin_amdgcn_s_getreg(kHwRegSimdId) & 3;
+  __syncthreads();
+  int grp = 0;
+  for (int w2 = 0; w2 < wave; ++w2) grp += simd_of[w2] == simd_of[wave];
+  grp = __builtin_amdgcn_readfirstlane(grp > 1 ? 1 : grp);  // wave-uniform: scalar branches
 
   // Workgroups are dispatched round-robin over the 8 XCDs; remap so that consecutive logical
   // blocks (the q-tiles of one head, sharing K and V) run on the same XCD and its L2.
@@ -212,48 +250,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (q_ok) x = *(const u32x4 *)(qp + ks * 16);
       qf[ks] = __builtin_bit_cast(bf16x8, x);
     }
+    // Settle the Q loads here, once, so no memory wait is charged to the first MFMA of every
+    // loop iteration.
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
-  int cnt;
-  const int32_t *lst = nullptr;
-  const int8_t *clsr = nullptr;
-  if (a.cls) {
+  // The key-tile list of this q-tile (written by the table kernel before this launch, so it is
+  // read-only here): read through the constant address space, i.e. with scalar loads.
+  int T;
+  const_i32 *lst = nullptr;
+  if (a.list) {
     const int bm = (a.kind == kMaskDocument) ? b : 0;
     const size_t row = (size_t)bm * a.n_qt + qt;
-    cnt = a.cnt[row];
-    lst = a.list + row * a.n_kt;
-    clsr = a.cls + row * a.n_kt;
+    T = ((const_i32 *)a.cnt)[row];
+    lst = (const_i32 *)a.list + row * a.n_kt;
   } else {
-    cnt = a.n_kt;
+    T = a.n_kt;
   }
-  const bool q_full = (qt + 1) * kBr <= N;
+  auto kt_of = [&](int t) -> int { return lst ? lst[t] : t; };
 
   const uint16_t *kbase = a.k + (size_t)bh * N * D;
   const uint16_t *vbase = a.vt + (size_t)bh * D * a.Npad;
   u32x4 kpre[KLD], vpre[VLD];
-  auto gload = [&](int kt) {
+  auto gload_k = [&](int kt) {
+    const bool in_range = (kt + 1) * kBc <= N;  // uniform: only the last tile can be ragged
 #pragma unroll
     for (int u = 0; u < KLD; ++u) {
-      const int c = tid + 256 * u, key = c / KCH, ch = c % KCH, j = kt * kBc + key;
+      const int c = tid + NT * u, key = c / KCH, ch = c % KCH, j = kt * kBc + key;
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (j < N) x = *(const u32x4 *)(kbase + (size_t)j * D + ch * 8);
+      if (in_range || j < N) x = *(const u32x4 *)(kbase + (size_t)j * D + ch * 8);
       kpre[u] = x;
     }
+  };
+  auto gload_v = [&](int kt) {
 #pragma unroll
     for (int u = 0; u < VLD; ++u) {
-      const int c = tid + 256 * u, row = c / VCH, ch = c % VCH;
+      const int c = tid + NT * u, row = c / VCH, ch = c % VCH;
       vpre[u] = *(const u32x4 *)(vbase + (size_t)row * a.Npad + (size_t)kt * kBc + ch * 8);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore_k = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < KLD; ++u) {
-      const int c = tid + 256 * u, key = c / KCH, ch = c % KCH;
+      const int c = tid + NT * u, key = c / KCH, ch = c % KCH;
       *(u32x4 *)&sK[buf][pi_key(key) * KP + ch * 8] = kpre[u];
     }
+  };
+  auto lstore_v = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < VLD; ++u) {
-      const int c = tid + 256 * u, row = c / VCH, ch = c % VCH;
+      const int c = tid + NT * u, row = c / VCH, ch = c % VCH;
       *(u32x4 *)&sV[buf][row * VP + ch * 8] = vpre[u];
     }
   };
@@ -264,35 +310,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f32x16 oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+  f32x16 s[2];
+  f16x8 pb[4];
 
-  if (cnt > 0) {
-    gload(lst ? lst[0] : 0);
-    lstore(0);
+  // One M-phase as a single software-pipelined sequence of MFMA steps: the P V steps
+  // (key group kk, d block db) and then the score steps (k-step ks, key block blk), ordered so
+  // that consecutive MFMAs write different accumulators.  The A
+  // fragment of step i + kDepth is read from LDS while step i runs, so LDS latency stays hidden
+  // behind the matrix core.
+  constexpr int kDepth = 4;
+  auto mphase = [&](int t) {
+    constexpr int NPV = 4 * NDB;
+    constexpr int NST = NPV + 2 * NKS;
+    const uint16_t *vbuf = &sV[(t - 1) & 1][l32 * VP + hf * 8];
+    const uint16_t *kbuf = &sK[t & 1][l32 * KP + hf * 8];
+    auto frag = [&](int i) -> u32x4 {
+      if (i < NPV) {
+        const int kk = i / NDB, db = i % NDB;
+        return *(const u32x4 *)(vbuf + db * 32 * VP + kk * 16);
+      }
+      const int j = i - NPV, ks = j >> 1, blk = j & 1;
+      return *(const u32x4 *)(kbuf + blk * 32 * KP + ks * 16);
+    };
+    u32x4 win[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i)
+      if (i < NST) win[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      const u32x4 cur = win[i % kDepth];
+      if (i + kDepth < NST) win[i % kDepth] = frag(i + kDepth);
+      if (i < NPV) {
+        const int kk = i / NDB, db = i % NDB;
+        oacc[db] = mfma32(__builtin_bit_cast(f16x8, cur), pb[kk], oacc[db]);
+      } else {
+        const int j = i - NPV, ks = j >> 1, blk = j & 1;
+        s[blk] = mfma32(__builtin_bit_cast(bf16x8, cur), qf[ks], ks == 0 ? f32x16{} : s[blk]);
+      }
+    }
+    // Pin that order for the scheduler: kDepth LDS reads, then MFMA / LDS read pairs.
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kDepth < NST) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  // Zero P and the V buffer read by the first M-phase (its P V step then adds exactly 0).
+#pragma unroll
+  for (int g = 0; g < 4; ++g) pb[g] = f16x8{};
+  for (int i = tid; i < D * VP / 8; i += NT) *(u32x4 *)&sV[1][i * 8] = u32x4{0u, 0u, 0u, 0u};
+  if (T > 0) {
+    gload_k(kt_of(0));
+    lstore_k(0);
   }
   __syncthreads();
 
-  for (int it = 0; it < cnt; ++it) {
-    const int buf = it & 1;
-    const int kt = lst ? lst[it] : it;
-    const int cls = clsr ? clsr[kt] : ((q_full && (kt + 1) * kBc <= N) ? 2 : 1);
-    const bool has_next = it + 1 < cnt;
-    if (has_next) gload(lst ? lst[it + 1] : it + 1);
-
-    // S^T = K Q^T, two 32-key blocks.
-    f32x16 s[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      s[blk] = f32x16{};
-      const uint16_t *kr = &sK[buf][(blk * 32 + l32) * KP + hf * 8];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kf = *(const bf16x8 *)(kr + ks * 16);
-        s[blk] = mfma32(kf, qf[ks], s[blk]);
-      }
-    }
-
-    // Score modifications, in base-2 units.  Register r of block blk is key
-    // kt*Bc + 32*blk + 16*(r/8) + 8*hf + r%8.
+  // V-phase of tile t: score modifications, mask, online softmax, P_t in fp16.
+  auto vphase = [&](int kt) {
+    // Register r of block blk is key kt*Bc + 32*blk + 16*(r/8) + 8*hf + r%8.
     const int kb = kt * kBc + 8 * hf;
     if constexpr (!POS) {
       const float abase = ALIBI ? slopeL * (float)(kb - qrow) : 0.f;
@@ -301,19 +379,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float x = s[blk][r];
-          float t;
+          float tt;
           if constexpr (SOFTCAP) {
             const float e = __builtin_amdgcn_exp2f(x * a.cap_c1);
-            t = fmaf(-2.f * a.capL, __builtin_amdgcn_rcpf(1.f + e), a.capL);
+            tt = fmaf(-2.f * a.capL, __builtin_amdgcn_rcpf(1.f + e), a.capL);
           } else {
-            t = x * c;
+            tt = x * c;
           }
-          if constexpr (ALIBI) t += fmaf(slopeL, (float)(32 * blk + 16 * (r >> 3) + (r & 7)), abase);
-          s[blk][r] = t;
+          if constexpr (ALIBI)
+            tt += fmaf(slopeL, (float)(32 * blk + 16 * (r >> 3) + (r & 7)), abase);
+          s[blk][r] = tt;
         }
       }
     }
-    if (cls == 1) {
+    // Element mask only when some row of this wave does not allow all 64 keys of the tile
+    // (hi <= N - 1 always, so a fully allowed row also has the tile in range).
+    if (__builtin_amdgcn_ballot_w64(!(lo <= kt * kBc && hi >= kt * kBc + kBc - 1))) {
       keep_branch();
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
@@ -324,16 +405,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
-
-    // Tile row maximum (in-lane over 32 keys, then across the lane pair sharing the query).
+    // Tile row maximum: in-lane over 32 keys, then with the lane that shares the query.
     float mx = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max(mx);
     const float m_tile = POS ? mx * c : mx;
-
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kTau)) {
       keep_branch();
       const float m_new = fmaxf(m_run, m_tile);
@@ -344,9 +423,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-    // Probabilities (fp32 for l, fp16 for the product), four 8-key groups.
-    f16x8 pb[4];
     float psum[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -364,24 +440,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       pb[g] = __builtin_convertvector(pv, f16x8);
     }
     l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+  };
+  // kt of tiles k - 1, k, k + 1 are kept in scalars; tile k + 2's is read one iteration ahead.
+  int kt_prev = 0, kt_cur = T > 0 ? kt_of(0) : 0, kt_next = T > 1 ? kt_of(1) : 0;
+  auto slot_a_loads = [&](int k) {
+    if (k + 1 < T) gload_k(kt_next);
+    if (k < T) gload_v(kt_cur);
+  };
+  auto slot_b_stores = [&](int k) {
+    if (k + 1 < T) lstore_k((k + 1) & 1);
+    if (k < T) lstore_v(k & 1);
+  };
+  auto advance = [&](int k) {
+    const int kt_nn = k + 2 < T ? kt_of(k + 2) : 0;
+    kt_prev = kt_cur;
+    kt_cur = kt_next;
+    kt_next = kt_nn;
+  };
 
-    // O^T += V^T P^T over the 4 groups of 16 keys.
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const uint16_t *vr = &sV[buf][(db * 32 + l32) * VP + hf * 8];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const f16x8 vf = *(const f16x8 *)(vr + kk * 16);
-        oacc[db] = mfma32(vf, pb[kk], oacc[db]);
-      }
+  // Two slots per iteration k.  Slot A: group 0 runs M-phase k, group 1 V-phase k-1.  Slot B:
+  // group 0 runs V-phase k, group 1 M-phase k.  K_k and V_{k-1} are read in both slots; K_{k+1}
+  // and V_k, fetched at the start of slot A, are written to the idle buffers at the end of slot B.
+  // Both groups execute the same 2T + 2 barriers.  In M-phase 0, P = 0 against a zeroed V
+  // buffer adds nothing; in M-phase T the score product reads a stale (finite, in-bounds) K
+  // buffer and its result is never used.
+  if (grp == 0) {
+    for (int k = 0; k <= T; ++k) {
+      slot_a_loads(k);
+      mphase(k);
+      __syncthreads();
+      if (k < T) vphase(kt_cur);
+      slot_b_stores(k);
+      advance(k);
+      __syncthreads();
     }
-
-    if (has_next) lstore(buf ^ 1);
-    __syncthreads();
+  } else {
+    for (int k = 0; k <= T; ++k) {
+      slot_a_loads(k);
+      if (k >= 1) vphase(kt_prev);
+      __syncthreads();
+      mphase(k);
+      slot_b_stores(k);
+      advance(k);
+      __syncthreads();
+    }
   }
 
   // Epilogue: O = O / l, L = (m + log2 l) * ln 2.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_ok) {
     const size_t obase = ((size_t)bh * N + qrow) * D + 16 * hf;
@@ -409,9 +515,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <int D, bool ALIBI, bool SOFTCAP, bool POS>
 hipError_t launch_out(bool out_f32, const FwdArgs &a, dim3 grid, hipStream_t s) {
   if (out_f32)
-    fwd_kernel<D, ALIBI, SOFTCAP, POS, true><<<grid, 256, 0, s>>>(a);
+    fwd_kernel<D, ALIBI, SOFTCAP, POS, true><<<grid, 512, 0, s>>>(a);
   else
-    fwd_kernel<D, ALIBI, SOFTCAP, POS, false><<<grid, 256, 0, s>>>(a);
+    fwd_kernel<D, ALIBI, SOFTCAP, POS, false><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

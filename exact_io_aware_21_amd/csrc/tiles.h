@@ -22,8 +22,8 @@ namespace attn {
 
 enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2, kMaskDocument = 3 };
 
-// Tile shape of the forward kernel: Br query rows (4 waves x 32) and Bc keys per step.
-constexpr int kBr = 128;
+// Tile shape of the forward kernel: Br query rows (8 waves x 32) and Bc keys per step.
+constexpr int kBr = 256;
 constexpr int kBc = 64;
 
 struct MaskDesc {

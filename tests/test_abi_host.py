@@ -34,8 +34,8 @@ def test_strerror_and_tile_shape():
     assert L.attn_strerror(0) == b"ok"
     for code in (-1, -2, -3, -4):
         assert L.attn_strerror(code) != b"unknown error code"
-    assert attn.attn_tile_shape(128, attn.ATTN_MASK_CAUSAL) == (128, 64)
-    assert attn.attn_tile_shape(64, attn.ATTN_MASK_DOCUMENT | attn.ATTN_MOD_SOFTCAP) == (128, 64)
+    assert attn.attn_tile_shape(128, attn.ATTN_MASK_CAUSAL) == (256, 64)
+    assert attn.attn_tile_shape(64, attn.ATTN_MASK_DOCUMENT | attn.ATTN_MOD_SOFTCAP) == (256, 64)
     with pytest.raises(attn.AttnError):
         attn.attn_tile_shape(96, 0)
     with pytest.raises(attn.AttnError):
@@ -48,7 +48,7 @@ def test_workspace_size():
     assert attn.attn_workspace_size(1, 1, 256, 64, 0) == al(1 * 64 * 256 * 2)
     B, H, N, d = 2, 3, 1000, 128
     npad = 16 * 64
-    rows = 8  # ceil(1000/128)
+    rows = 4  # ceil(1000/256)
     exp = al(B * H * d * npad * 2) + al(rows * 16) + al(rows * 4) + al(rows * 16 * 4)
     assert attn.attn_workspace_size(B, H, N, d, attn.ATTN_MASK_CAUSAL) == exp
     rows_doc = B * rows
