@@ -110,6 +110,7 @@ __global__ __launch_bounds__(256) void lds_rate(float *out, float seed) {
   const float *base = &lds[(lane & 31) * 68 + (lane >> 5) * 4];
   f32x4 acc = {};
   for (int it = 0; it < kIters; ++it) {
+    asm volatile("" ::: "memory");  // the reads are loop-invariant: force them every iteration
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const f32x4 v = *(const f32x4 *)(base + 8 * k + ((it & 1) << 11));
@@ -117,6 +118,66 @@ __global__ __launch_bounds__(256) void lds_rate(float *out, float seed) {
     }
   }
   if (acc[0] + acc[1] + acc[2] + acc[3] == 1234.5f) out[threadIdx.x] = acc[0];
+}
+
+// Dependent v_fma_f32 chain in one wave (latency): 64 dependent FMAs per iteration.
+__global__ __launch_bounds__(64) void fma_latency(float *out, float seed) {
+  float x = seed * threadIdx.x;
+  for (int it = 0; it < kIters / 16; ++it) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x = fmaf(x, 0.999f, 0.001f);
+  }
+  if (x == 1234.5f) out[threadIdx.x] = x;
+}
+
+// Interleaved independent exp and fma chains in one wave: do the transcendental and FMA work
+// overlap?
+__global__ __launch_bounds__(256) void expfma_rate(float *out, float seed) {
+  float x[8], y[8];
+  for (int i = 0; i < 8; ++i) {
+    x[i] = seed * (threadIdx.x + i) * 1e-3f;
+    y[i] = seed * (threadIdx.x + 2 * i);
+  }
+  for (int it = 0; it < kIters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] = __builtin_amdgcn_exp2f(x[i]);
+      y[i] = fmaf(y[i], 0.999f, 0.001f);
+    }
+  }
+  float s = 0.f;
+  for (int i = 0; i < 8; ++i) s += x[i] + y[i];
+  if (s == 1234.5f) out[threadIdx.x] = s;
+}
+
+// Even waves MFMA, odd waves FMA.
+__global__ __launch_bounds__(512) void mixed_fma(float *out, float seed) {
+  const int wave = threadIdx.x >> 6;
+  float s = 0.f;
+  if (wave & 1) {
+    float x[8];
+    for (int i = 0; i < 8; ++i) x[i] = seed * (threadIdx.x + i);
+    for (int it = 0; it < kIters; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = fmaf(x[i], 0.999f, 0.001f);
+    }
+    for (int i = 0; i < 8; ++i) s += x[i];
+  } else {
+    bf16x8 a, b;
+    for (int i = 0; i < 8; ++i) {
+      a[i] = (__bf16)(seed * (threadIdx.x + i));
+      b[i] = (__bf16)(seed * (i + 1));
+    }
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < kIters; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+    for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  }
+  if (s == 1234.5f) out[threadIdx.x] = s;
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const f32x4 *__restrict__ src,
@@ -166,6 +227,28 @@ int main() {
     ms = time_ms([&] { fma_rate<<<grid, 256>>>(out, seed); }, 5);
     printf("v_fma_f32, %d wave/SIMD: %.1f Gop/s = %.2f lane-ops/clk/CU at 2.4 GHz\n", wg_per_cu,
            ops / ms / 1e6, ops / (ms * 1e-3) / 2.4e9 / cus);
+  }
+  // Throughput-bound VALU: 4 waves per SIMD (four 256-thread workgroups per CU).
+  {
+    const int grid = cus * 4;
+    float ms = time_ms([&] { fma_rate<<<grid * 4, 256>>>(out, seed); }, 5);
+    double ops = (double)grid * 1024 * kIters * 8;
+    printf("v_fma_f32, 4 wave/SIMD: %.2f lane-ops/clk/CU (%.2f cycles per wave64 instruction per SIMD)\n",
+           ops / (ms * 1e-3) / 2.4e9 / cus, 64.0 * 4 / (ops / (ms * 1e-3) / 2.4e9 / cus));
+    ms = time_ms([&] { exp_rate<<<grid * 4, 256>>>(out, seed); }, 5);
+    printf("v_exp_f32 (+1 sub each), 4 wave/SIMD: %.2f exp lane-ops/clk/CU\n", ops / (ms * 1e-3) / 2.4e9 / cus);
+    ms = time_ms([&] { expfma_rate<<<grid * 4, 256>>>(out, seed); }, 5);
+    printf("exp + fma interleaved, 4 wave/SIMD: %.2f (exp+fma) lane-ops/clk/CU\n", 2 * ops / (ms * 1e-3) / 2.4e9 / cus);
+    ms = time_ms([&] { fma_latency<<<cus * 4, 64>>>(out, seed); }, 3);
+    printf("dependent v_fma_f32 chain, 1 wave: %.2f cycles per FMA\n", ms * 1e-3 * 2.4e9 / ((double)(kIters / 16) * 64));
+  }
+  {
+    const int grid = cus * 8;
+    const float ms_mf = time_ms([&] { mixed_fma<<<grid, 512>>>(out, seed); }, 5);
+    const float ms_f = time_ms([&] { fma_rate<<<grid, 256>>>(out, seed); }, 5);
+    const float ms_mm = time_ms([&] { mfma_rate<<<grid, 256>>>(out, seed); }, 5);
+    printf("overlap: mfma wave + fma wave per SIMD %.3f ms vs mfma alone %.3f ms, fma alone %.3f ms\n",
+           ms_mf, ms_mm, ms_f);
   }
   {
     const int grid = cus * 8;
