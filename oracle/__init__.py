@@ -1,11 +1,13 @@
-"""fp64 CPU oracle for the attention forward pass.
+"""fp64 CPU oracle for the attention forward and backward passes.
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check in __graft_entry__ and by the
 CPU-baseline leg of bench.py, never by the HIP path.  It shares no code with that path.
 """
 from .attention import (MASKS, allowed, allowed_pair_count, attention, attention_blocked,
                         decode_bf16, doc_index, scores)
+from .backward import attention_backward, backward_row_dot
 from .tiles import tile_class_counts, tile_table
 
-__all__ = ["MASKS", "allowed", "allowed_pair_count", "attention", "attention_blocked",
-           "decode_bf16", "doc_index", "scores", "tile_class_counts", "tile_table"]
+__all__ = ["MASKS", "allowed", "allowed_pair_count", "attention", "attention_backward",
+           "attention_blocked", "backward_row_dot", "decode_bf16", "doc_index", "scores",
+           "tile_class_counts", "tile_table"]
