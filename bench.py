@@ -145,6 +145,59 @@ def cpu_baseline(w, inp, budget_s=20.0, chunk=2048):
                       f"{dt:.1f} s wall"}
 
 
+def bench_bwd(args, w, inp, q, k, v, o, lse, var, slopes, offs, dev):
+    """Times attn_bwd on the workload (after one attn_fwd for O and L): K timed steps, with the
+    library's event pair around the two main backward kernels."""
+    import numpy as np
+    import torch
+
+    from exact_io_aware_21_amd import attn, inputs
+
+    g = torch.from_numpy(inputs.draw_dout(w.B, w.H, w.N, w.d, w.seed).view(np.int16)) \
+        .view(torch.bfloat16).to(dev)
+    attn.attn_fwd(q, k, v, o, lse, inp["scale"], var, window=w.window, softcap=w.softcap,
+                  alibi_slopes=slopes, doc_offsets=offs)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = attn.alloc_bwd_workspace(w.B, w.H, w.N, w.d, var, dev)
+    kw = dict(window=w.window, softcap=w.softcap, alibi_slopes=slopes, doc_offsets=offs,
+              workspace=ws)
+    for _ in range(args.warmup):
+        attn.attn_bwd(q, k, v, o, lse, g, dq, dk, dv, inp["scale"], var, **kw)
+    K = args.steps
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, b in kev:
+        a.record()
+        b.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        attn.attn_bwd(q, k, v, o, lse, g, dq, dk, dv, inp["scale"], var, timing_events=kev[i],
+                      **kw)
+    end.record()
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / K
+    kern_ms = sum(a.elapsed_time(b) for a, b in kev) / K
+    flops = 10.0 * w.d * allowed_pairs(w, inp["doc_offsets"])
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    out = {
+        "metric": "attention bwd TFLOP/s (unmasked FLOPs, 10 d per allowed pair) and % of MFMA "
+                  "peak, 1 MI355X",
+        "value": round(flops / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0, sigma^2) Q/K/V and N(0, 1) dO rounded to bf16)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
+                   "window": w.window, "alibi": w.alibi, "softcap": w.softcap,
+                   "unmasked_gflop": round(flops / 1e9, 3), "bwd_kernels_ms": round(kern_ms, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +205,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="bwd: time attn_bwd instead (10 d FLOPs per allowed pair; no CPU leg)")
     ap.add_argument("--traffic", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH",
                                                     "COPY_WRITE"),
                     help="write profiles/traffic_fwd_<workload>.json from rocprofv3 counter CSVs")
@@ -186,6 +241,10 @@ def main():
     ws = attn.alloc_workspace(w.B, w.H, w.N, w.d, var, dev)
     kw = dict(window=w.window, softcap=w.softcap, alibi_slopes=slopes, doc_offsets=offs,
               workspace=ws)
+
+    if args.which == "bwd":
+        bench_bwd(args, w, inp, q, k, v, o, lse, var, slopes, offs, dev)
+        return
 
     for _ in range(args.warmup):
         attn.attn_fwd(q, k, v, o, lse, inp["scale"], var, **kw)

@@ -1,6 +1,6 @@
 """Thin Python binding of libattn.so (include/attn.h): argument marshalling only.
 
-Every step of the forward pass runs in the library's HIP kernels.  torch is used only to hold
+Every step of the forward and backward passes runs in the library's HIP kernels.  torch is used only to hold
 device memory and to name the current HIP stream.  There is no fallback: if the library is not
 built, or the device is not gfx950, calls raise.
 """
@@ -30,7 +30,8 @@ MASK_BITS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
              "window": ATTN_MASK_SLIDING_WINDOW, "document": ATTN_MASK_DOCUMENT}
 
 EXPORTS = ("attn_fwd", "attn_workspace_size", "attn_tile_shape", "attn_block_table",
-           "attn_block_table_host", "attn_strerror", "attn_last_error")
+           "attn_block_table_host", "attn_bwd", "attn_bwd_workspace_size", "attn_strerror",
+           "attn_last_error")
 
 
 class attn_params(ctypes.Structure):
@@ -71,6 +72,10 @@ def lib():
         L.attn_block_table.restype = c_int
         L.attn_block_table_host.argtypes = [c_int, c_int, c_int, c_int, c_u32, P, c_vp, c_vp, c_vp]
         L.attn_block_table_host.restype = c_int
+        L.attn_bwd.argtypes = [c_vp] * 9 + [c_int, c_int, c_int, c_int, c_f, c_u32, P, c_vp]
+        L.attn_bwd.restype = c_int
+        L.attn_bwd_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_u32]
+        L.attn_bwd_workspace_size.restype = ctypes.c_size_t
         L.attn_strerror.argtypes = [c_int]
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_last_error.argtypes = []
@@ -171,6 +176,51 @@ def attn_fwd(q, k, v, o, lse, scale, variant, window=0, softcap=0.0, alibi_slope
     _check(lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                           float(scale), variant, ctypes.byref(p), _stream(stream)))
     return o, lse
+
+
+def attn_bwd_workspace_size(B: int, H: int, N: int, d: int, variant: int) -> int:
+    return int(lib().attn_bwd_workspace_size(B, H, N, d, variant))
+
+
+def alloc_bwd_workspace(B, H, N, d, variant, device="cuda"):
+    """A workspace tensor of the size attn_bwd needs (allocated by torch, outside any call)."""
+    import torch
+    n = attn_bwd_workspace_size(B, H, N, d, variant)
+    if n == 0:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "invalid shape for attn_bwd_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale, variant, window=0, softcap=0.0,
+             alibi_slopes=None, doc_offsets=None, workspace=None, stream=None, timing_events=None):
+    """Calls attn_bwd: q, k, v, dout bf16 [B,H,N,d]; o the forward output and dq, dk, dv the
+    gradients, all of one dtype (bf16 or fp32); lse fp32 [B,H,N] from the forward."""
+    import torch
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{name} must be a contiguous bf16 [B,H,N,d] tensor")
+    for name, t in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.dtype != o.dtype or o.dtype not in (torch.bfloat16, torch.float32) \
+                or not t.is_contiguous() or tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{name} must be a contiguous [B,H,N,d] tensor of o's dtype "
+                             f"(bf16 or fp32)")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be a contiguous fp32 [B,H,N] tensor")
+    if workspace is None:
+        workspace = alloc_bwd_workspace(B, H, N, d, variant, q.device)
+    p = make_params(window, softcap, alibi_slopes, doc_offsets,
+                    ATTN_O_F32 if o.dtype == torch.float32 else ATTN_O_BF16, workspace)
+    ev = None
+    if timing_events is not None:
+        if not (timing_events[0].cuda_event and timing_events[1].cuda_event):
+            raise ValueError("timing events must have been recorded once before use")
+        ev = (ctypes.c_void_p * 2)(timing_events[0].cuda_event, timing_events[1].cuda_event)
+        p.timing_events = ctypes.cast(ev, ctypes.c_void_p)
+    _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                          _ptr(dk), _ptr(dv), B, H, N, d, float(scale), variant, ctypes.byref(p),
+                          _stream(stream)))
+    return dq, dk, dv
 
 
 def attn_block_table(B, H, N, d, variant, cls, kv_cnt, kv_list, window=0, doc_offsets=None,

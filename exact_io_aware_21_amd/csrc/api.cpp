@@ -106,6 +106,37 @@ WsLayout ws_layout(const Shape &s) {
   return w;
 }
 
+// Backward workspace: D (fp32 [BH][N]), the bf16 packs Q^T, dO^T, K^T ([BH][d][Npad] each) and,
+// for masked kinds, the forward block table.
+struct BwdLayout {
+  size_t dvec, qt, dot, kt, cls, cnt, list, total;
+};
+
+BwdLayout bwd_layout(const Shape &s) {
+  BwdLayout w{};
+  size_t off = 0;
+  const size_t pack = (size_t)s.B * s.H * s.d * s.Npad * 2;
+  w.dvec = off;
+  off = align256(off + (size_t)s.B * s.H * s.N * 4);
+  w.qt = off;
+  off = align256(off + pack);
+  w.dot = off;
+  off = align256(off + pack);
+  w.kt = off;
+  off = align256(off + pack);
+  if (s.kind != ATTN_MASK_NONE) {
+    const size_t rows = (size_t)s.Bm * s.n_qt;
+    w.cls = off;
+    off = align256(off + rows * s.n_kt);
+    w.cnt = off;
+    off = align256(off + rows * 4);
+    w.list = off;
+    off = align256(off + rows * s.n_kt * 4);
+  }
+  w.total = off;
+  return w;
+}
+
 int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
@@ -234,7 +265,7 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
   const hipStream_t st = (hipStream_t)stream;
   char *ws = (char *)params->workspace;
   uint16_t *vt = (uint16_t *)(ws + wl.vt);
-  if (attn::launch_vt_pack((const uint16_t *)v, vt, B * H, N, s.Npad, d, st) != hipSuccess)
+  if (attn::launch_vt_pack((const uint16_t *)v, vt, B * H, N, s.Npad, d, true, st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "V transpose kernel launch failed");
 
   attn::FwdArgs a{};
@@ -280,6 +311,97 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
     return fail(ATTN_ERR_LAUNCH, "timing event record failed");
   if (attn::launch_fwd(in, a, st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "forward kernel launch failed");
+  if (ev && hipEventRecord((hipEvent_t)ev[1], st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "timing event record failed");
+  return ATTN_OK;
+}
+
+size_t attn_bwd_workspace_size(int B, int H, int N, int d, uint32_t variant) {
+  Shape s;
+  if (check_shape(B, H, N, d, variant, s) != ATTN_OK) return 0;
+  return bwd_layout(s).total;
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             const void *dout, void *dq, void *dk, void *dv, int B, int H, int N, int d,
+             float scale, uint32_t variant, const attn_params *params, void *stream) {
+  Shape s;
+  int rc = check_shape(B, H, N, d, variant, s);
+  if (rc) return rc;
+  if ((long long)B * H > 65535) return fail(ATTN_ERR_INVALID_ARG, "B*H must be <= 65535");
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(ATTN_ERR_INVALID_ARG, "tensor arguments must be 16-byte aligned");
+  if ((uintptr_t)lse & 3u) return fail(ATTN_ERR_INVALID_ARG, "lse misaligned");
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+  if ((rc = check_params(s, variant, params, true))) return rc;
+  const BwdLayout wl = bwd_layout(s);
+  if (!params->workspace || ((uintptr_t)params->workspace & 255u))
+    return fail(ATTN_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (params->workspace_bytes < wl.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", params->workspace_bytes,
+                wl.total);
+  if ((rc = check_device())) return rc;
+
+  const hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)params->workspace;
+  attn::BwdArgs a{};
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v;
+  a.dout = (const uint16_t *)dout;
+  a.o = o;
+  a.lse = lse;
+  a.qt = (const uint16_t *)(ws + wl.qt);
+  a.dot = (const uint16_t *)(ws + wl.dot);
+  a.kt = (const uint16_t *)(ws + wl.kt);
+  a.dvec = (float *)(ws + wl.dvec);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.Npad = s.Npad;
+  a.n_qt = s.n_qt;
+  a.n_kt = s.n_kt;
+  const float log2e = 1.4426950408889634f;
+  a.scale = scale;
+  a.c = scale * log2e;
+  if (variant & ATTN_MOD_SOFTCAP) {
+    a.cap_c1 = 2.f * scale * log2e / params->softcap;
+    a.capL = params->softcap * log2e;
+  }
+  a.slopes = (variant & ATTN_MOD_ALIBI) ? params->alibi_slopes : nullptr;
+  a.kind = (int)s.kind;
+  a.window = s.kind == ATTN_MASK_SLIDING_WINDOW ? params->window : 0;
+  a.max_docs = s.kind == ATTN_MASK_DOCUMENT ? params->max_docs : 0;
+  a.offs = s.kind == ATTN_MASK_DOCUMENT ? params->doc_offsets : nullptr;
+  a.o_f32 = a.out_f32 = params->o_dtype == ATTN_O_F32;
+
+  if (attn::launch_vt_pack(a.q, (uint16_t *)a.qt, B * H, N, s.Npad, d, false, st) != hipSuccess ||
+      attn::launch_vt_pack(a.dout, (uint16_t *)a.dot, B * H, N, s.Npad, d, false, st) !=
+          hipSuccess ||
+      attn::launch_vt_pack(a.k, (uint16_t *)a.kt, B * H, N, s.Npad, d, false, st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "transpose kernel launch failed");
+  if (attn::launch_bwd_dot(a, d, st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "row-dot kernel launch failed");
+  if (s.kind != ATTN_MASK_NONE) {
+    a.cnt = (const int32_t *)(ws + wl.cnt);
+    a.list = (const int32_t *)(ws + wl.list);
+    if (attn::launch_block_table(mask_desc(s, params), a.offs, s.Bm, s.n_qt, s.n_kt,
+                                 (int8_t *)(ws + wl.cls), (int32_t *)(ws + wl.cnt),
+                                 (int32_t *)(ws + wl.list), st) != hipSuccess)
+      return fail(ATTN_ERR_LAUNCH, "block table kernel launch failed");
+  }
+  void *const *ev = params->timing_events;
+  if (ev && hipEventRecord((hipEvent_t)ev[0], st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "timing event record failed");
+  if (attn::launch_bwd(a, d, (variant & ATTN_MOD_ALIBI) != 0, (variant & ATTN_MOD_SOFTCAP) != 0,
+                       st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "backward kernel launch failed");
   if (ev && hipEventRecord((hipEvent_t)ev[1], st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "timing event record failed");
   return ATTN_OK;

@@ -1,0 +1,436 @@
+// gfx950 kernels of the attention backward pass.
+//
+// Page "FlashAttention/es" (marovi.ai), section "Paso hacia atrás y recomputación": the backward
+// pass does not read a stored attention matrix; it recomputes S and P tile by tile from the saved
+// log-sum-exp L and the output gradient dO.  With P_ij = exp(s_ij - L_i) recomputed:
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D) with D_i = dO_i . O_i,
+//   dT = dS * (1 - tanh^2) under the soft-cap,  dQ = scale * dT K,  dK = scale * dT^T Q.
+// Two kernels, both deterministic (no atomics; every output element is written by one lane):
+//  * bwd_dkdv_kernel owns keys: 4 waves x 32 keys per workgroup; it walks the query steps
+//    (32 rows) that the mask allows for its keys and accumulates dK^T and dV^T in registers.
+//  * bwd_dq_kernel owns queries: 8 waves x 32 rows = one forward q-tile; it walks that q-tile's
+//    non-empty key tiles from the forward block table and accumulates dQ^T in registers.
+// Both recompute S and dP, so the score and dP products run twice; in exchange no partial dQ is
+// ever summed across workgroups.
+//
+// gfx950 mapping (same devices as the forward kernel, see fwd.hip):
+//  * Every product is a v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Q, K, V, dO are the
+//    exact bf16 inputs; P (<= 1) and dS are rounded to bf16 as MFMA operands.
+//  * The recomputed tile is built so that its lane owns one row of the output being accumulated:
+//    in bwd_dkdv_kernel S = Q K^T (A = Q rows from LDS, B = K^T of the wave's keys in VGPRs), so
+//    lane % 32 is a key; in bwd_dq_kernel S^T = K Q^T, so lane % 32 is a query.
+//  * The rows of the LDS operand are stored with index bits 2 and 3 swapped (pi_key), which makes
+//    the 16 accumulator registers of a lane two runs of 8 consecutive rows: P and dS then feed the
+//    next product as its B operand straight from registers.
+//  * The other operand of those products (Q^T, dO^T for dK, dV; K^T for dQ) comes from the
+//    transposed, sigma-permuted bf16 packs in the workspace, so each lane's accumulator registers
+//    are 16 consecutive output columns and the epilogue stores 16-byte vectors.
+#include "kcommon.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// D_i = sum_c dO_ic O_ic (fp32).  One group of D/8 lanes per row, 16-byte loads.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;  // lanes per row
+  constexpr int RPB = 256 / LPR;
+  const size_t rows = (size_t)a.B * a.H * a.N;
+  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int ch = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 g = *(const u32x4 *)(a.dout + row * D + ch * 8);
+    float of[8];
+    if (a.o_f32) {
+      const f32x4 o0 = *(const f32x4 *)((const float *)a.o + row * D + ch * 8);
+      const f32x4 o1 = *(const f32x4 *)((const float *)a.o + row * D + ch * 8 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        of[e] = o0[e];
+        of[4 + e] = o1[e];
+      }
+    } else {
+      const u32x4 ob = *(const u32x4 *)((const uint16_t *)a.o + row * D + ch * 8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        of[2 * w] = __uint_as_float(ob[w] << 16);
+        of[2 * w + 1] = __uint_as_float(ob[w] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = fmaf(__uint_as_float(g[w] << 16), of[2 * w], acc);
+      acc = fmaf(__uint_as_float(g[w] & 0xFFFF0000u), of[2 * w + 1], acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (row < rows && ch == 0) a.dvec[row] = acc;
+}
+
+// Stores one lane's 16 consecutive fp32 output columns (bf16 or fp32 output).
+template <bool OUTF32>
+__device__ __forceinline__ void store16(void *out, size_t off, const f32x16 &o) {
+  if constexpr (OUTF32) {
+    float *op = (float *)out + off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(f32x4 *)(op + 4 * i) = f32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+  } else {
+    uint16_t *op = (uint16_t *)out + off;
+    const f32x8 o0 = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+    const f32x8 o1 = {o[8], o[9], o[10], o[11], o[12], o[13], o[14], o[15]};
+    *(bf16x8 *)op = __builtin_convertvector(o0, bf16x8);
+    *(bf16x8 *)(op + 8) = __builtin_convertvector(o1, bf16x8);
+  }
+}
+
+// Score of one (query i, key j) pair from its raw dot product x, in base-2 units, and the factor
+// d s / d t of the soft-cap (1 - tanh^2; 1 without it).
+template <bool ALIBI, bool SOFTCAP>
+__device__ __forceinline__ float score2(const BwdArgs &a, float x, float slopeL, int i, int j,
+                                        float &dcap) {
+  float t;
+  if constexpr (SOFTCAP) {
+    const float e = __builtin_amdgcn_exp2f(x * a.cap_c1);
+    t = fmaf(-2.f * a.capL, __builtin_amdgcn_rcpf(1.f + e), a.capL);  // cap tanh(x scale/cap) log2e
+    const float th = t / a.capL;
+    dcap = 1.f - th * th;
+  } else {
+    t = x * a.c;
+    dcap = 1.f;
+  }
+  if constexpr (ALIBI) t = fmaf(slopeL, (float)(j - i), t);
+  return t;
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK, dV: one workgroup = 4 waves x 32 keys of one (batch, head); query steps of 32 rows.
+template <int D, bool ALIBI, bool SOFTCAP, bool OUTF32>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NT = 256, QS = 32, KPW = 32;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int RP = pitch(D);   // LDS pitch of a Q / dO row
+  constexpr int TP = pitch(QS);  // LDS pitch of a Q^T / dO^T row (d x 32 queries)
+  constexpr int RCH = QS * (D / 8) / NT;  // row-tile chunks per thread
+  constexpr int TCH = D * (QS / 8) / NT;  // transposed-tile chunks per thread
+  static_assert(RCH >= 1 && TCH >= 1, "tile copies must cover the workgroup");
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[QS * RP], sDO[QS * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t sQT[D * TP], sDOT[D * TP];
+  __shared__ __attribute__((aligned(16))) float sL2[QS], sDv[QS];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
+  const int N = a.N;
+  const int key0 = blockIdx.x * (4 * KPW);
+  const int j = key0 + wave * KPW + l32;  // this lane's key
+  const bool j_ok = j < N;
+  const MaskDesc md{a.kind, N, a.window, a.offs ? a.offs + (size_t)b * (a.max_docs + 1) : nullptr,
+                    a.max_docs};
+  int qlo = 1, qhi = 0;  // queries allowed to attend to key j (empty past N)
+  if (j_ok) {
+    qlo = col_lo(md, j);
+    qhi = col_hi(md, j);
+  }
+  // Query steps the workgroup visits: the union over its keys (both bounds grow with j).
+  const int jl = min(key0 + 4 * KPW, N) - 1;
+  const int qs_begin = col_lo(md, key0) / QS, qs_end = col_hi(md, jl) / QS + 1;
+
+  const size_t hbase = (size_t)bh * N * D;
+  const float slopeL = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+  bf16x8 kf[NKS], vf[NKS];  // B operands: K^T and V^T of this lane's key
+  {
+    const size_t off = hbase + (size_t)(j_ok ? j : 0) * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (j_ok) {
+        x = *(const u32x4 *)(a.k + off + ks * 16);
+        y = *(const u32x4 *)(a.v + off + ks * 16);
+      }
+      kf[ks] = __builtin_bit_cast(bf16x8, x);
+      vf[ks] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  f32x16 dkt[NDB], dvt[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dkt[i] = dvt[i] = f32x16{};
+
+  for (int qs = qs_begin; qs < qs_end; ++qs) {
+    const int q0 = qs * QS;
+    // Stage the query step: Q and dO rows (rows pi-permuted; past N: row N - 1, masked below),
+    // the transposed packs, and L (base 2) and D of the 32 queries.
+#pragma unroll
+    for (int u = 0; u < RCH; ++u) {
+      const int c = tid + NT * u, r = c / (D / 8), ch = c % (D / 8);
+      const size_t src = hbase + (size_t)min(q0 + r, N - 1) * D + ch * 8;
+      *(u32x4 *)&sQ[pi_key(r) * RP + ch * 8] = *(const u32x4 *)(a.q + src);
+      *(u32x4 *)&sDO[pi_key(r) * RP + ch * 8] = *(const u32x4 *)(a.dout + src);
+    }
+#pragma unroll
+    for (int u = 0; u < TCH; ++u) {
+      const int c = tid + NT * u, r = c / (QS / 8), ch = c % (QS / 8);
+      const size_t src = ((size_t)bh * D + r) * a.Npad + q0 + ch * 8;
+      *(u32x4 *)&sQT[r * TP + ch * 8] = *(const u32x4 *)(a.qt + src);
+      *(u32x4 *)&sDOT[r * TP + ch * 8] = *(const u32x4 *)(a.dot + src);
+    }
+    if (tid < QS) {
+      const int i = q0 + tid;
+      sL2[tid] = i < N ? a.lse[(size_t)bh * N + i] * kLog2e : 0.f;
+      sDv[tid] = i < N ? a.dvec[(size_t)bh * N + i] : 0.f;
+    }
+    __syncthreads();
+
+    // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys: accumulator register r
+    // (row 8(r/4) + 4 hf + r%4 of the pi-permuted tile) is query q0 + qq(r), column = key j.
+    f32x16 s = {}, dp = {};
+    {
+      const uint16_t *qa = &sQ[l32 * RP + hf * 8];
+      const uint16_t *da = &sDO[l32 * RP + hf * 8];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4 *)(qa + ks * 16)), kf[ks], s);
+        dp = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4 *)(da + ks * 16)), vf[ks], dp);
+      }
+    }
+    f32x4 l2v[4], dv4[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      const int base = 16 * (aa >> 1) + 8 * hf + 4 * (aa & 1);
+      l2v[aa] = *(const f32x4 *)&sL2[base];
+      dv4[aa] = *(const f32x4 *)&sDv[base];
+    }
+    const bool partial =
+        __builtin_amdgcn_ballot_w64(!(qlo <= q0 && qhi >= q0 + QS - 1)) != 0;
+    float p[16], ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int aa = r >> 2, bb = r & 3;
+      const int i = q0 + 16 * (aa >> 1) + 8 * hf + 4 * (aa & 1) + bb;
+      float dcap;
+      const float t = score2<ALIBI, SOFTCAP>(a, s[r], slopeL, i, j, dcap);
+      float pr = __builtin_amdgcn_exp2f(t - l2v[aa][bb]);
+      if (partial && (i < qlo || i > qhi)) pr = 0.f;
+      p[r] = pr;
+      ds[r] = pr * (dp[r] - dv4[aa][bb]) * dcap;
+    }
+    bf16x8 pb[2], db[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      f32x8 x, y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = p[8 * kk + e];
+        y[e] = ds[8 * kk + e];
+      }
+      pb[kk] = __builtin_convertvector(x, bf16x8);
+      db[kk] = __builtin_convertvector(y, bf16x8);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries (two 16-row steps).
+    {
+      const uint16_t *ta = &sDOT[l32 * TP + hf * 8];
+      const uint16_t *qa = &sQT[l32 * TP + hf * 8];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int d0 = 0; d0 < NDB; ++d0) {
+          dvt[d0] = mfma32(
+              __builtin_bit_cast(bf16x8, *(const u32x4 *)(ta + d0 * 32 * TP + kk * 16)), pb[kk],
+              dvt[d0]);
+          dkt[d0] = mfma32(
+              __builtin_bit_cast(bf16x8, *(const u32x4 *)(qa + d0 * 32 * TP + kk * 16)), db[kk],
+              dkt[d0]);
+        }
+    }
+    __syncthreads();
+  }
+
+  if (j_ok) {
+    const size_t off = hbase + (size_t)j * D + 16 * hf;
+#pragma unroll
+    for (int d0 = 0; d0 < NDB; ++d0) {
+      store16<OUTF32>(a.dk, off + 32 * d0, dkt[d0] * a.scale);
+      store16<OUTF32>(a.dv, off + 32 * d0, dvt[d0]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ: one workgroup = 8 waves x 32 queries = one forward q-tile; it walks the q-tile's list of
+// non-empty 64-key tiles (the forward block table).
+template <int D, bool ALIBI, bool SOFTCAP, bool OUTF32>
+__global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int NT = 512;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int KP = pitch(D);    // LDS pitch of a K / V row
+  constexpr int TP = pitch(kBc);  // LDS pitch of a K^T row (d x 64 keys)
+  constexpr int RCH = kBc * (D / 8) / NT;
+  constexpr int TCH = D * (kBc / 8) / NT;
+  static_assert(kBr == 256 && kBc == 64, "kernel is written for 256 x 64 tiles");
+  static_assert(RCH >= 1 && TCH >= 1, "tile copies must cover the workgroup");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kBc * KP], sV[kBc * KP], sKT[D * TP];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
+  const int qt = blockIdx.x;
+  const int N = a.N;
+  const int qrow = qt * kBr + wave * 32 + l32;
+  const bool q_ok = qrow < N;
+  const MaskDesc md{a.kind, N, a.window, a.offs ? a.offs + (size_t)b * (a.max_docs + 1) : nullptr,
+                    a.max_docs};
+  int lo = 1, hi = 0;  // empty interval for rows past N
+  if (q_ok) {
+    lo = row_lo(md, qrow);
+    hi = row_hi(md, qrow);
+  }
+  const size_t hbase = (size_t)bh * N * D;
+  bf16x8 qf[NKS], df[NKS];  // B operands: Q^T and dO^T of this lane's query
+  {
+    const size_t off = hbase + (size_t)(q_ok ? qrow : 0) * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (q_ok) {
+        x = *(const u32x4 *)(a.q + off + ks * 16);
+        y = *(const u32x4 *)(a.dout + off + ks * 16);
+      }
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
+      df[ks] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  const float l2 = q_ok ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  const float dq_row = q_ok ? a.dvec[(size_t)bh * N + qrow] : 0.f;
+  const float slopeL = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+
+  int T;
+  const int32_t *lst = nullptr;
+  if (a.list) {
+    const int bm = (a.kind == kMaskDocument) ? b : 0;
+    const size_t row = (size_t)bm * a.n_qt + qt;
+    T = a.cnt[row];
+    lst = a.list + row * a.n_kt;
+  } else {
+    T = a.n_kt;
+  }
+
+  f32x16 dqt[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dqt[i] = f32x16{};
+
+  for (int t = 0; t < T; ++t) {
+    const int kt = lst ? lst[t] : t;
+#pragma unroll
+    for (int u = 0; u < RCH; ++u) {
+      const int c = tid + NT * u, r = c / (D / 8), ch = c % (D / 8);
+      const size_t src = hbase + (size_t)min(kt * kBc + r, N - 1) * D + ch * 8;
+      *(u32x4 *)&sK[pi_key(r) * KP + ch * 8] = *(const u32x4 *)(a.k + src);
+      *(u32x4 *)&sV[pi_key(r) * KP + ch * 8] = *(const u32x4 *)(a.v + src);
+    }
+#pragma unroll
+    for (int u = 0; u < TCH; ++u) {
+      const int c = tid + NT * u, r = c / (kBc / 8), ch = c % (kBc / 8);
+      *(u32x4 *)&sKT[r * TP + ch * 8] =
+          *(const u32x4 *)(a.kt + ((size_t)bh * D + r) * a.Npad + (size_t)kt * kBc + ch * 8);
+    }
+    __syncthreads();
+
+    // S^T = K Q^T and dP^T = V dO^T: register r of key block blk is key
+    // kt*Bc + 32*blk + 16*(r/8) + 8*hf + r%8, column = query qrow.
+    f32x16 s[2] = {}, dp[2] = {};
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const uint16_t *ka = &sK[(32 * blk + l32) * KP + hf * 8];
+      const uint16_t *va = &sV[(32 * blk + l32) * KP + hf * 8];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s[blk] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4 *)(ka + ks * 16)), qf[ks], s[blk]);
+        dp[blk] =
+            mfma32(__builtin_bit_cast(bf16x8, *(const u32x4 *)(va + ks * 16)), df[ks], dp[blk]);
+      }
+    }
+    const bool partial =
+        __builtin_amdgcn_ballot_w64(!(lo <= kt * kBc && hi >= kt * kBc + kBc - 1)) != 0;
+    bf16x8 db[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int blk = g >> 1, r = 8 * (g & 1) + e;
+        const int jj = kt * kBc + 32 * blk + 16 * (r >> 3) + 8 * hf + (r & 7);
+        float dcap;
+        const float tt = score2<ALIBI, SOFTCAP>(a, s[blk][r], slopeL, qrow, jj, dcap);
+        float pr = __builtin_amdgcn_exp2f(tt - l2);
+        if (partial && (jj < lo || jj > hi)) pr = 0.f;
+        y[e] = pr * (dp[blk][r] - dq_row) * dcap;
+      }
+      db[g] = __builtin_convertvector(y, bf16x8);
+    }
+    // dQ^T += K^T dS^T over the 64 keys (four 16-key steps).
+    {
+      const uint16_t *ta = &sKT[l32 * TP + hf * 8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int d0 = 0; d0 < NDB; ++d0)
+          dqt[d0] = mfma32(
+              __builtin_bit_cast(bf16x8, *(const u32x4 *)(ta + d0 * 32 * TP + g * 16)), db[g],
+              dqt[d0]);
+    }
+    __syncthreads();
+  }
+
+  if (q_ok) {
+    const size_t off = hbase + (size_t)qrow * D + 16 * hf;
+#pragma unroll
+    for (int d0 = 0; d0 < NDB; ++d0) store16<OUTF32>(a.dq, off + 32 * d0, dqt[d0] * a.scale);
+  }
+}
+
+template <int D, bool ALIBI, bool SOFTCAP, bool OUTF32>
+hipError_t launch_bwd_inst(const BwdArgs &a, hipStream_t s) {
+  const unsigned BH = (unsigned)(a.B * a.H);
+  bwd_dkdv_kernel<D, ALIBI, SOFTCAP, OUTF32>
+      <<<dim3((unsigned)((a.N + 127) / 128), BH), 256, 0, s>>>(a);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  bwd_dq_kernel<D, ALIBI, SOFTCAP, OUTF32><<<dim3((unsigned)a.n_qt, BH), 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int D, bool ALIBI, bool SOFTCAP>
+hipError_t launch_bwd_out(const BwdArgs &a, hipStream_t s) {
+  return a.out_f32 ? launch_bwd_inst<D, ALIBI, SOFTCAP, true>(a, s)
+                   : launch_bwd_inst<D, ALIBI, SOFTCAP, false>(a, s);
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs &a, bool alibi, bool softcap, hipStream_t s) {
+  if (alibi && softcap) return launch_bwd_out<D, true, true>(a, s);
+  if (alibi) return launch_bwd_out<D, true, false>(a, s);
+  if (softcap) return launch_bwd_out<D, false, true>(a, s);
+  return launch_bwd_out<D, false, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dot(const BwdArgs &a, int d, hipStream_t stream) {
+  const size_t rows = (size_t)a.B * a.H * a.N;
+  const int rpb = 256 / (d / 8);
+  const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+  if (d == 128)
+    bwd_dot_kernel<128><<<grid, 256, 0, stream>>>(a);
+  else
+    bwd_dot_kernel<64><<<grid, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs &a, int d, bool alibi, bool softcap, hipStream_t stream) {
+  if (d == 128) return launch_bwd_d<128>(a, alibi, softcap, stream);
+  return launch_bwd_d<64>(a, alibi, softcap, stream);
+}
+
+}  // namespace attn

@@ -1,0 +1,76 @@
+// Device helpers shared by the forward and backward kernels: operand types of the gfx950
+// 32x32x16 MFMAs, the register-layout permutations that let MFMA results feed the next MFMA
+// directly, and lane-pair reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+constexpr float kLn2 = 0.69314718055994531f;
+// s_getreg operand for HW_ID.SIMD_ID: register 4, bit offset 4, 2 bits.
+constexpr int kHwRegSimdId = (4) | (4 << 6) | ((2 - 1) << 11);
+constexpr float kTau = 8.0f;
+
+// Key permutation inside a 64-key tile: swap bits 2 and 3 (an involution).
+__device__ __forceinline__ int pi_key(int x) {
+  return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// Output-column permutation inside a 32-block of d: accumulator row i = 8a + 4h + b of the
+// 32x32 MFMA result (a = i>>3, h = (i>>2)&1, b = i&3) holds column 16h + 4a + b.
+__host__ __device__ constexpr int sigma_d(int i) {
+  return (((i >> 2) & 1) << 4) | ((i >> 3) << 2) | (i & 3);
+}
+
+// LDS row pitch (elements) for a row of `len` 2-byte elements: 16 bytes of padding.  With a
+// 256-, 128- or 144-byte row (len 128 or 64), rows r = 0..15 start at 16 distinct 16-byte bank
+// slots modulo 256 bytes (and r = 0..7 at 8 distinct slots modulo 128 bytes).
+constexpr int pitch(int len) { return len + 8; }
+
+// Marks a wave-uniform branch body as having a side effect so the compiler keeps the branch
+// instead of speculating the body into straight-line selects (the element mask and the output
+// rescale are rare and must cost nothing when skipped).
+__device__ __forceinline__ void keep_branch() { __asm__ volatile("" ::); }
+
+// max / sum of x over the lane pair (l, l ^ 32) that holds the two halves of one query's keys,
+// with v_permlane32_swap (no LDS round trip).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// bf16 bits -> fp16 bits; exact for |x| in [2^-14, 65504], saturating beyond (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_to_f16_bits(uint32_t b) {
+  float f = __uint_as_float(b << 16);
+  if (fabsf(f) > 65504.f) f = copysignf(65504.f, f);
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+}  // namespace
+}  // namespace attn

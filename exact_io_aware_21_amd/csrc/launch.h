@@ -35,8 +35,33 @@ struct FwdInstance {
   bool out_f32;
 };
 
+// X [BH][N][d] bf16 -> X^T [BH][d][Npad], keys contiguous, zero beyond N, d rows permuted within
+// 32-blocks (sigma_d); fp16 (saturating) or bf16 values.
+// Backward pass (bwd.hip).
+struct BwdArgs {
+  const uint16_t *q, *k, *v, *dout;  // bf16 [BH][N][D]
+  const void *o;                     // bf16 or fp32 [BH][N][D] (o_f32)
+  const float *lse;                  // fp32 [BH][N], natural log
+  const uint16_t *qt, *dot, *kt;     // Q^T, dO^T, K^T: bf16 [BH][D][Npad], d rows sigma-permuted
+  float *dvec;                       // fp32 [BH][N]: D_i = dO_i . O_i
+  void *dq, *dk, *dv;                // bf16 or fp32 [BH][N][D] (out_f32)
+  int B, H, N, Npad, n_qt, n_kt;
+  float scale;   // dQ = scale * dS K, dK = scale * dS^T Q
+  float c;       // scale * log2(e)
+  float cap_c1;  // soft-cap: 2 * scale * log2(e) / cap
+  float capL;    // soft-cap: cap * log2(e)
+  const float *slopes;
+  int kind, window, max_docs;
+  const int32_t *offs;
+  const int32_t *cnt, *list;  // forward block table (null for the unmasked kind)
+  bool o_f32, out_f32;
+};
+
+hipError_t launch_bwd_dot(const BwdArgs &a, int d, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, int d, bool alibi, bool softcap, hipStream_t stream);
+
 hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Npad, int d,
-                          hipStream_t stream);
+                          bool to_f16, hipStream_t stream);
 hipError_t launch_block_table(MaskDesc m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,
                               int8_t *cls, int32_t *cnt, int32_t *list, hipStream_t stream);
 hipError_t launch_fwd(const FwdInstance &inst, const FwdArgs &a, hipStream_t stream);

@@ -48,6 +48,40 @@ __host__ __device__ inline int doc_start(const int32_t *offs, int max_docs, int 
   return offs[lo];
 }
 
+// offs[r + 1] for the same r as doc_start: the first index of the next document.
+__host__ __device__ inline int doc_end(const int32_t *offs, int max_docs, int i) {
+  int lo = 0, hi = max_docs;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (offs[mid] <= i)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo < max_docs ? offs[lo + 1] : offs[max_docs];
+}
+
+// The same interval seen from a key j: the queries that may attend to it are [col_lo, col_hi]
+// (used by the backward pass, whose key-major kernel owns keys).
+__host__ __device__ inline int col_lo(const MaskDesc &m, int j) {
+  return m.kind == kMaskNone ? 0 : j;
+}
+
+__host__ __device__ inline int col_hi(const MaskDesc &m, int j) {
+  switch (m.kind) {
+    case kMaskWindow: {
+      const long long x = (long long)j + m.window - 1;
+      return x < m.N - 1 ? (int)x : m.N - 1;
+    }
+    case kMaskDocument: {
+      const int e = doc_end(m.offs, m.max_docs, j);
+      return (e < m.N ? e : m.N) - 1;
+    }
+    default:
+      return m.N - 1;
+  }
+}
+
 __host__ __device__ inline int row_lo(const MaskDesc &m, int i) {
   switch (m.kind) {
     case kMaskWindow: {

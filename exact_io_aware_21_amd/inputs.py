@@ -91,6 +91,13 @@ def draw_qkv(B: int, H: int, N: int, d: int, sigma: float, seed: int):
     return tuple(out)
 
 
+def draw_dout(B: int, H: int, N: int, d: int, seed: int) -> np.ndarray:
+    """The output gradient dO of a backward call: i.i.d. N(0, 1) rounded to bfloat16 bits
+    [B, H, N, d], from its own stream (seed, 99) so that Q, K, V are unchanged."""
+    rng = np.random.default_rng((seed, 99))
+    return f32_to_bf16_bits(rng.standard_normal((B, H, N, d), dtype=np.float32))
+
+
 def draw_doc_lengths(N: int, lo: int, hi: int, seed) -> list:
     """Document lengths, uniform integers on [lo, hi], drawn until they cover N tokens."""
     rng = np.random.default_rng(seed)

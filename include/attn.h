@@ -131,6 +131,32 @@ int attn_block_table(int B, int H, int N, int d, uint32_t variant, const attn_pa
 int attn_block_table_host(int B, int H, int N, int d, uint32_t variant, const attn_params *params,
                           int8_t *cls, int32_t *kv_cnt, int32_t *kv_list);
 
+/*
+ * attn_bwd -- the backward pass (page "FlashAttention/es", section "Paso hacia atrás y
+ * recomputación"): the gradients dQ, dK, dV of a loss whose gradient with respect to the
+ * forward output O is dout, for the same (scale, variant, params) as the forward call.  S and P
+ * are recomputed tile by tile from q, k and the saved log-sum-exp; no N x N matrix is stored.
+ *   q, k, v : device, bf16, [B][H][N][d], 16-byte aligned (the forward inputs).
+ *   o       : device, [B][H][N][d], the forward output, bf16 or fp32 per params->o_dtype.
+ *   lse     : device, fp32 [B][H][N], the forward's natural-log L (required).
+ *   dout    : device, bf16, [B][H][N][d], 16-byte aligned.
+ *   dq, dk, dv : device outputs, [B][H][N][d], bf16 or fp32 per params->o_dtype, 16-byte
+ *             aligned; every element is written (deterministically: no atomics).
+ *   B, H, N, d, scale, variant : as for attn_fwd; additionally B*H <= 65535.
+ *   params  : required; workspace of >= attn_bwd_workspace_size() bytes, 256-byte aligned.
+ *             timing_events, if set, bracket the two main backward kernels.
+ * Precision: all products are bf16 MFMAs with fp32 accumulation; P (<= 1) and dS are rounded
+ * to bf16 as operands, D_i = dO_i . O_i is formed in fp32 from the given o.
+ * Returns ATTN_OK or an error code; no HIP call is made for invalid arguments.
+ */
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             const void *dout, void *dq, void *dk, void *dv, int B, int H, int N, int d,
+             float scale, uint32_t variant, const attn_params *params, void *stream);
+
+/* Bytes of workspace attn_bwd needs (0 on invalid arguments): D (fp32 [B][H][N]), transposed
+   bf16 copies of Q, dO and K, and the block table. */
+size_t attn_bwd_workspace_size(int B, int H, int N, int d, uint32_t variant);
+
 const char *attn_strerror(int code);
 const char *attn_last_error(void);
 

@@ -5,9 +5,9 @@ CPU-baseline leg of bench.py, never by the HIP path.  It shares no code with tha
 """
 from .attention import (MASKS, allowed, allowed_pair_count, attention, attention_blocked,
                         decode_bf16, doc_index, scores)
-from .backward import attention_backward, backward_row_dot
+from .backward import attention_backward, backward_magnitudes, backward_row_dot
 from .tiles import tile_class_counts, tile_table
 
 __all__ = ["MASKS", "allowed", "allowed_pair_count", "attention", "attention_backward",
-           "attention_blocked", "backward_row_dot", "decode_bf16", "doc_index", "scores",
+           "attention_blocked", "backward_magnitudes", "backward_row_dot", "decode_bf16", "doc_index", "scores",
            "tile_class_counts", "tile_table"]

@@ -85,3 +85,38 @@ def backward_row_dot(o, do):
     """D_i = sum_c dO_ic O_ic: the row term of the softmax Jacobian written with the output
     (equal to sum_j P_ij dP_ij because O_i = sum_j P_ij V_j)."""
     return (np.asarray(o, dtype=np.float64) * np.asarray(do, dtype=np.float64)).sum(axis=-1)
+
+
+def backward_magnitudes(q, k, v, do, scale, mask="none", window=0, softcap=0.0, slopes=None,
+                        doc_offsets=None, heads=None):
+    """Sums of absolute terms behind each gradient element (float64, [B, H, N, d] each):
+         M_dV = |P|^T |dO|,   M_dK = scale |dT'|^T |Q|,   M_dQ = scale |dT'| |K|,
+    with |dT'| = (|dS| + P * sum_c |dO_c O_c|) * |1 - (s_c/cap)^2|.  Rounding one operand of every
+    product term to a relative precision u changes a gradient element by at most u times its M
+    (the P * sum|dO O| part covers D_i = dO_i . O_i formed from an O rounded the same way).
+    These are error scales for comparing a reduced-precision implementation, not gradients."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, N, d = q.shape
+    mq = np.full(q.shape, np.nan)
+    mk = np.full(k.shape, np.nan)
+    mv = np.full(v.shape, np.nan)
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    for b, h in heads:
+        off = None if doc_offsets is None else np.asarray(doc_offsets)[b]
+        p, s_c = _head_forward(q[b, h], k[b, h], v[b, h], scale, h, N, mask, window, softcap,
+                               slopes, off)
+        g = do[b, h]
+        o = p @ v[b, h]
+        dp = g @ v[b, h].T
+        ds = p * (dp - (p * dp).sum(axis=1)[:, None])
+        mds = np.abs(ds) + p * np.abs(g * o).sum(axis=1)[:, None]
+        if softcap:
+            mds = mds * np.abs(1.0 - (s_c / float(softcap)) ** 2)
+        mv[b, h] = p.T @ np.abs(g)
+        mk[b, h] = float(scale) * (mds.T @ np.abs(q[b, h]))
+        mq[b, h] = float(scale) * (mds @ np.abs(k[b, h]))
+    return mq, mk, mv

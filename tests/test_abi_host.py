@@ -187,3 +187,58 @@ def test_host_table_document_workload():
     ref = oracle.tile_table(w.N, Br, Bc, "document", 0, off)
     for a, b in zip(ours, ref):
         assert np.array_equal(a, b)
+
+
+# --- backward entry point ---------------------------------------------------------------------
+def test_bwd_workspace_size():
+    # D (fp32 B*H*N), Q^T, dO^T, K^T (bf16 B*H*d*Npad each), then the table for masked kinds.
+    al = lambda x: (x + 255) // 256 * 256
+    B, H, N, d = 2, 3, 1000, 128
+    npad = 16 * 64
+    pack = al(B * H * d * npad * 2)
+    base = al(B * H * N * 4) + 3 * pack
+    assert attn.attn_bwd_workspace_size(B, H, N, d, attn.ATTN_MASK_NONE) == base
+    rows = 4
+    assert attn.attn_bwd_workspace_size(B, H, N, d, attn.ATTN_MASK_CAUSAL) == \
+        base + al(rows * 16) + al(rows * 4) + al(rows * 16 * 4)
+    assert attn.attn_bwd_workspace_size(1, 1, 16, 80, 0) == 0
+
+
+def _call_bwd(ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, variant=0, params="default"):
+    L = attn.lib()
+    p = attn.attn_params()
+    p.workspace = 256
+    p.workspace_bytes = 1 << 40
+    pp = ctypes.byref(p) if params == "default" else params
+    args = {"q": 16, "k": 16, "v": 16, "o": 16, "lse": 16, "dout": 16, "dq": 16, "dk": 16,
+            "dv": 16}
+    args.update(ptrs or {})
+    return L.attn_bwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dout"],
+                      args["dq"], args["dk"], args["dv"], B, H, N, d, scale, variant, pp, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"ptrs": {"lse": None}}, attn.ATTN_ERR_INVALID_ARG),
+    ({"ptrs": {"dout": None}}, attn.ATTN_ERR_INVALID_ARG),
+    ({"ptrs": {"dk": 8}}, attn.ATTN_ERR_INVALID_ARG),
+    ({"ptrs": {"lse": 2}}, attn.ATTN_ERR_INVALID_ARG),
+    ({"N": 0}, attn.ATTN_ERR_INVALID_ARG),
+    ({"d": 96}, attn.ATTN_ERR_INVALID_ARG),
+    ({"B": 300, "H": 300}, attn.ATTN_ERR_INVALID_ARG),
+    ({"scale": float("nan")}, attn.ATTN_ERR_INVALID_ARG),
+    ({"params": None}, attn.ATTN_ERR_INVALID_ARG),
+])
+def test_bwd_rejects_invalid_arguments(kw, code):
+    assert _call_bwd(**kw) == code
+    assert attn.lib().attn_last_error() != b""
+
+
+def test_bwd_rejects_small_workspace():
+    p = attn.attn_params()
+    p.workspace, p.workspace_bytes = 256, 100
+    assert _call_bwd(params=ctypes.byref(p)) == attn.ATTN_ERR_WORKSPACE
+
+
+@pytest.mark.skipif(_gpu_present(), reason="only meaningful on a host without a GPU")
+def test_bwd_valid_call_without_gpu_reports_unsupported_device():
+    assert _call_bwd() == attn.ATTN_ERR_UNSUPPORTED_DEVICE
