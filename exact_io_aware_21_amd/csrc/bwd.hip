@@ -14,6 +14,9 @@
 // ever summed across workgroups.
 //
 // gfx950 mapping (same devices as the forward kernel, see fwd.hip):
+//  * The key-major kernel double-buffers its LDS tiles: the next step's global loads are in
+//    flight in VGPRs while the current step computes, and are written to the idle buffer before
+//    the step's barrier.
 //  * Every product is a v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Q, K, V, dO are the
 //    exact bf16 inputs; P (<= 1) and dS are rounded to bf16 as MFMA operands.
 //  * The recomputed tile is built so that its lane owns one row of the output being accumulated:
@@ -119,9 +122,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int RCH = QS * (D / 8) / NT;  // row-tile chunks per thread
   constexpr int TCH = D * (QS / 8) / NT;  // transposed-tile chunks per thread
   static_assert(RCH >= 1 && TCH >= 1, "tile copies must cover the workgroup");
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[QS * RP], sDO[QS * RP];
-  __shared__ __attribute__((aligned(16))) uint16_t sQT[D * TP], sDOT[D * TP];
-  __shared__ __attribute__((aligned(16))) float sL2[QS], sDv[QS];
+  // Double-buffered query-step tiles: step s is read from buffer s & 1 while the loads of step
+  // s + 1 are in flight into VGPRs; they are written to the other buffer after the compute.
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][QS * RP], sDO[2][QS * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t sQT[2][D * TP], sDOT[2][D * TP];
+  __shared__ __attribute__((aligned(16))) float sL2[2][QS], sDv[2][QS];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
@@ -160,37 +165,65 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dkt[i] = dvt[i] = f32x16{};
 
-  for (int qs = qs_begin; qs < qs_end; ++qs) {
+  // Query-step staging: Q and dO rows (rows pi-permuted; past N: row N - 1, masked below), the
+  // transposed packs, and L (base 2) and D of the 32 queries.
+  u32x4 rq[RCH], rdo[RCH], rqt[TCH], rdot[TCH];
+  float rl2 = 0.f, rdv = 0.f;
+  auto fetch = [&](int qs) {
     const int q0 = qs * QS;
-    // Stage the query step: Q and dO rows (rows pi-permuted; past N: row N - 1, masked below),
-    // the transposed packs, and L (base 2) and D of the 32 queries.
 #pragma unroll
     for (int u = 0; u < RCH; ++u) {
       const int c = tid + NT * u, r = c / (D / 8), ch = c % (D / 8);
       const size_t src = hbase + (size_t)min(q0 + r, N - 1) * D + ch * 8;
-      *(u32x4 *)&sQ[pi_key(r) * RP + ch * 8] = *(const u32x4 *)(a.q + src);
-      *(u32x4 *)&sDO[pi_key(r) * RP + ch * 8] = *(const u32x4 *)(a.dout + src);
+      rq[u] = *(const u32x4 *)(a.q + src);
+      rdo[u] = *(const u32x4 *)(a.dout + src);
     }
 #pragma unroll
     for (int u = 0; u < TCH; ++u) {
       const int c = tid + NT * u, r = c / (QS / 8), ch = c % (QS / 8);
       const size_t src = ((size_t)bh * D + r) * a.Npad + q0 + ch * 8;
-      *(u32x4 *)&sQT[r * TP + ch * 8] = *(const u32x4 *)(a.qt + src);
-      *(u32x4 *)&sDOT[r * TP + ch * 8] = *(const u32x4 *)(a.dot + src);
+      rqt[u] = *(const u32x4 *)(a.qt + src);
+      rdot[u] = *(const u32x4 *)(a.dot + src);
     }
     if (tid < QS) {
       const int i = q0 + tid;
-      sL2[tid] = i < N ? a.lse[(size_t)bh * N + i] * kLog2e : 0.f;
-      sDv[tid] = i < N ? a.dvec[(size_t)bh * N + i] : 0.f;
+      rl2 = i < N ? a.lse[(size_t)bh * N + i] * kLog2e : 0.f;
+      rdv = i < N ? a.dvec[(size_t)bh * N + i] : 0.f;
     }
-    __syncthreads();
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < RCH; ++u) {
+      const int c = tid + NT * u, r = c / (D / 8), ch = c % (D / 8);
+      *(u32x4 *)&sQ[buf][pi_key(r) * RP + ch * 8] = rq[u];
+      *(u32x4 *)&sDO[buf][pi_key(r) * RP + ch * 8] = rdo[u];
+    }
+#pragma unroll
+    for (int u = 0; u < TCH; ++u) {
+      const int c = tid + NT * u, r = c / (QS / 8), ch = c % (QS / 8);
+      *(u32x4 *)&sQT[buf][r * TP + ch * 8] = rqt[u];
+      *(u32x4 *)&sDOT[buf][r * TP + ch * 8] = rdot[u];
+    }
+    if (tid < QS) {
+      sL2[buf][tid] = rl2;
+      sDv[buf][tid] = rdv;
+    }
+  };
+  if (qs_begin < qs_end) {
+    fetch(qs_begin);
+    stage(0);
+  }
+  __syncthreads();
 
+  for (int qs = qs_begin; qs < qs_end; ++qs) {
+    const int q0 = qs * QS, buf = (qs - qs_begin) & 1;
+    if (qs + 1 < qs_end) fetch(qs + 1);
     // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys: accumulator register r
     // (row 8(r/4) + 4 hf + r%4 of the pi-permuted tile) is query q0 + qq(r), column = key j.
     f32x16 s = {}, dp = {};
     {
-      const uint16_t *qa = &sQ[l32 * RP + hf * 8];
-      const uint16_t *da = &sDO[l32 * RP + hf * 8];
+      const uint16_t *qa = &sQ[buf][l32 * RP + hf * 8];
+      const uint16_t *da = &sDO[buf][l32 * RP + hf * 8];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         s = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4 *)(qa + ks * 16)), kf[ks], s);
@@ -201,8 +234,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
       const int base = 16 * (aa >> 1) + 8 * hf + 4 * (aa & 1);
-      l2v[aa] = *(const f32x4 *)&sL2[base];
-      dv4[aa] = *(const f32x4 *)&sDv[base];
+      l2v[aa] = *(const f32x4 *)&sL2[buf][base];
+      dv4[aa] = *(const f32x4 *)&sDv[buf][base];
     }
     const bool partial =
         __builtin_amdgcn_ballot_w64(!(qlo <= q0 && qhi >= q0 + QS - 1)) != 0;
@@ -232,8 +265,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     }
     // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries (two 16-row steps).
     {
-      const uint16_t *ta = &sDOT[l32 * TP + hf * 8];
-      const uint16_t *qa = &sQT[l32 * TP + hf * 8];
+      const uint16_t *ta = &sDOT[buf][l32 * TP + hf * 8];
+      const uint16_t *qa = &sQT[buf][l32 * TP + hf * 8];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -246,6 +279,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
               dkt[d0]);
         }
     }
+    if (qs + 1 < qs_end) stage(buf ^ 1);
     __syncthreads();
   }
 
@@ -272,6 +306,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   constexpr int TCH = D * (kBc / 8) / NT;
   static_assert(kBr == 256 && kBc == 64, "kernel is written for 256 x 64 tiles");
   static_assert(RCH >= 1 && TCH >= 1, "tile copies must cover the workgroup");
+  // Single-buffered key tiles (with 8 waves per workgroup the register budget has no room for
+  // a prefetch; measured faster than double buffering).
   __shared__ __attribute__((aligned(16))) uint16_t sK[kBc * KP], sV[kBc * KP], sKT[D * TP];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
