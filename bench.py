@@ -1,6 +1,7 @@
 """Benchmark of the attention forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--cold] [--pass fwd|bwd]
 
 A step is one attn_fwd call over one batch of seeded synthetic input already resident in HBM:
 the V transpose-pack kernel, the block-table kernel (masked kinds) and the forward kernel.
@@ -14,6 +15,10 @@ throughput target is quoted on).  The metric counts only unmasked FLOPs: 4*d per
 The "roofline" object is for the forward kernel alone: algorithmic FLOPs per launch divided by
 its average duration, measured with a HIP event pair the library records around that kernel on
 the same stream, against the published dense bf16 MFMA peak of MI355X.
+
+--cold writes a 512 MiB buffer before every step (more than L2 and the Infinity Cache hold) and
+times each call alone with its own event pair: the cold-cache figure for the short, HBM-bound
+workloads.  The default is warm: back-to-back calls.
 
 The "cpu_baseline" object times the fp64 CPU oracle (a plain, untuned reference) on the host
 cores on a bounded sample of the same workload, in the same unit.
@@ -31,9 +36,11 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
+MAX_SCLK_MHZ = 2400.0      # MI355X peak engine clock, the one the MFMA peak is quoted at
 METRIC = "attention fwd TFLOP/s (unmasked FLOPs) and % of MFMA peak, 1 MI355X"
 DEFAULT_WORKLOAD = "causal_h32_n16384_d128"
-KERNEL_SOURCES = ["exact_io_aware_21_amd/csrc/fwd.hip", "exact_io_aware_21_amd/csrc/tiles.h",
+KERNEL_SOURCES = ["exact_io_aware_21_amd/csrc/fwd.hip", "exact_io_aware_21_amd/csrc/kcommon.h",
+                  "exact_io_aware_21_amd/csrc/tiles.h",
                   "exact_io_aware_21_amd/csrc/launch.h"]
 
 
@@ -105,6 +112,61 @@ def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv
     print(json.dumps(rec))
 
 
+class SclkSampler:
+    """Samples the GPU core clock in a background thread while a timed region runs: the current
+    level of the driver's `pp_dpm_sclk` file in sysfs (the line marked '*'), every `period_s`.
+    The published MFMA peak assumes the 2.4 GHz maximum clock; under sustained matrix-core load the
+    clock settles lower, and this records where."""
+
+    def __init__(self, period_s=0.005):
+        import glob
+        import threading
+        self.period_s = period_s
+        self.samples = []
+        self.path = None
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            if self._read(path) is not None:
+                self.path = path
+                break
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _read(path):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            mhz = self._read(self.path)
+            if mhz is not None:
+                self.samples.append(mhz)
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.path:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        x = sorted(self.samples)
+        return {"median": x[len(x) // 2], "min": x[0], "max": x[-1], "samples": len(x),
+                "source": self.path}
+
+
 def cpu_baseline(w, inp, budget_s=20.0, chunk=2048):
     """The fp64 oracle on host cores, over whole heads in order (query rows in chunks of `chunk`)
     until `budget_s` has elapsed.  Throughput in the metric's unit (unmasked TFLOP/s)."""
@@ -171,12 +233,14 @@ def bench_bwd(args, w, inp, q, k, v, o, lse, var, slopes, offs, dev):
         b.record()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
-    for i in range(K):
-        attn.attn_bwd(q, k, v, o, lse, g, dq, dk, dv, inp["scale"], var, timing_events=kev[i],
-                      **kw)
-    end.record()
-    torch.cuda.synchronize()
+    sclk = SclkSampler()
+    with sclk:
+        start.record()
+        for i in range(K):
+            attn.attn_bwd(q, k, v, o, lse, g, dq, dk, dv, inp["scale"], var,
+                          timing_events=kev[i], **kw)
+        end.record()
+        torch.cuda.synchronize()
     step_ms = start.elapsed_time(end) / K
     kern_ms = sum(a.elapsed_time(b) for a, b in kev) / K
     flops = 10.0 * w.d * allowed_pairs(w, inp["doc_offsets"])
@@ -190,7 +254,8 @@ def bench_bwd(args, w, inp, q, k, v, o, lse, var, slopes, offs, dev):
         "data": "synthetic (seeded N(0, sigma^2) Q/K/V and N(0, 1) dO rounded to bf16)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
                    "window": w.window, "alibi": w.alibi, "softcap": w.softcap,
-                   "unmasked_gflop": round(flops / 1e9, 3), "bwd_kernels_ms": round(kern_ms, 4)},
+                   "unmasked_gflop": round(flops / 1e9, 3), "bwd_kernels_ms": round(kern_ms, 4),
+                   "sclk_mhz": sclk.summary()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
@@ -202,9 +267,12 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)  # also lets the clock settle
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MiB buffer before every step (evicts L2 and the 256 MB "
+                         "Infinity Cache) and time each call alone: the cold-cache HBM figure")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="bwd: time attn_bwd instead (10 d FLOPs per allowed pair; no CPU leg)")
     ap.add_argument("--traffic", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH",
@@ -253,24 +321,43 @@ def main():
     K = args.steps
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
-    for a, b in kev:  # torch creates the underlying hipEvent on the first record
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K if args.cold else 0)]
+    for a, b in kev + cev:  # torch creates the underlying hipEvent on the first record
         a.record()
         b.record()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
-    for i in range(K):
-        attn.attn_fwd(q, k, v, o, lse, inp["scale"], var, timing_events=kev[i], **kw)
-    end.record()
-    torch.cuda.synchronize()
-    step_ms = start.elapsed_time(end) / K
-    kern_ms = sum(a.elapsed_time(b) for a, b in kev) / K
+    sclk = SclkSampler()
+    with sclk:  # sampled until the device has finished the timed work
+        start.record()
+        for i in range(K):
+            if args.cold:
+                flush.fill_(i & 255)
+                cev[i][0].record()
+            attn.attn_fwd(q, k, v, o, lse, inp["scale"], var, timing_events=kev[i], **kw)
+            if args.cold:
+                cev[i][1].record()
+        end.record()
+        torch.cuda.synchronize()
+    if args.cold:  # the flush is not part of a step: time the calls alone
+        step_ms = sum(a.elapsed_time(b) for a, b in cev) / K
+    else:
+        step_ms = start.elapsed_time(end) / K
+    kern = sorted(a.elapsed_time(b) for a, b in kev)
+    kern_ms = sum(kern) / K
 
     flops = 4.0 * w.d * allowed_pairs(w, inp["doc_offsets"])
     hbm_bytes = w.B * w.H * w.N * (4 * w.d * 2 + 4)  # Q, K, V read; O (bf16) and L written
     value = flops / (step_ms * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
     traffic = traffic_from_profile(w.name)
+    sclk_rec = sclk.summary()
+    if sclk_rec:  # the same peak scaled to the clock the device ran at
+        sclk_rec["mfma_peak_at_median_tflops"] = round(PEAK_BF16_TFLOPS * sclk_rec["median"] /
+                                                       MAX_SCLK_MHZ, 1)
+        sclk_rec["frac_of_that_peak"] = round(achieved / sclk_rec["mfma_peak_at_median_tflops"], 4)
     mfma_bound = flops / hbm_bytes > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -289,7 +376,12 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
                    "window": w.window, "alibi": w.alibi, "softcap": w.softcap,
                    "unmasked_gflop": round(flops / 1e9, 3),
-                   "fwd_kernel_ms": round(kern_ms, 4)},
+                   "fwd_kernel_ms": round(kern_ms, 4),
+                   "fwd_kernel_ms_median": round(kern[K // 2], 4),
+                   "fwd_kernel_ms_min": round(kern[0], 4),
+                   "cache": "cold: 512 MiB written before each call" if args.cold else "warm",
+                   "compulsory_hbm_bytes": hbm_bytes,
+                   "sclk_mhz": sclk_rec},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -160,6 +160,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       kf[ks] = __builtin_bit_cast(bf16x8, x);
       vf[ks] = __builtin_bit_cast(bf16x8, y);
     }
+    // Settle these loads here, once.  Otherwise the wait for them lands on their first use
+    // inside the loop, where it also waits for the next step's tile loads in flight.
+    __builtin_amdgcn_s_waitcnt(0);
   }
   f32x16 dkt[NDB], dvt[NDB];
 #pragma unroll
@@ -185,11 +188,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       rqt[u] = *(const u32x4 *)(a.qt + src);
       rdot[u] = *(const u32x4 *)(a.dot + src);
     }
-    if (tid < QS) {
-      const int i = q0 + tid;
-      rl2 = i < N ? a.lse[(size_t)bh * N + i] * kLog2e : 0.f;
-      rdv = i < N ? a.dvec[(size_t)bh * N + i] : 0.f;
-    }
+    // Every lane loads (clamped index, no branch) so that no wait for these loads is placed
+    // before the step's compute: the loads stay in flight until stage() writes them.
+    const size_t li = (size_t)bh * N + min(q0 + (tid & (QS - 1)), N - 1);
+    rl2 = a.lse[li];
+    rdv = a.dvec[li];
   };
   auto stage = [&](int buf) {
 #pragma unroll
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       *(u32x4 *)&sDOT[buf][r * TP + ch * 8] = rdot[u];
     }
     if (tid < QS) {
-      sL2[buf][tid] = rl2;
+      sL2[buf][tid] = rl2 * kLog2e;
       sDv[buf][tid] = rdv;
     }
   };
@@ -340,15 +343,18 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   }
   const float l2 = q_ok ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
   const float dq_row = q_ok ? a.dvec[(size_t)bh * N + qrow] : 0.f;
+  __builtin_amdgcn_s_waitcnt(0);  // settle the loads above once, outside the loop
   const float slopeL = ALIBI ? a.slopes[h] * kLog2e : 0.f;
 
+  // The key-tile list (written by the table kernel before this launch): read through the
+  // constant address space, i.e. with scalar loads, so the loop below is wave-uniform.
   int T;
-  const int32_t *lst = nullptr;
+  const_i32 *lst = nullptr;
   if (a.list) {
     const int bm = (a.kind == kMaskDocument) ? b : 0;
     const size_t row = (size_t)bm * a.n_qt + qt;
-    T = a.cnt[row];
-    lst = a.list + row * a.n_kt;
+    T = ((const_i32 *)a.cnt)[row];
+    lst = (const_i32 *)a.list + row * a.n_kt;
   } else {
     T = a.n_kt;
   }

@@ -7,6 +7,9 @@
 //   make micro && ./micro
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <vector>
+
 #include <cstdio>
 #include <cstdlib>
 
@@ -42,6 +45,34 @@ __global__ __launch_bounds__(256) void mfma_rate(float *out, float seed) {
   float s = 0.f;
   for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
   if (s == 1234.5f) out[threadIdx.x] = s;
+}
+
+// The same MFMA stream, 4x longer, with the shader clock measured inside the kernel: thread 0 of
+// each workgroup records the elapsed s_memtime cycles (core clock) and s_memrealtime ticks
+// (constant wall clock) around its loop.
+__global__ __launch_bounds__(256) void mfma_clock(unsigned long long *clk, float seed) {
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(seed * (threadIdx.x + i));
+    b[i] = (__bf16)(seed * (i + 1));
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < 4 * kIters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    clk[2 * blockIdx.x] = t1 - t0;
+    clk[2 * blockIdx.x + 1] = (r1 - r0) + (s == 1234.5f);
+  }
 }
 
 // 8 independent chains of v_exp_f32 per lane.
@@ -227,6 +258,29 @@ int main() {
     ms = time_ms([&] { fma_rate<<<grid, 256>>>(out, seed); }, 5);
     printf("v_fma_f32, %d wave/SIMD: %.1f Gop/s = %.2f lane-ops/clk/CU at 2.4 GHz\n", wg_per_cu,
            ops / ms / 1e6, ops / (ms * 1e-3) / 2.4e9 / cus);
+  }
+  // The core clock under sustained MFMA load (one wave per SIMD), from inside the kernel.
+  {
+    int wall_khz = 0;
+    CHECK(hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, 0));
+    const int grid = cus;
+    unsigned long long *clk;
+    CHECK(hipMalloc(&clk, 2 * grid * sizeof(unsigned long long)));
+    const float ms = time_ms([&] { mfma_clock<<<grid, 256>>>(clk, seed); }, 3);
+    std::vector<unsigned long long> h(2 * grid);
+    CHECK(hipMemcpy(h.data(), clk, h.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+    std::vector<double> mhz, cyc;
+    for (int g = 0; g < grid; ++g) {
+      mhz.push_back((double)h[2 * g] / (double)h[2 * g + 1] * wall_khz / 1e3);
+      cyc.push_back((double)h[2 * g] / (4.0 * kIters * 4));
+    }
+    std::sort(mhz.begin(), mhz.end());
+    std::sort(cyc.begin(), cyc.end());
+    const double flops = (double)grid * 4 * 4 * kIters * 4 * 32768.0;
+    printf("core clock under MFMA load (s_memtime / s_memrealtime at %d kHz): median %.0f MHz "
+           "(min %.0f, max %.0f); %.2f core cycles per 32x32x16 MFMA; %.1f TFLOP/s\n",
+           wall_khz, mhz[grid / 2], mhz[0], mhz[grid - 1], cyc[grid / 2], flops / ms / 1e9);
+    CHECK(hipFree(clk));
   }
   // Throughput-bound VALU: 4 waves per SIMD (four 256-thread workgroups per CU).
   {
