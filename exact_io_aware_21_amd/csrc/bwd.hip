@@ -35,6 +35,9 @@ namespace attn {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw (unformatted, stride 0) buffer resource on gfx9-family parts: 32-bit data
+// format, no swizzle.  Loads past the resource's byte size return zero.
+constexpr int kBufferWord3 = 0x00020000;
 
 // D_i = sum_c dO_ic O_ic (fp32).  One group of D/8 lanes per row, 16-byte loads.
 template <int D>
@@ -143,7 +146,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   }
   // Query steps the workgroup visits: the union over its keys (both bounds grow with j).
   const int jl = min(key0 + 4 * KPW, N) - 1;
-  const int qs_begin = col_lo(md, key0) / QS, qs_end = col_hi(md, jl) / QS + 1;
+  // (wave-uniform: read into scalars, so the loop below is a scalar loop)
+  const int qs_begin = __builtin_amdgcn_readfirstlane(col_lo(md, key0) / QS);
+  const int qs_end = __builtin_amdgcn_readfirstlane(col_hi(md, jl) / QS + 1);
 
   const size_t hbase = (size_t)bh * N * D;
   const float slopeL = ALIBI ? a.slopes[h] * kLog2e : 0.f;
@@ -168,31 +173,54 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dkt[i] = dvt[i] = f32x16{};
 
-  // Query-step staging: Q and dO rows (rows pi-permuted; past N: row N - 1, masked below), the
-  // transposed packs, and L (base 2) and D of the 32 queries.
+  // Query-step staging: Q and dO rows (rows pi-permuted), the transposed packs, and L (base 2)
+  // and D of the 32 queries.  The loads are buffer loads: the step moves a scalar base (the
+  // resource), the per-lane byte offsets are fixed, and rows past N lie beyond the resource's
+  // size, so they read as zero (and are masked below).
   u32x4 rq[RCH], rdo[RCH], rqt[TCH], rdot[TCH];
   float rl2 = 0.f, rdv = 0.f;
+  int voff_r[RCH], voff_t[TCH];
+#pragma unroll
+  for (int u = 0; u < RCH; ++u) {
+    const int c = tid + NT * u, r = c / (D / 8), ch = c % (D / 8);
+    voff_r[u] = (r * D + ch * 8) * 2;
+  }
+#pragma unroll
+  for (int u = 0; u < TCH; ++u) {
+    const int c = tid + NT * u, r = c / (QS / 8), ch = c % (QS / 8);
+    voff_t[u] = (r * a.Npad + ch * 8) * 2;
+  }
+  const int voff_l = (tid & (QS - 1)) * 4;
   auto fetch = [&](int qs) {
     const int q0 = qs * QS;
+    const int rows_left = N - q0;  // >= 1
+    const auto rsq = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.q + hbase + (size_t)q0 * D), 0, rows_left * D * 2, kBufferWord3);
+    const auto rsd = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.dout + hbase + (size_t)q0 * D), 0, rows_left * D * 2, kBufferWord3);
+    const size_t tbase = (size_t)bh * D * a.Npad + q0;
+    const int tbytes = (D * a.Npad - q0) * 2;
+    const auto rsqt = __builtin_amdgcn_make_buffer_rsrc((void *)(a.qt + tbase), 0, tbytes,
+                                                        kBufferWord3);
+    const auto rsdt = __builtin_amdgcn_make_buffer_rsrc((void *)(a.dot + tbase), 0, tbytes,
+                                                        kBufferWord3);
 #pragma unroll
     for (int u = 0; u < RCH; ++u) {
-      const int c = tid + NT * u, r = c / (D / 8), ch = c % (D / 8);
-      const size_t src = hbase + (size_t)min(q0 + r, N - 1) * D + ch * 8;
-      rq[u] = *(const u32x4 *)(a.q + src);
-      rdo[u] = *(const u32x4 *)(a.dout + src);
+      rq[u] = __builtin_amdgcn_raw_buffer_load_b128(rsq, voff_r[u], 0, 0);
+      rdo[u] = __builtin_amdgcn_raw_buffer_load_b128(rsd, voff_r[u], 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < TCH; ++u) {
-      const int c = tid + NT * u, r = c / (QS / 8), ch = c % (QS / 8);
-      const size_t src = ((size_t)bh * D + r) * a.Npad + q0 + ch * 8;
-      rqt[u] = *(const u32x4 *)(a.qt + src);
-      rdot[u] = *(const u32x4 *)(a.dot + src);
+      rqt[u] = __builtin_amdgcn_raw_buffer_load_b128(rsqt, voff_t[u], 0, 0);
+      rdot[u] = __builtin_amdgcn_raw_buffer_load_b128(rsdt, voff_t[u], 0, 0);
     }
-    // Every lane loads (clamped index, no branch) so that no wait for these loads is placed
-    // before the step's compute: the loads stay in flight until stage() writes them.
-    const size_t li = (size_t)bh * N + min(q0 + (tid & (QS - 1)), N - 1);
-    rl2 = a.lse[li];
-    rdv = a.dvec[li];
+    const size_t lbase = (size_t)bh * N + q0;
+    const auto rsl = __builtin_amdgcn_make_buffer_rsrc((void *)(a.lse + lbase), 0, rows_left * 4,
+                                                       kBufferWord3);
+    const auto rsv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.dvec + lbase), 0,
+                                                       rows_left * 4, kBufferWord3);
+    rl2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsl, voff_l, 0, 0));
+    rdv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsv, voff_l, 0, 0));
   };
   auto stage = [&](int buf) {
 #pragma unroll
@@ -221,17 +249,42 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   for (int qs = qs_begin; qs < qs_end; ++qs) {
     const int q0 = qs * QS, buf = (qs - qs_begin) & 1;
     if (qs + 1 < qs_end) fetch(qs + 1);
-    // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys: accumulator register r
-    // (row 8(r/4) + 4 hf + r%4 of the pi-permuted tile) is query q0 + qq(r), column = key j.
-    f32x16 s = {}, dp = {};
-    {
-      const uint16_t *qa = &sQ[buf][l32 * RP + hf * 8];
-      const uint16_t *da = &sDO[buf][l32 * RP + hf * 8];
+    // The step's 32 MFMAs read one A fragment (16 bytes a lane) each from LDS: first the
+    // score products S = Q K^T and dP = dO V^T (steps 0..15: k-step i/2, dP when i is odd),
+    // then dV^T += dO^T P and dK^T += Q^T dS (steps 16..31: 16-query half kk, d block d0, dK
+    // when i is odd).  Fragment i + kDepth is read while MFMA i runs, across the softmax too.
+    constexpr int kDepth = 4;
+    constexpr int NA = 2 * NKS, NS = NA + 4 * NDB;
+    const uint16_t *qa = &sQ[buf][l32 * RP + hf * 8];
+    const uint16_t *da = &sDO[buf][l32 * RP + hf * 8];
+    const uint16_t *ta = &sDOT[buf][l32 * TP + hf * 8];
+    const uint16_t *qta = &sQT[buf][l32 * TP + hf * 8];
+    auto frag = [&](int i) -> u32x4 {
+      if (i < NA) return *(const u32x4 *)(((i & 1) ? da : qa) + (i >> 1) * 16);
+      const int b = i - NA, kk = b / (2 * NDB), d0 = (b >> 1) % NDB;
+      return *(const u32x4 *)(((b & 1) ? qta : ta) + d0 * 32 * TP + kk * 16);
+    };
+    u32x4 win[kDepth];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        s = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4 *)(qa + ks * 16)), kf[ks], s);
-        dp = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4 *)(da + ks * 16)), vf[ks], dp);
-      }
+    for (int i = 0; i < kDepth; ++i) win[i] = frag(i);
+    // S and dP: accumulator register r (row 8(r/4) + 4 hf + r%4 of the pi-permuted tile) is
+    // query q0 + 16(r/8) + 8 hf + r%8, column = key j.
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const u32x4 cur = win[i % kDepth];
+      win[i % kDepth] = frag(i + kDepth);
+      if (i & 1)
+        dp = mfma32(__builtin_bit_cast(bf16x8, cur), vf[i >> 1], dp);
+      else
+        s = mfma32(__builtin_bit_cast(bf16x8, cur), kf[i >> 1], s);
+    }
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     f32x4 l2v[4], dv4[4];
 #pragma unroll
@@ -240,20 +293,26 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       l2v[aa] = *(const f32x4 *)&sL2[buf][base];
       dv4[aa] = *(const f32x4 *)&sDv[buf][base];
     }
-    const bool partial =
-        __builtin_amdgcn_ballot_w64(!(qlo <= q0 && qhi >= q0 + QS - 1)) != 0;
-    float p[16], ds[16];
+    float p[16], ds[16], dc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int aa = r >> 2, bb = r & 3;
       const int i = q0 + 16 * (aa >> 1) + 8 * hf + 4 * (aa & 1) + bb;
-      float dcap;
-      const float t = score2<ALIBI, SOFTCAP>(a, s[r], slopeL, i, j, dcap);
-      float pr = __builtin_amdgcn_exp2f(t - l2v[aa][bb]);
-      if (partial && (i < qlo || i > qhi)) pr = 0.f;
-      p[r] = pr;
-      ds[r] = pr * (dp[r] - dv4[aa][bb]) * dcap;
+      const float t = score2<ALIBI, SOFTCAP>(a, s[r], slopeL, i, j, dc[r]);
+      p[r] = __builtin_amdgcn_exp2f(t - l2v[aa][bb]);
     }
+    // Element mask only when some key of this wave does not take all 32 queries of the step.
+    if (__builtin_amdgcn_ballot_w64(!(qlo <= q0 && qhi >= q0 + QS - 1))) {
+      keep_branch();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int aa = r >> 2, bb = r & 3;
+        const int i = q0 + 16 * (aa >> 1) + 8 * hf + 4 * (aa & 1) + bb;
+        if (i < qlo || i > qhi) p[r] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = p[r] * (dp[r] - dv4[r >> 2][r & 3]) * dc[r];
     bf16x8 pb[2], db[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -266,21 +325,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       pb[kk] = __builtin_convertvector(x, bf16x8);
       db[kk] = __builtin_convertvector(y, bf16x8);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries (two 16-row steps).
-    {
-      const uint16_t *ta = &sDOT[buf][l32 * TP + hf * 8];
-      const uint16_t *qa = &sQT[buf][l32 * TP + hf * 8];
+    // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries (two 16-row halves).
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+    for (int i = NA; i < NS; ++i) {
+      const u32x4 cur = win[i % kDepth];
+      if (i + kDepth < NS) win[i % kDepth] = frag(i + kDepth);
+      const int b = i - NA, kk = b / (2 * NDB), d0 = (b >> 1) % NDB;
+      if (b & 1)
+        dkt[d0] = mfma32(__builtin_bit_cast(bf16x8, cur), db[kk], dkt[d0]);
+      else
+        dvt[d0] = mfma32(__builtin_bit_cast(bf16x8, cur), pb[kk], dvt[d0]);
+    }
 #pragma unroll
-        for (int d0 = 0; d0 < NDB; ++d0) {
-          dvt[d0] = mfma32(
-              __builtin_bit_cast(bf16x8, *(const u32x4 *)(ta + d0 * 32 * TP + kk * 16)), pb[kk],
-              dvt[d0]);
-          dkt[d0] = mfma32(
-              __builtin_bit_cast(bf16x8, *(const u32x4 *)(qa + d0 * 32 * TP + kk * 16)), db[kk],
-              dkt[d0]);
-        }
+    for (int i = NA; i < NS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kDepth < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     if (qs + 1 < qs_end) stage(buf ^ 1);
     __syncthreads();
