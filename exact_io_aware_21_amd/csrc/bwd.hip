@@ -356,23 +356,59 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Buffer-to-LDS copy of one K and one V tile (byte size `bytes` each from k and v) into dst:
+// wave instruction j (j = wave + 8 r < NJK) fills the 64 16-byte slots j * 64 .. j * 64 + 63 of
+// the K tile and the same slots of the V tile that follows it, from per-lane byte offsets
+// voff[r].  (A free device function: the copy builtin must not sit in a lambda, which the host
+// compilation pass also instantiates.)
+template <int NRK, int NJK>
+__device__ __forceinline__ void copy_tiles_to_lds(const uint16_t *k, const uint16_t *v,
+                                                  int bytes, uint16_t *dst, int wave,
+                                                  const int *voff) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void *)k, 0, bytes, kBufferWord3);
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void *)v, 0, bytes, kBufferWord3);
+#pragma unroll
+  for (int r = 0; r < NRK; ++r) {
+    const int j = r * 8 + wave;
+    if (j < NJK) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)&dst[j * 64 * 8], 16, voff[r], 0,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)&dst[(NJK + j) * 64 * 8], 16,
+                                               voff[r], 0, 0, 0);
+    }
+  }
+}
+
 // dQ: one workgroup = 8 waves x 32 queries = one forward q-tile; it walks the q-tile's list of
 // non-empty 64-key tiles (the forward block table).
+//
+// The K and V tiles are double-buffered in LDS and filled by buffer-to-LDS loads
+// (buffer_load_dwordx4 ... lds): no VGPR staging, and the loads of tile t + 1 are in flight
+// while tile t is computed.  One LDS stage holds the K tile then the V tile, each 64
+// pi-permuted key rows of pitch KP, as 16-byte slots; a wave instruction fills 64 consecutive
+// slots, and a wave fills slot group j of both tiles (same offsets).  A pad slot repeats a real
+// chunk of its row; keys past N lie beyond the K and V resources and read as zero.
+// K^T, the A operand of dQ^T += K^T dS^T, is read from the same K tile with the transposing
+// LDS read ds_read_b64_tr_b16.
 template <int D, bool ALIBI, bool SOFTCAP, bool OUTF32>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   constexpr int NT = 512;
   constexpr int NKS = D / 16, NDB = D / 32;
-  constexpr int KP = pitch(D);    // LDS pitch of a K / V row
-  constexpr int TP = pitch(kBc);  // LDS pitch of a K^T row (d x 64 keys)
-  constexpr int RCH = kBc * (D / 8) / NT;
-  constexpr int TCH = D * (kBc / 8) / NT;
+  constexpr int KP = pitch(D);          // LDS pitch of a K / V row
+  constexpr int KSPR = KP / 8;          // 16-byte slots per LDS row
+  constexpr int KSLOT = kBc * KSPR;     // slots of one tile
+  constexpr int NJK = KSLOT / 64;       // wave instructions per tile
+  constexpr int NRK = (NJK + 7) / 8;    // slot groups per wave (at most)
+  constexpr int STAGE = 2 * KSLOT * 8;  // elements per LDS stage
   static_assert(kBr == 256 && kBc == 64, "kernel is written for 256 x 64 tiles");
-  static_assert(RCH >= 1 && TCH >= 1, "tile copies must cover the workgroup");
-  // Single-buffered key tiles (with 8 waves per workgroup the register budget has no room for
-  // a prefetch; measured faster than double buffering).
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBc * KP], sV[kBc * KP], sKT[D * TP];
+  static_assert(KSLOT % 64 == 0, "tiles must be whole wave instructions");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  // wave-uniform by construction; readfirstlane tells the compiler, so the LDS destinations of
+  // the buffer-to-LDS copies (M0) are scalars
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
   const int qt = blockIdx.x;
   const int N = a.N;
@@ -402,7 +438,6 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   }
   const float l2 = q_ok ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
   const float dq_row = q_ok ? a.dvec[(size_t)bh * N + qrow] : 0.f;
-  __builtin_amdgcn_s_waitcnt(0);  // settle the loads above once, outside the loop
   const float slopeL = ALIBI ? a.slopes[h] * kLog2e : 0.f;
 
   // The key-tile list (written by the table kernel before this launch): read through the
@@ -417,27 +452,58 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   } else {
     T = a.n_kt;
   }
+  auto kt_of = [&](int t) -> int { return lst ? lst[t] : t; };
+
+  // Zero both stages once, so that no LDS byte is ever read unwritten (keys past N may read as
+  // stale finite data or zero; their probabilities are masked to 0 either way).
+  for (int i = tid; i < 2 * STAGE / 8; i += NT) *(u32x4 *)&lds[i * 8] = u32x4{0u, 0u, 0u, 0u};
+
+  // Per-lane byte offsets of this wave's slot groups j = wave + 8 r (the same in K and V).
+  int voff[NRK];
+#pragma unroll
+  for (int r = 0; r < NRK; ++r) {
+    const int slot = 64 * (r * 8 + wave) + lane;
+    const int row = slot / KSPR, ch = slot % KSPR;
+    voff[r] = (pi_key(row) * D + (ch < D / 8 ? ch : D / 8 - 1) * 8) * 2;
+  }
+  auto fill = [&](int kt, int stage) {
+    const int keys_left = N - kt * kBc;  // >= 1
+    const size_t off = hbase + (size_t)kt * kBc * D;
+    copy_tiles_to_lds<NRK, NJK>(a.k + off, a.v + off, keys_left * D * 2, &lds[stage * STAGE],
+                                wave, voff);
+  };
+
+  // Transposing-read addresses for the K^T fragments.  ds_read_b64_tr_b16 hands lane
+  // 16 g + 4 q + e, for m = 0..3, element e of the 8 bytes addressed by lane 16 g + q + 4 m.  So
+  // for the A fragment (row = d block row dd = lane % 32, whose output column is
+  // 32 d0 + sigma_d(dd); k = key 16 kg + 8 (lane / 32) + t, t = 0..7) the addressing lane
+  // s = 16 g + q + 4 m points at key 16 kg + 8 (g / 2) + m (+ 4 for t = 4..7) and at column
+  // 32 d0 + 16 (q & 1) + 8 (g & 1) + 4 (q >> 1); kg and d0 are immediate offsets.
+  int tr_off[2];
+  {
+    const int q = lane & 3, m = (lane >> 2) & 3, g = lane >> 4;
+    const int col = 16 * (q & 1) + 8 * (g & 1) + 4 * (q >> 1);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) tr_off[u] = pi_key(8 * (g >> 1) + m + 4 * u) * KP + col;
+  }
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
   f32x16 dqt[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dqt[i] = f32x16{};
 
+  __syncthreads();  // the zero fill is complete before any copy lands
+  if (T > 0) fill(kt_of(0), 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
   for (int t = 0; t < T; ++t) {
-    const int kt = lst ? lst[t] : t;
-#pragma unroll
-    for (int u = 0; u < RCH; ++u) {
-      const int c = tid + NT * u, r = c / (D / 8), ch = c % (D / 8);
-      const size_t src = hbase + (size_t)min(kt * kBc + r, N - 1) * D + ch * 8;
-      *(u32x4 *)&sK[pi_key(r) * KP + ch * 8] = *(const u32x4 *)(a.k + src);
-      *(u32x4 *)&sV[pi_key(r) * KP + ch * 8] = *(const u32x4 *)(a.v + src);
-    }
-#pragma unroll
-    for (int u = 0; u < TCH; ++u) {
-      const int c = tid + NT * u, r = c / (kBc / 8), ch = c % (kBc / 8);
-      *(u32x4 *)&sKT[r * TP + ch * 8] =
-          *(const u32x4 *)(a.kt + ((size_t)bh * D + r) * a.Npad + (size_t)kt * kBc + ch * 8);
-    }
-    __syncthreads();
+    const int kt = kt_of(t), stage = t & 1;
+    if (t + 1 < T) fill(kt_of(t + 1), stage ^ 1);  // in flight during this tile's compute
+    const uint16_t *sK = &lds[stage * STAGE];
+    const uint16_t *sV = sK + KSLOT * 8;
 
     // S^T = K Q^T and dP^T = V dO^T: register r of key block blk is key
     // kt*Bc + 32*blk + 16*(r/8) + 8*hf + r%8, column = query qrow.
@@ -453,8 +519,27 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
             mfma32(__builtin_bit_cast(bf16x8, *(const u32x4 *)(va + ks * 16)), df[ks], dp[blk]);
       }
     }
-    const bool partial =
-        __builtin_amdgcn_ballot_w64(!(lo <= kt * kBc && hi >= kt * kBc + kBc - 1)) != 0;
+    // P^T overwrites S^T in place.
+    float dc[2][16];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jj = kt * kBc + 32 * blk + 16 * (r >> 3) + 8 * hf + (r & 7);
+        const float tt = score2<ALIBI, SOFTCAP>(a, s[blk][r], slopeL, qrow, jj, dc[blk][r]);
+        s[blk][r] = __builtin_amdgcn_exp2f(tt - l2);
+      }
+    // Element mask only when some row of this wave does not allow all 64 keys of the tile.
+    if (__builtin_amdgcn_ballot_w64(!(lo <= kt * kBc && hi >= kt * kBc + kBc - 1))) {
+      keep_branch();
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jj = kt * kBc + 32 * blk + 16 * (r >> 3) + 8 * hf + (r & 7);
+          if (jj < lo || jj > hi) s[blk][r] = 0.f;
+        }
+    }
     bf16x8 db[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -462,26 +547,25 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int blk = g >> 1, r = 8 * (g & 1) + e;
-        const int jj = kt * kBc + 32 * blk + 16 * (r >> 3) + 8 * hf + (r & 7);
-        float dcap;
-        const float tt = score2<ALIBI, SOFTCAP>(a, s[blk][r], slopeL, qrow, jj, dcap);
-        float pr = __builtin_amdgcn_exp2f(tt - l2);
-        if (partial && (jj < lo || jj > hi)) pr = 0.f;
-        y[e] = pr * (dp[blk][r] - dq_row) * dcap;
+        y[e] = s[blk][r] * (dp[blk][r] - dq_row) * dc[blk][r];
       }
       db[g] = __builtin_convertvector(y, bf16x8);
     }
-    // dQ^T += K^T dS^T over the 64 keys (four 16-key steps).
-    {
-      const uint16_t *ta = &sKT[l32 * TP + hf * 8];
+    // dQ^T += K^T dS^T over the 64 keys (four 16-key steps); K^T fragments by transposing
+    // reads of the K tile.
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int d0 = 0; d0 < NDB; ++d0)
-          dqt[d0] = mfma32(
-              __builtin_bit_cast(bf16x8, *(const u32x4 *)(ta + d0 * 32 * TP + g * 16)), db[g],
-              dqt[d0]);
-    }
+      for (int d0 = 0; d0 < NDB; ++d0) {
+        const int imm = 16 * g * KP + 32 * d0;
+        const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)&sK[tr_off[0] + imm]);
+        const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)&sK[tr_off[1] + imm]);
+        const v8i16 x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        dqt[d0] = mfma32(__builtin_bit_cast(bf16x8, x), db[g], dqt[d0]);
+      }
+    // This wave's copies of tile t + 1 have landed; after the barrier every wave's have, and
+    // every wave is done reading this stage (the next iteration's copies overwrite it).
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
