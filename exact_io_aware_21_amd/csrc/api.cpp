@@ -106,24 +106,16 @@ WsLayout ws_layout(const Shape &s) {
   return w;
 }
 
-// Backward workspace: D (fp32 [BH][N]), the bf16 packs Q^T, dO^T, K^T ([BH][d][Npad] each) and,
-// for masked kinds, the forward block table.
+// Backward workspace: D (fp32 [BH][N]) and, for masked kinds, the forward block table.
 struct BwdLayout {
-  size_t dvec, qt, dot, kt, cls, cnt, list, total;
+  size_t dvec, cls, cnt, list, total;
 };
 
 BwdLayout bwd_layout(const Shape &s) {
   BwdLayout w{};
   size_t off = 0;
-  const size_t pack = (size_t)s.B * s.H * s.d * s.Npad * 2;
   w.dvec = off;
   off = align256(off + (size_t)s.B * s.H * s.N * 4);
-  w.qt = off;
-  off = align256(off + pack);
-  w.dot = off;
-  off = align256(off + pack);
-  w.kt = off;
-  off = align256(off + pack);
   if (s.kind != ATTN_MASK_NONE) {
     const size_t rows = (size_t)s.Bm * s.n_qt;
     w.cls = off;
@@ -265,7 +257,7 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
   const hipStream_t st = (hipStream_t)stream;
   char *ws = (char *)params->workspace;
   uint16_t *vt = (uint16_t *)(ws + wl.vt);
-  if (attn::launch_vt_pack((const uint16_t *)v, vt, B * H, N, s.Npad, d, true, st) != hipSuccess)
+  if (attn::launch_vt_pack((const uint16_t *)v, vt, B * H, N, s.Npad, d, st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "V transpose kernel launch failed");
 
   attn::FwdArgs a{};
@@ -354,9 +346,6 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
   a.dout = (const uint16_t *)dout;
   a.o = o;
   a.lse = lse;
-  a.qt = (const uint16_t *)(ws + wl.qt);
-  a.dot = (const uint16_t *)(ws + wl.dot);
-  a.kt = (const uint16_t *)(ws + wl.kt);
   a.dvec = (float *)(ws + wl.dvec);
   a.dq = dq;
   a.dk = dk;
@@ -381,11 +370,6 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
   a.offs = s.kind == ATTN_MASK_DOCUMENT ? params->doc_offsets : nullptr;
   a.o_f32 = a.out_f32 = params->o_dtype == ATTN_O_F32;
 
-  if (attn::launch_vt_pack(a.q, (uint16_t *)a.qt, B * H, N, s.Npad, d, false, st) != hipSuccess ||
-      attn::launch_vt_pack(a.dout, (uint16_t *)a.dot, B * H, N, s.Npad, d, false, st) !=
-          hipSuccess ||
-      attn::launch_vt_pack(a.k, (uint16_t *)a.kt, B * H, N, s.Npad, d, false, st) != hipSuccess)
-    return fail(ATTN_ERR_LAUNCH, "transpose kernel launch failed");
   if (attn::launch_bwd_dot(a, d, st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "row-dot kernel launch failed");
   if (s.kind != ATTN_MASK_NONE) {

@@ -14,20 +14,21 @@
 // ever summed across workgroups.
 //
 // gfx950 mapping (same devices as the forward kernel, see fwd.hip):
-//  * The key-major kernel double-buffers its LDS tiles: the next step's global loads are in
-//    flight in VGPRs while the current step computes, and are written to the idle buffer before
-//    the step's barrier.
 //  * Every product is a v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Q, K, V, dO are the
 //    exact bf16 inputs; P (<= 1) and dS are rounded to bf16 as MFMA operands.
 //  * The recomputed tile is built so that its lane owns one row of the output being accumulated:
 //    in bwd_dkdv_kernel S = Q K^T (A = Q rows from LDS, B = K^T of the wave's keys in VGPRs), so
 //    lane % 32 is a key; in bwd_dq_kernel S^T = K Q^T, so lane % 32 is a query.
-//  * The rows of the LDS operand are stored with index bits 2 and 3 swapped (pi_key), which makes
+//  * The rows of the LDS tiles are stored with index bits 2 and 3 swapped (pi_key), which makes
 //    the 16 accumulator registers of a lane two runs of 8 consecutive rows: P and dS then feed the
 //    next product as its B operand straight from registers.
-//  * The other operand of those products (Q^T, dO^T for dK, dV; K^T for dQ) comes from the
-//    transposed, sigma-permuted bf16 packs in the workspace, so each lane's accumulator registers
-//    are 16 consecutive output columns and the epilogue stores 16-byte vectors.
+//  * The other operand of those products (Q^T, dO^T for dK, dV; K^T for dQ) is read from the
+//    same row tiles with the transposing LDS read ds_read_b64_tr_b16, with its columns in the
+//    sigma_d order, so each lane's accumulator registers are 16 consecutive output columns and
+//    the epilogue stores 16-byte vectors.  No transposed copy of any input is made.
+//  * The row tiles are copied straight from global memory into LDS (buffer loads with the LDS
+//    destination), double-buffered one step or tile ahead, with no VGPR staging; rows past N lie
+//    outside the buffer resource and read as zero.
 #include "kcommon.h"
 #include "launch.h"
 
@@ -115,26 +116,100 @@ __device__ __forceinline__ float score2(const BwdArgs &a, float x, float slopeL,
 }
 
 // ---------------------------------------------------------------------------------------------
+// Buffer-to-LDS copy of two equally laid-out tiles (byte size `bytes` each, from x and y) into
+// dst: wave instruction j (j = wave + NW r < NJ) fills the 64 16-byte slots j * 64 .. j * 64 + 63
+// of the first tile and the same slots of the second, which starts NJ * 64 slots later, from
+// per-lane byte offsets voff[r].  Loads past `bytes` read as zero.  (A free device function: the
+// copy builtin must not sit in a lambda, which the host compilation pass also instantiates.)
+template <int NR, int NJ, int NW>
+__device__ __forceinline__ void copy_tiles_to_lds(const void *x, const void *y, int bytes,
+                                                  uint16_t *dst, int wave, const int *voff) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  const auto rx = __builtin_amdgcn_make_buffer_rsrc((void *)x, 0, bytes, kBufferWord3);
+  const auto ry = __builtin_amdgcn_make_buffer_rsrc((void *)y, 0, bytes, kBufferWord3);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int j = r * NW + wave;
+    if (j < NJ) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)&dst[j * 64 * 8], 16, voff[r], 0,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void *)&dst[(NJ + j) * 64 * 8], 16,
+                                               voff[r], 0, 0, 0);
+    }
+  }
+}
+
+// Buffer-to-LDS copy of two 4-byte-per-lane rows (bytes each, from x and y) into dst and
+// dst + 128 elements (64 floats each); loads past `bytes` read as zero.
+__device__ __forceinline__ void copy_rows4_to_lds(const float *x, const float *y, int bytes,
+                                                  uint16_t *dst, int voff) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  const auto rx = __builtin_amdgcn_make_buffer_rsrc((void *)x, 0, bytes, kBufferWord3);
+  const auto ry = __builtin_amdgcn_make_buffer_rsrc((void *)y, 0, bytes, kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)dst, 4, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void *)&dst[128], 4, voff, 0, 0, 0);
+}
+
+// Per-lane byte offset of 16-byte slot `slot` of a tile of pi-permuted rows (pitch P elements,
+// P / 8 slots a row) of a row-major [rows][D] bf16 source: LDS row rho holds source row
+// pi_key(rho); a pad slot repeats the row's last chunk; slots past the tile read row 0.
+template <int D, int P, int ROWS>
+__device__ __forceinline__ int tile_slot_offset(int slot) {
+  constexpr int SPR = P / 8;
+  if (slot >= ROWS * SPR) return 0;
+  const int row = slot / SPR, ch = slot % SPR;
+  return (pi_key(row) * D + (ch < D / 8 ? ch : D / 8 - 1) * 8) * 2;
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Transposed A fragment of a 32x32x16 MFMA from an LDS tile of pi-permuted rows (pitch P):
+// lane l gets, for output row dd = l % 32 (column 32 d0 + sigma_d(dd) of the tile) and
+// k = 8 (l / 32) + t, t = 0..7, the element of tile row 16 kg + 8 (l / 32) + t (before the
+// permutation).  ds_read_b64_tr_b16 hands lane 16 g + 4 q + e, for m = 0..3, element e of the
+// 8 bytes addressed by lane 16 g + q + 4 m, so the addressing lane s = 16 g + q + 4 m points at
+// row 16 kg + 8 (g / 2) + m (+ 4 for t = 4..7) and column 32 d0 + 16 (q & 1) + 8 (g & 1) +
+// 4 (q >> 1).  tr_base() is the lane's part; kg and d0 add the immediate 16 kg P + 32 d0.
+template <int P>
+__device__ __forceinline__ void tr_base(int lane, int off[2]) {
+  const int q = lane & 3, m = (lane >> 2) & 3, g = lane >> 4;
+  const int col = 16 * (q & 1) + 8 * (g & 1) + 4 * (q >> 1);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) off[u] = pi_key(8 * (g >> 1) + m + 4 * u) * P + col;
+}
+
+__device__ __forceinline__ u32x4 tr_frag(const uint16_t *tile, const int off[2], int imm) {
+  const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)&tile[off[0] + imm]);
+  const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)&tile[off[1] + imm]);
+  return __builtin_bit_cast(u32x4, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// ---------------------------------------------------------------------------------------------
 // dK, dV: one workgroup = 4 waves x 32 keys of one (batch, head); query steps of 32 rows.
+//
+// Each query step's Q and dO rows (32 pi-permuted rows of pitch RP each) and its L and D are
+// copied straight into LDS (buffer-to-LDS loads) one step ahead, double-buffered; the
+// transposed operands Q^T and dO^T of the dK and dV products are read from the same row tiles
+// with ds_read_b64_tr_b16.
 template <int D, bool ALIBI, bool SOFTCAP, bool OUTF32>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int NT = 256, QS = 32, KPW = 32;
+  constexpr int NT = 256, NW = 4, QS = 32, KPW = 32;
   constexpr int NKS = D / 16, NDB = D / 32;
-  constexpr int RP = pitch(D);   // LDS pitch of a Q / dO row
-  constexpr int TP = pitch(QS);  // LDS pitch of a Q^T / dO^T row (d x 32 queries)
-  constexpr int RCH = QS * (D / 8) / NT;  // row-tile chunks per thread
-  constexpr int TCH = D * (QS / 8) / NT;  // transposed-tile chunks per thread
-  static_assert(RCH >= 1 && TCH >= 1, "tile copies must cover the workgroup");
-  // Double-buffered query-step tiles: step s is read from buffer s & 1 while the loads of step
-  // s + 1 are in flight into VGPRs; they are written to the other buffer after the compute.
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][QS * RP], sDO[2][QS * RP];
-  __shared__ __attribute__((aligned(16))) uint16_t sQT[2][D * TP], sDOT[2][D * TP];
-  __shared__ __attribute__((aligned(16))) float sL2[2][QS], sDv[2][QS];
+  constexpr int RP = pitch(D);                    // LDS pitch of a Q / dO row
+  constexpr int RSLOT = QS * (RP / 8);            // 16-byte slots of a row tile
+  constexpr int NJR = (RSLOT + 63) / 64;          // wave instructions per row tile
+  constexpr int NRR = (NJR + NW - 1) / NW;        // per wave (at most)
+  constexpr int TILE = NJR * 64 * 8;              // elements per row tile (with the spill-over)
+  constexpr int STAGE = 2 * TILE + 2 * 64 * 2;    // Q, dO, then L and D (64 floats each)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS copy targets
   const int bh = blockIdx.y, b = bh / a.H, h = bh - b * a.H;
   const int N = a.N;
-  const int key0 = blockIdx.x * (4 * KPW);
+  const int key0 = blockIdx.x * (NW * KPW);
   const int j = key0 + wave * KPW + l32;  // this lane's key
   const bool j_ok = j < N;
   const MaskDesc md{a.kind, N, a.window, a.offs ? a.offs + (size_t)b * (a.max_docs + 1) : nullptr,
@@ -145,8 +220,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     qhi = col_hi(md, j);
   }
   // Query steps the workgroup visits: the union over its keys (both bounds grow with j).
-  const int jl = min(key0 + 4 * KPW, N) - 1;
   // (wave-uniform: read into scalars, so the loop below is a scalar loop)
+  const int jl = min(key0 + NW * KPW, N) - 1;
   const int qs_begin = __builtin_amdgcn_readfirstlane(col_lo(md, key0) / QS);
   const int qs_end = __builtin_amdgcn_readfirstlane(col_hi(md, jl) / QS + 1);
 
@@ -165,133 +240,88 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       kf[ks] = __builtin_bit_cast(bf16x8, x);
       vf[ks] = __builtin_bit_cast(bf16x8, y);
     }
-    // Settle these loads here, once.  Otherwise the wait for them lands on their first use
-    // inside the loop, where it also waits for the next step's tile loads in flight.
-    __builtin_amdgcn_s_waitcnt(0);
   }
   f32x16 dkt[NDB], dvt[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dkt[i] = dvt[i] = f32x16{};
 
-  // Query-step staging: Q and dO rows (rows pi-permuted), the transposed packs, and L (base 2)
-  // and D of the 32 queries.  The loads are buffer loads: the step moves a scalar base (the
-  // resource), the per-lane byte offsets are fixed, and rows past N lie beyond the resource's
-  // size, so they read as zero (and are masked below).
-  u32x4 rq[RCH], rdo[RCH], rqt[TCH], rdot[TCH];
-  float rl2 = 0.f, rdv = 0.f;
-  int voff_r[RCH], voff_t[TCH];
+  // Zero both stages once, so that no LDS byte is ever read unwritten.
+  for (int i = tid; i < 2 * STAGE / 8; i += NT) *(u32x4 *)&lds[i * 8] = u32x4{0u, 0u, 0u, 0u};
+  int voff[NRR];
 #pragma unroll
-  for (int u = 0; u < RCH; ++u) {
-    const int c = tid + NT * u, r = c / (D / 8), ch = c % (D / 8);
-    voff_r[u] = (r * D + ch * 8) * 2;
-  }
-#pragma unroll
-  for (int u = 0; u < TCH; ++u) {
-    const int c = tid + NT * u, r = c / (QS / 8), ch = c % (QS / 8);
-    voff_t[u] = (r * a.Npad + ch * 8) * 2;
-  }
-  const int voff_l = (tid & (QS - 1)) * 4;
-  auto fetch = [&](int qs) {
+  for (int r = 0; r < NRR; ++r) voff[r] = tile_slot_offset<D, RP, QS>(64 * (r * NW + wave) + lane);
+  auto fill = [&](int qs, int stage) {
     const int q0 = qs * QS;
     const int rows_left = N - q0;  // >= 1
-    const auto rsq = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.q + hbase + (size_t)q0 * D), 0, rows_left * D * 2, kBufferWord3);
-    const auto rsd = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.dout + hbase + (size_t)q0 * D), 0, rows_left * D * 2, kBufferWord3);
-    const size_t tbase = (size_t)bh * D * a.Npad + q0;
-    const int tbytes = (D * a.Npad - q0) * 2;
-    const auto rsqt = __builtin_amdgcn_make_buffer_rsrc((void *)(a.qt + tbase), 0, tbytes,
-                                                        kBufferWord3);
-    const auto rsdt = __builtin_amdgcn_make_buffer_rsrc((void *)(a.dot + tbase), 0, tbytes,
-                                                        kBufferWord3);
-#pragma unroll
-    for (int u = 0; u < RCH; ++u) {
-      rq[u] = __builtin_amdgcn_raw_buffer_load_b128(rsq, voff_r[u], 0, 0);
-      rdo[u] = __builtin_amdgcn_raw_buffer_load_b128(rsd, voff_r[u], 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < TCH; ++u) {
-      rqt[u] = __builtin_amdgcn_raw_buffer_load_b128(rsqt, voff_t[u], 0, 0);
-      rdot[u] = __builtin_amdgcn_raw_buffer_load_b128(rsdt, voff_t[u], 0, 0);
-    }
-    const size_t lbase = (size_t)bh * N + q0;
-    const auto rsl = __builtin_amdgcn_make_buffer_rsrc((void *)(a.lse + lbase), 0, rows_left * 4,
-                                                       kBufferWord3);
-    const auto rsv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.dvec + lbase), 0,
-                                                       rows_left * 4, kBufferWord3);
-    rl2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsl, voff_l, 0, 0));
-    rdv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsv, voff_l, 0, 0));
+    uint16_t *dst = &lds[stage * STAGE];
+    copy_tiles_to_lds<NRR, NJR, NW>(a.q + hbase + (size_t)q0 * D, a.dout + hbase + (size_t)q0 * D,
+                                    rows_left * D * 2, dst, wave, voff);
+    // L and D of the 32 queries: one 4-byte-per-lane copy each (lanes 32..63 land in the unused
+    // upper half of the 64-float slot).
+    if (wave == 0)
+      copy_rows4_to_lds(a.lse + (size_t)bh * N + q0, a.dvec + (size_t)bh * N + q0,
+                        rows_left * 4, &dst[2 * TILE], lane * 4);
   };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < RCH; ++u) {
-      const int c = tid + NT * u, r = c / (D / 8), ch = c % (D / 8);
-      *(u32x4 *)&sQ[buf][pi_key(r) * RP + ch * 8] = rq[u];
-      *(u32x4 *)&sDO[buf][pi_key(r) * RP + ch * 8] = rdo[u];
-    }
-#pragma unroll
-    for (int u = 0; u < TCH; ++u) {
-      const int c = tid + NT * u, r = c / (QS / 8), ch = c % (QS / 8);
-      *(u32x4 *)&sQT[buf][r * TP + ch * 8] = rqt[u];
-      *(u32x4 *)&sDOT[buf][r * TP + ch * 8] = rdot[u];
-    }
-    if (tid < QS) {
-      sL2[buf][tid] = rl2 * kLog2e;
-      sDv[buf][tid] = rdv;
-    }
-  };
-  if (qs_begin < qs_end) {
-    fetch(qs_begin);
-    stage(0);
-  }
+  int tro[2];
+  tr_base<RP>(lane, tro);
+  // Settle the loads above and the zero fill before the first copy lands.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (qs_begin < qs_end) fill(qs_begin, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int qs = qs_begin; qs < qs_end; ++qs) {
-    const int q0 = qs * QS, buf = (qs - qs_begin) & 1;
-    if (qs + 1 < qs_end) fetch(qs + 1);
-    // The step's 32 MFMAs read one A fragment (16 bytes a lane) each from LDS: first the
-    // score products S = Q K^T and dP = dO V^T (steps 0..15: k-step i/2, dP when i is odd),
-    // then dV^T += dO^T P and dK^T += Q^T dS (steps 16..31: 16-query half kk, d block d0, dK
-    // when i is odd).  Fragment i + kDepth is read while MFMA i runs, across the softmax too.
+    const int q0 = qs * QS, stage = (qs - qs_begin) & 1;
+    const uint16_t *sQ = &lds[stage * STAGE];
+    const uint16_t *sDO = sQ + TILE;
+    const float *sL = (const float *)(sQ + 2 * TILE);
+    const float *sDv = sL + 64;
+    // The step's 32 MFMAs each take one A fragment (16 bytes a lane) from LDS.  The transposed
+    // ones of dV^T += dO^T P and dK^T += Q^T dS (16-query half kk, d block d0; dK when odd) are
+    // all read first, before the copies of the next step are issued: a transposing read issued
+    // after those copies would be made to wait for them.  The score products S = Q K^T and
+    // dP = dO V^T (k-step i/2, dP when i is odd) read theirs kDepth MFMAs ahead.
     constexpr int kDepth = 4;
-    constexpr int NA = 2 * NKS, NS = NA + 4 * NDB;
-    const uint16_t *qa = &sQ[buf][l32 * RP + hf * 8];
-    const uint16_t *da = &sDO[buf][l32 * RP + hf * 8];
-    const uint16_t *ta = &sDOT[buf][l32 * TP + hf * 8];
-    const uint16_t *qta = &sQT[buf][l32 * TP + hf * 8];
+    constexpr int NA = 2 * NKS, NB = 4 * NDB;
+    u32x4 fb[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int kk = i / (2 * NDB), d0 = (i >> 1) % NDB;
+      fb[i] = tr_frag((i & 1) ? sQ : sDO, tro, 16 * kk * RP + 32 * d0);
+    }
+    const uint16_t *qa = &sQ[l32 * RP + hf * 8];
+    const uint16_t *da = &sDO[l32 * RP + hf * 8];
     auto frag = [&](int i) -> u32x4 {
-      if (i < NA) return *(const u32x4 *)(((i & 1) ? da : qa) + (i >> 1) * 16);
-      const int b = i - NA, kk = b / (2 * NDB), d0 = (b >> 1) % NDB;
-      return *(const u32x4 *)(((b & 1) ? qta : ta) + d0 * 32 * TP + kk * 16);
+      return *(const u32x4 *)(((i & 1) ? da : qa) + (i >> 1) * 16);
     };
     u32x4 win[kDepth];
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) win[i] = frag(i);
+    if (qs + 1 < qs_end) fill(qs + 1, stage ^ 1);  // in flight during this step's compute
     // S and dP: accumulator register r (row 8(r/4) + 4 hf + r%4 of the pi-permuted tile) is
     // query q0 + 16(r/8) + 8 hf + r%8, column = key j.
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const u32x4 cur = win[i % kDepth];
-      win[i % kDepth] = frag(i + kDepth);
+      if (i + kDepth < NA) win[i % kDepth] = frag(i + kDepth);
       if (i & 1)
         dp = mfma32(__builtin_bit_cast(bf16x8, cur), vf[i >> 1], dp);
       else
         s = mfma32(__builtin_bit_cast(bf16x8, cur), kf[i >> 1], s);
     }
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
     for (int i = 0; i < NA; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i + kDepth < NA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     f32x4 l2v[4], dv4[4];
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
       const int base = 16 * (aa >> 1) + 8 * hf + 4 * (aa & 1);
-      l2v[aa] = *(const f32x4 *)&sL2[buf][base];
-      dv4[aa] = *(const f32x4 *)&sDv[buf][base];
+      l2v[aa] = *(const f32x4 *)&sL[base];
+      dv4[aa] = *(const f32x4 *)&sDv[base];
     }
     float p[16], ds[16], dc[16];
 #pragma unroll
@@ -299,7 +329,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const int aa = r >> 2, bb = r & 3;
       const int i = q0 + 16 * (aa >> 1) + 8 * hf + 4 * (aa & 1) + bb;
       const float t = score2<ALIBI, SOFTCAP>(a, s[r], slopeL, i, j, dc[r]);
-      p[r] = __builtin_amdgcn_exp2f(t - l2v[aa][bb]);
+      p[r] = __builtin_amdgcn_exp2f(fmaf(-kLog2e, l2v[aa][bb], t));  // L is natural-log
     }
     // Element mask only when some key of this wave does not take all 32 queries of the step.
     if (__builtin_amdgcn_ballot_w64(!(qlo <= q0 && qhi >= q0 + QS - 1))) {
@@ -327,21 +357,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     }
     // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries (two 16-row halves).
 #pragma unroll
-    for (int i = NA; i < NS; ++i) {
-      const u32x4 cur = win[i % kDepth];
-      if (i + kDepth < NS) win[i % kDepth] = frag(i + kDepth);
-      const int b = i - NA, kk = b / (2 * NDB), d0 = (b >> 1) % NDB;
-      if (b & 1)
-        dkt[d0] = mfma32(__builtin_bit_cast(bf16x8, cur), db[kk], dkt[d0]);
+    for (int i = 0; i < NB; ++i) {
+      const int kk = i / (2 * NDB), d0 = (i >> 1) % NDB;
+      if (i & 1)
+        dkt[d0] = mfma32(__builtin_bit_cast(bf16x8, fb[i]), db[kk], dkt[d0]);
       else
-        dvt[d0] = mfma32(__builtin_bit_cast(bf16x8, cur), pb[kk], dvt[d0]);
+        dvt[d0] = mfma32(__builtin_bit_cast(bf16x8, fb[i]), pb[kk], dvt[d0]);
     }
-#pragma unroll
-    for (int i = NA; i < NS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + kDepth < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if (qs + 1 < qs_end) stage(buf ^ 1);
+    // This wave's copies of step qs + 1 have landed; after the barrier every wave's have, and
+    // every wave is done reading this stage (the next step's copies overwrite it).
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -356,30 +381,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Buffer-to-LDS copy of one K and one V tile (byte size `bytes` each from k and v) into dst:
-// wave instruction j (j = wave + 8 r < NJK) fills the 64 16-byte slots j * 64 .. j * 64 + 63 of
-// the K tile and the same slots of the V tile that follows it, from per-lane byte offsets
-// voff[r].  (A free device function: the copy builtin must not sit in a lambda, which the host
-// compilation pass also instantiates.)
-template <int NRK, int NJK>
-__device__ __forceinline__ void copy_tiles_to_lds(const uint16_t *k, const uint16_t *v,
-                                                  int bytes, uint16_t *dst, int wave,
-                                                  const int *voff) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void *)k, 0, bytes, kBufferWord3);
-  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void *)v, 0, bytes, kBufferWord3);
-#pragma unroll
-  for (int r = 0; r < NRK; ++r) {
-    const int j = r * 8 + wave;
-    if (j < NJK) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)&dst[j * 64 * 8], 16, voff[r], 0,
-                                               0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)&dst[(NJK + j) * 64 * 8], 16,
-                                               voff[r], 0, 0, 0);
-    }
-  }
-}
-
 // dQ: one workgroup = 8 waves x 32 queries = one forward q-tile; it walks the q-tile's list of
 // non-empty 64-key tiles (the forward block table).
 //
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   auto fill = [&](int kt, int stage) {
     const int keys_left = N - kt * kBc;  // >= 1
     const size_t off = hbase + (size_t)kt * kBc * D;
-    copy_tiles_to_lds<NRK, NJK>(a.k + off, a.v + off, keys_left * D * 2, &lds[stage * STAGE],
+    copy_tiles_to_lds<NRK, NJK, 8>(a.k + off, a.v + off, keys_left * D * 2, &lds[stage * STAGE],
                                 wave, voff);
   };
 

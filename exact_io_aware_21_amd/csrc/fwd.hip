@@ -47,8 +47,7 @@ namespace {
 // ---------------------------------------------------------------------------------------------
 // V [BH][N][D] bf16 -> V^T [BH][D][Npad] fp16: keys contiguous, zero beyond N, d rows permuted
 // by sigma_d.
-// With F16 = false the values stay bf16 (the backward pass's transposed operands).
-template <int D, bool F16>
+template <int D>
 __global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t *__restrict__ v,
                                                       uint16_t *__restrict__ vt, int N, int Npad) {
   constexpr int RS = D + 2;  // padded LDS row, in elements
@@ -75,8 +74,8 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t *__restrict
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t b0 = t[(e * 8 + 2 * w) * RS + dcol], b1 = t[(e * 8 + 2 * w + 1) * RS + dcol];
-      const uint32_t lo = F16 ? bf16_to_f16_bits(b0) : b0;
-      const uint32_t hi = F16 ? bf16_to_f16_bits(b1) : b1;
+      const uint32_t lo = bf16_to_f16_bits(b0);
+      const uint32_t hi = bf16_to_f16_bits(b1);
       x[w] = lo | (hi << 16);
     }
     *(u32x4 *)(out + (size_t)p * Npad + e * 8) = x;
@@ -473,19 +472,12 @@ hipError_t launch_d(const FwdInstance &in, const FwdArgs &a, dim3 grid, hipStrea
 }  // namespace
 
 hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Npad, int d,
-                          bool to_f16, hipStream_t stream) {
+                          hipStream_t stream) {
   dim3 grid(Npad / 64, BH);
-  if (d == 128) {
-    if (to_f16)
-      vt_pack_kernel<128, true><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
-    else
-      vt_pack_kernel<128, false><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
-  } else {
-    if (to_f16)
-      vt_pack_kernel<64, true><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
-    else
-      vt_pack_kernel<64, false><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
-  }
+  if (d == 128)
+    vt_pack_kernel<128><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
+  else
+    vt_pack_kernel<64><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
   return hipGetLastError();
 }
 

@@ -42,7 +42,6 @@ struct BwdArgs {
   const uint16_t *q, *k, *v, *dout;  // bf16 [BH][N][D]
   const void *o;                     // bf16 or fp32 [BH][N][D] (o_f32)
   const float *lse;                  // fp32 [BH][N], natural log
-  const uint16_t *qt, *dot, *kt;     // Q^T, dO^T, K^T: bf16 [BH][D][Npad], d rows sigma-permuted
   float *dvec;                       // fp32 [BH][N]: D_i = dO_i . O_i
   void *dq, *dk, *dv;                // bf16 or fp32 [BH][N][D] (out_f32)
   int B, H, N, Npad, n_qt, n_kt;
@@ -61,7 +60,7 @@ hipError_t launch_bwd_dot(const BwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, int d, bool alibi, bool softcap, hipStream_t stream);
 
 hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Npad, int d,
-                          bool to_f16, hipStream_t stream);
+                          hipStream_t stream);
 hipError_t launch_block_table(MaskDesc m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,
                               int8_t *cls, int32_t *cnt, int32_t *list, hipStream_t stream);
 hipError_t launch_fwd(const FwdInstance &inst, const FwdArgs &a, hipStream_t stream);

@@ -153,8 +153,8 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
              const void *dout, void *dq, void *dk, void *dv, int B, int H, int N, int d,
              float scale, uint32_t variant, const attn_params *params, void *stream);
 
-/* Bytes of workspace attn_bwd needs (0 on invalid arguments): D (fp32 [B][H][N]), transposed
-   bf16 copies of Q, dO and K, and the block table. */
+/* Bytes of workspace attn_bwd needs (0 on invalid arguments): D (fp32 [B][H][N]) and, for the
+   masked kinds, the block table. */
 size_t attn_bwd_workspace_size(int B, int H, int N, int d, uint32_t variant);
 
 const char *attn_strerror(int code);
