@@ -263,6 +263,108 @@ def bench_bwd(args, w, inp, q, k, v, o, lse, var, slopes, offs, dev):
     print(json.dumps(out), flush=True)
 
 
+DECODE_DEFAULT = "decode_b8h32_len2k_14k_d128_p64"
+
+
+def bench_decode(args):
+    """Times attn_decode (split and merge kernels, the library's event pair around them) on a
+    paged-cache workload; the metric is GB/s of compulsory traffic: every cached K and V row of
+    every sequence read once, Q read, O (bf16) and L written."""
+    import numpy as np
+    import torch
+
+    from exact_io_aware_21_amd import attn, inputs
+
+    name = DECODE_DEFAULT if args.workload == DEFAULT_WORKLOAD else args.workload
+    w = inputs.DECODE_WORKLOADS[name]
+    x = inputs.make_paged_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, kc, vc = to_dev(x["q"]), to_dev(x["k_cache"]), to_dev(x["v_cache"])
+    table = torch.from_numpy(x["page_table"]).to(dev)
+    lens = torch.from_numpy(x["seq_lens"]).to(dev)
+    o = torch.empty(w.B, w.H, w.Lq, w.d, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(w.B, w.H, w.Lq, dtype=torch.float32, device=dev)
+    ws = attn.alloc_decode_workspace(w.B, w.H, w.Lq, w.d, w.page, table.shape[1], dev)
+    kw = dict(causal=w.causal, workspace=ws)
+    for _ in range(args.warmup):
+        attn.attn_decode(q, kc, vc, table, lens, o, lse, float(x["scale"]), **kw)
+    K = args.steps
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, b in kev:
+        a.record()
+        b.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    sclk = SclkSampler()
+    with sclk:
+        start.record()
+        for i in range(K):
+            attn.attn_decode(q, kc, vc, table, lens, o, lse, float(x["scale"]),
+                             timing_events=kev[i], **kw)
+        end.record()
+        torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / K
+    kern = sorted(a.elapsed_time(b) for a, b in kev)
+    kern_ms = sum(kern) / K
+    positions = int(x["seq_lens"].astype(np.int64).sum())
+    hbm_bytes = positions * w.H * w.d * 2 * 2 + w.B * w.H * w.Lq * (w.d * 2 * 2 + 4)
+    gbs = hbm_bytes / (kern_ms * 1e-3) / 1e9
+    out = {
+        "metric": "attention decode GB/s (compulsory bytes: every cached K and V row once, q, "
+                  "O, L), 1 MI355X",
+        "value": round(hbm_bytes / (step_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0, 1) q and paged K/V cache rounded to bf16; "
+                "uniform sequence lengths; scattered pages)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "d": w.d,
+                   "page": w.page, "causal": w.causal,
+                   "seq_lens": [int(v) for v in x["seq_lens"]],
+                   "compulsory_hbm_bytes": hbm_bytes, "decode_kernels_ms": round(kern_ms, 4),
+                   "decode_kernels_ms_median": round(kern[K // 2], 4),
+                   "decode_kernels_ms_min": round(kern[0], 4), "sclk_mhz": sclk.summary()},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(w, x)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_decode(w, x, budget_s=20.0):
+    """The fp64 decoding oracle on host cores, one sequence at a time until `budget_s` has
+    elapsed; GB/s of the same compulsory bytes."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i["num_threads"] for i in threadpool_info() if i["user_api"] == "blas"]
+                      or [1])
+    except Exception:
+        threads = 1
+    kc, vc = oracle.decode_bf16(x["k_cache"]), oracle.decode_bf16(x["v_cache"])  # inputs, once
+    t0 = time.perf_counter()
+    done, nbytes = 0, 0
+    for b in range(w.B):
+        q = oracle.decode_bf16(x["q"][b:b + 1])
+        oracle.decode_attention(q, kc, vc, x["page_table"][b:b + 1], x["seq_lens"][b:b + 1],
+                                float(x["scale"]), w.causal)
+        done += 1
+        nbytes += int(x["seq_lens"][b]) * w.H * w.d * 4 + w.H * w.Lq * (w.d * 4 + 4)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 decoding oracle on {done} of {w.B} sequences of {w.name} "
+                      f"(all {w.H} heads), {dt:.1f} s wall"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,8 +375,9 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="write a 512 MiB buffer before every step (evicts L2 and the 256 MB "
                          "Infinity Cache) and time each call alone: the cold-cache HBM figure")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
-                    help="bwd: time attn_bwd instead (10 d FLOPs per allowed pair; no CPU leg)")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode"), default="fwd",
+                    help="bwd: time attn_bwd instead (10 d FLOPs per allowed pair; no CPU leg); "
+                         "decode: time attn_decode on a paged-cache workload (GB/s)")
     ap.add_argument("--traffic", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH",
                                                     "COPY_WRITE"),
                     help="write profiles/traffic_fwd_<workload>.json from rocprofv3 counter CSVs")
@@ -292,6 +395,9 @@ def main():
 
     from exact_io_aware_21_amd import attn, inputs
 
+    if args.which == "decode":
+        bench_decode(args)
+        return
     w = inputs.WORKLOADS[args.workload]
     inp = inputs.make_inputs(w)
     dev = torch.device("cuda:0")

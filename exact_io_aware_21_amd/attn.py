@@ -1,6 +1,6 @@
 """Thin Python binding of libattn.so (include/attn.h): argument marshalling only.
 
-Every step of the forward and backward passes runs in the library's HIP kernels.  torch is used only to hold
+Every step of the forward, backward and decoding passes runs in the library's HIP kernels.  torch is used only to hold
 device memory and to name the current HIP stream.  There is no fallback: if the library is not
 built, or the device is not gfx950, calls raise.
 """
@@ -30,8 +30,8 @@ MASK_BITS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
              "window": ATTN_MASK_SLIDING_WINDOW, "document": ATTN_MASK_DOCUMENT}
 
 EXPORTS = ("attn_fwd", "attn_workspace_size", "attn_tile_shape", "attn_block_table",
-           "attn_block_table_host", "attn_bwd", "attn_bwd_workspace_size", "attn_strerror",
-           "attn_last_error")
+           "attn_block_table_host", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
+           "attn_decode_workspace_size", "attn_strerror", "attn_last_error")
 
 
 class attn_params(ctypes.Structure):
@@ -76,6 +76,10 @@ def lib():
         L.attn_bwd.restype = c_int
         L.attn_bwd_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_u32]
         L.attn_bwd_workspace_size.restype = ctypes.c_size_t
+        L.attn_decode.argtypes = [c_vp] * 7 + [c_int] * 7 + [c_f, c_u32, P, c_vp]
+        L.attn_decode.restype = c_int
+        L.attn_decode_workspace_size.argtypes = [c_int] * 6
+        L.attn_decode_workspace_size.restype = ctypes.c_size_t
         L.attn_strerror.argtypes = [c_int]
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_last_error.argtypes = []
@@ -221,6 +225,63 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale, variant, window=0, softca
                           _ptr(dk), _ptr(dv), B, H, N, d, float(scale), variant, ctypes.byref(p),
                           _stream(stream)))
     return dq, dk, dv
+
+
+def attn_decode_workspace_size(B: int, H: int, Lq: int, d: int, page_size: int,
+                               max_pages: int) -> int:
+    return int(lib().attn_decode_workspace_size(B, H, Lq, d, page_size, max_pages))
+
+
+def alloc_decode_workspace(B, H, Lq, d, page_size, max_pages, device="cuda"):
+    """A workspace tensor of the size attn_decode needs (allocated by torch, outside any call)."""
+    import torch
+    n = attn_decode_workspace_size(B, H, Lq, d, page_size, max_pages)
+    if n == 0:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "invalid shape for attn_decode_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def attn_decode(q, k_cache, v_cache, page_table, seq_lens, o, lse, scale, causal=True,
+                workspace=None, stream=None, timing_events=None):
+    """Calls attn_decode: q bf16 [B,H,Lq,d]; k_cache, v_cache bf16 [n_pages,H,page,d];
+    page_table int32 [B,max_pages]; seq_lens int32 [B]; o bf16 or fp32 [B,H,Lq,d]; lse fp32
+    [B,H,Lq] or None."""
+    import torch
+    B, H, Lq, d = q.shape
+    n_pages, Hc, page, dc = k_cache.shape
+    if q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [B,H,Lq,d] tensor")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or \
+                tuple(t.shape) != (n_pages, H, page, d):
+            raise ValueError(f"{name} must be a contiguous bf16 [n_pages,H,page,d] tensor")
+    if page_table.dtype != torch.int32 or not page_table.is_contiguous() or \
+            page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be a contiguous int32 [B,max_pages] tensor")
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be an int32 [B] tensor")
+    if o.dtype not in (torch.bfloat16, torch.float32) or not o.is_contiguous() or \
+            tuple(o.shape) != (B, H, Lq, d):
+        raise ValueError("o must be a contiguous bf16/fp32 [B,H,Lq,d] tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, H, Lq)):
+        raise ValueError("lse must be a contiguous fp32 [B,H,Lq] tensor")
+    max_pages = page_table.shape[1]
+    if workspace is None:
+        workspace = alloc_decode_workspace(B, H, Lq, d, page, max_pages, q.device)
+    p = make_params(o_dtype=ATTN_O_F32 if o.dtype == torch.float32 else ATTN_O_BF16,
+                    workspace=workspace)
+    ev = None
+    if timing_events is not None:
+        if not (timing_events[0].cuda_event and timing_events[1].cuda_event):
+            raise ValueError("timing events must have been recorded once before use")
+        ev = (ctypes.c_void_p * 2)(timing_events[0].cuda_event, timing_events[1].cuda_event)
+        p.timing_events = ctypes.cast(ev, ctypes.c_void_p)
+    variant = ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE
+    _check(lib().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                             _ptr(seq_lens), _ptr(o), _ptr(lse), B, H, Lq, d, page, max_pages,
+                             n_pages, float(scale), variant, ctypes.byref(p), _stream(stream)))
+    return o, lse
 
 
 def attn_block_table(B, H, N, d, variant, cls, kv_cnt, kv_list, window=0, doc_offsets=None,

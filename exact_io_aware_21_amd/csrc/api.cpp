@@ -129,6 +129,50 @@ BwdLayout bwd_layout(const Shape &s) {
   return w;
 }
 
+// Paged decoding: shape check and the split plan.  A split covers keys_per_split consecutive
+// positions (a multiple of the G = 256 / (d / 8) rows of a chunk).  The lengths live on the
+// device, so the plan is made for the longest possible sequence: about 8192 workgroups over all
+// (sequence, head) pairs when every sequence has that length (shorter ones leave their trailing
+// splits empty; those exit at once), and no split shorter than 256 positions.
+struct DecodePlan {
+  int lq_pad, rows, keys_per_split, nsplit;
+  size_t part_o, part_m, part_l, total;  // workspace offsets and size
+};
+
+int decode_plan(int B, int H, int Lq, int d, int page, int max_pages, DecodePlan &p) {
+  if (B < 1 || H < 1) return fail(ATTN_ERR_INVALID_ARG, "B and H must be >= 1");
+  if ((long long)B * H > 65535) return fail(ATTN_ERR_INVALID_ARG, "B*H must be <= 65535");
+  if (Lq < 1 || Lq > 8) return fail(ATTN_ERR_INVALID_ARG, "Lq must be in [1, 8]");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_INVALID_ARG, "d must be 64 or 128");
+  p.rows = 256 / (d / 8);
+  if (page < p.rows || page > 4096 || (page & (page - 1)))
+    return fail(ATTN_ERR_INVALID_ARG, "page_size must be a power of two in [%d, 4096]", p.rows);
+  if (max_pages < 1 || (long long)max_pages * page > (1 << 24))
+    return fail(ATTN_ERR_INVALID_ARG, "max_pages must be >= 1 with max_pages*page_size <= 2^24");
+  p.lq_pad = Lq <= 1 ? 1 : Lq <= 2 ? 2 : Lq <= 4 ? 4 : 8;
+  const long long max_len = (long long)max_pages * page;
+  const long long bh = (long long)B * H;
+  long long ns = (8192 + bh - 1) / bh;
+  const long long ns_max = (max_len + 255) / 256;
+  if (ns > ns_max) ns = ns_max;
+  if (ns > 65535) ns = 65535;  // grid dimension
+  if (ns < 1) ns = 1;
+  long long kps = (max_len + ns - 1) / ns;
+  kps = (kps + p.rows - 1) / p.rows * p.rows;
+  p.keys_per_split = (int)kps;
+  p.nsplit = (int)((max_len + kps - 1) / kps);
+  const size_t nparts = (size_t)bh * p.nsplit * p.lq_pad;
+  size_t off = 0;
+  p.part_o = off;
+  off = align256(off + nparts * d * 4);
+  p.part_m = off;
+  off = align256(off + nparts * 4);
+  p.part_l = off;
+  off = align256(off + nparts * 4);
+  p.total = off;
+  return ATTN_OK;
+}
+
 int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
@@ -386,6 +430,73 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
   if (attn::launch_bwd(a, d, (variant & ATTN_MOD_ALIBI) != 0, (variant & ATTN_MOD_SOFTCAP) != 0,
                        st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "backward kernel launch failed");
+  if (ev && hipEventRecord((hipEvent_t)ev[1], st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "timing event record failed");
+  return ATTN_OK;
+}
+
+size_t attn_decode_workspace_size(int B, int H, int Lq, int d, int page_size, int max_pages) {
+  DecodePlan p;
+  if (decode_plan(B, H, Lq, d, page_size, max_pages, p) != ATTN_OK) return 0;
+  return p.total;
+}
+
+int attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                const int32_t *page_table, const int32_t *seq_lens, void *o, float *lse, int B,
+                int H, int Lq, int d, int page_size, int max_pages, int n_pages, float scale,
+                uint32_t variant, const attn_params *params, void *stream) {
+  DecodePlan p;
+  int rc = decode_plan(B, H, Lq, d, page_size, max_pages, p);
+  if (rc) return rc;
+  if (n_pages < 1) return fail(ATTN_ERR_INVALID_ARG, "n_pages must be >= 1");
+  if (variant != ATTN_MASK_NONE && variant != ATTN_MASK_CAUSAL)
+    return fail(ATTN_ERR_INVALID_ARG, "decode supports ATTN_MASK_NONE and ATTN_MASK_CAUSAL only");
+  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !o)
+    return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, page_table, seq_lens and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
+  if (((uintptr_t)page_table | (uintptr_t)seq_lens | (uintptr_t)lse) & 3u)
+    return fail(ATTN_ERR_INVALID_ARG, "page_table, seq_lens or lse misaligned");
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+  if (!params) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (params->o_dtype != ATTN_O_BF16 && params->o_dtype != ATTN_O_F32)
+    return fail(ATTN_ERR_INVALID_ARG, "unknown o_dtype");
+  if (!params->workspace || ((uintptr_t)params->workspace & 255u))
+    return fail(ATTN_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (params->workspace_bytes < p.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", params->workspace_bytes,
+                p.total);
+  if ((rc = check_device())) return rc;
+
+  const hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)params->workspace;
+  attn::DecodeArgs a{};
+  a.q = (const uint16_t *)q;
+  a.k_cache = (const uint16_t *)k_cache;
+  a.v_cache = (const uint16_t *)v_cache;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.o = o;
+  a.lse = lse;
+  a.part_o = (float *)(ws + p.part_o);
+  a.part_m = (float *)(ws + p.part_m);
+  a.part_l = (float *)(ws + p.part_l);
+  a.B = B;
+  a.H = H;
+  a.Lq = Lq;
+  a.lq_pad = p.lq_pad;
+  a.page = page_size;
+  a.max_pages = max_pages;
+  a.n_pages = n_pages;
+  a.keys_per_split = p.keys_per_split;
+  a.nsplit = p.nsplit;
+  a.causal = variant == ATTN_MASK_CAUSAL;
+  a.c = scale * 1.4426950408889634f;
+  void *const *ev = params->timing_events;
+  if (ev && hipEventRecord((hipEvent_t)ev[0], st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "timing event record failed");
+  if (attn::launch_decode(a, d, params->o_dtype == ATTN_O_F32, st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "decode kernel launch failed");
   if (ev && hipEventRecord((hipEvent_t)ev[1], st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "timing event record failed");
   return ATTN_OK;

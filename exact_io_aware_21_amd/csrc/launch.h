@@ -59,6 +59,21 @@ struct BwdArgs {
 hipError_t launch_bwd_dot(const BwdArgs &a, int d, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, int d, bool alibi, bool softcap, hipStream_t stream);
 
+// Paged-cache decoding (decode.hip).
+struct DecodeArgs {
+  const uint16_t *q;                 // bf16 [B][H][Lq][D]
+  const uint16_t *k_cache, *v_cache; // bf16 [n_pages][H][page][D]
+  const int32_t *page_table;         // [B][max_pages]
+  const int32_t *seq_lens;           // [B]
+  void *o;                           // bf16 or fp32 [B][H][Lq][D]
+  float *lse;                        // fp32 [B][H][Lq] or null
+  float *part_o, *part_m, *part_l;   // split partials [B*H][nsplit][lq_pad]([D])
+  int B, H, Lq, lq_pad, page, max_pages, n_pages, keys_per_split, nsplit, causal;
+  float c;  // scale * log2(e)
+};
+
+hipError_t launch_decode(const DecodeArgs &a, int d, bool out_f32, hipStream_t stream);
+
 hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Npad, int d,
                           hipStream_t stream);
 hipError_t launch_block_table(MaskDesc m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,

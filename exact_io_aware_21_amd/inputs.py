@@ -139,3 +139,67 @@ def make_inputs(w: Workload, with_qkv: bool = True) -> dict:
         inp["doc_lengths"] = lens
         inp["doc_offsets"] = doc_offsets(lens, w.N)
     return inp
+
+
+# ---------------------------------------------------------------------------------------------
+# Paged key/value cache for decoding.
+#
+# Recipe (numpy PCG64, default_rng((seed, 7))): sequence lengths uniform integers on
+# [len_lo, len_hi] (at least Lq); each sequence gets ceil(len / page) pages, and the pool holds
+# those plus `spare` extra pages; the physical page of every logical page is a random
+# permutation of the pool (so a sequence's pages are scattered, as in a shared cache);
+# unused table entries point at page 0.  Then K cache, V cache ([n_pages, H, page, d]) and Q
+# ([B, H, Lq, d]) are standard_normal * sigma rounded to bfloat16, in that order.
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One decoding workload: B sequences of H heads, Lq query rows each, over a paged cache."""
+
+    name: str
+    B: int
+    H: int
+    Lq: int
+    d: int
+    page: int
+    len_lo: int
+    len_hi: int
+    causal: bool = True
+    sigma: float = 1.0
+    seed: int = 11
+    spare: int = 3
+    max_pages: int = field(default=None)  # None -> ceil(len_hi / page)
+
+    def scale_f32(self) -> np.float32:
+        return np.float32(1.0 / math.sqrt(self.d))
+
+
+DECODE_WORKLOADS = {
+    # one new token per sequence against 2k-14k cached tokens: 1.07 GB of K and V per step
+    "decode_b8h32_len2k_14k_d128_p64": DecodeWorkload(
+        "decode_b8h32_len2k_14k_d128_p64", B=8, H=32, Lq=1, d=128, page=64, len_lo=2048,
+        len_hi=14336, seed=12),
+}
+
+
+def make_paged_inputs(w: DecodeWorkload) -> dict:
+    """q, k_cache, v_cache (bf16 bits), page_table, seq_lens (int32) and scalars."""
+    rng = np.random.default_rng((w.seed, 7))
+    lens = rng.integers(max(w.len_lo, w.Lq), w.len_hi, size=w.B, endpoint=True).astype(np.int32)
+    max_pages = w.max_pages or -(-w.len_hi // w.page)
+    need = [-(-int(n) // w.page) for n in lens]
+    n_pages = int(sum(need)) + w.spare
+    perm = rng.permutation(n_pages).astype(np.int32)
+    table = np.zeros((w.B, max_pages), dtype=np.int32)
+    at = 0
+    for b, k in enumerate(need):
+        table[b, :k] = perm[at:at + k]
+        at += k
+    out = {"workload": w, "scale": w.scale_f32(), "seq_lens": lens, "page_table": table,
+           "n_pages": n_pages}
+    for name, shape in (("k_cache", (n_pages, w.H, w.page, w.d)),
+                        ("v_cache", (n_pages, w.H, w.page, w.d)), ("q", (w.B, w.H, w.Lq, w.d))):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if w.sigma != 1.0:
+            x *= np.float32(w.sigma)
+        out[name] = f32_to_bf16_bits(x)
+    return out

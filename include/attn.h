@@ -1,5 +1,6 @@
 /*
- * attn.h -- C ABI of the MI355X (gfx950) FlashAttention forward library (libattn.so).
+ * attn.h -- C ABI of the MI355X (gfx950) FlashAttention library (libattn.so): the forward pass,
+ * its backward pass, and decoding over a paged key/value cache.
  *
  * What it computes.  For every batch entry b and head h, with Q, K, V in R^{N x d}:
  *     O = softmax(S) V,   S_ij = modified score of query i and key j,
@@ -156,6 +157,45 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
 /* Bytes of workspace attn_bwd needs (0 on invalid arguments): D (fp32 [B][H][N]) and, for the
    masked kinds, the block table. */
 size_t attn_bwd_workspace_size(int B, int H, int N, int d, uint32_t variant);
+
+/*
+ * attn_decode -- attention of the last Lq positions of each sequence over a paged key/value
+ * cache (decoding).  Page "FlashAttention/es", section "Variantes y sucesores", names
+ * PagedAttention: at inference the cache is cut into pages shared by many sequences.  The
+ * result is the plain attention of the definition above over each sequence's keys and values
+ * in position order, computed by split-KV: each workgroup forms a partial (m, l, O) over a range
+ * of positions with the online softmax (section "El truco del softmax en línea"), and a second
+ * kernel merges the partials of a (sequence, head) with the same identity.
+ *   q          : device, bf16 [B][H][Lq][d], 16-byte aligned; row i of sequence b is position
+ *                seq_lens[b] - Lq + i.
+ *   k_cache, v_cache : device, bf16 [n_pages][H][page_size][d], 16-byte aligned.  Position t
+ *                of sequence b is slot t % page_size of page page_table[b][t / page_size].
+ *   page_table : device, int32 [B][max_pages], page indices in [0, n_pages).
+ *   seq_lens   : device, int32 [B], lengths in [Lq, max_pages * page_size].
+ *   o          : device, [B][H][Lq][d], bf16 or fp32 per params->o_dtype, 16-byte aligned.
+ *   lse        : device, fp32 [B][H][Lq], natural-log L; NULL skips it.
+ *   B, H       : >= 1, B*H <= 65535.   Lq : 1..8.   d : 64 or 128.
+ *   page_size  : a power of two in [256 / (d / 8), 4096] (16 for d = 128, 32 for d = 64).
+ *   max_pages  : >= 1, max_pages * page_size <= 2^24.   n_pages : >= 1.
+ *   scale      : finite.
+ *   variant    : ATTN_MASK_CAUSAL (query i sees positions <= seq_lens[b] - Lq + i) or
+ *                ATTN_MASK_NONE (every position < seq_lens[b]); no score modifications.
+ *   params     : required; workspace of >= attn_decode_workspace_size() bytes, 256-byte
+ *                aligned; o_dtype; timing_events, if set, bracket the two decode kernels.
+ * Device data is not validated: page indices outside [0, n_pages) are clamped into it and
+ * lengths into [0, max_pages * page_size] (wrong values, no out-of-bounds access); a query row
+ * with no allowed position gets O = 0 and L = -inf.
+ * Precision: fp32 scores and accumulation from the bf16 inputs; O rounded once at the end.
+ * Returns ATTN_OK or an error code; no HIP call is made for invalid arguments.
+ */
+int attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                const int32_t *page_table, const int32_t *seq_lens, void *o, float *lse, int B,
+                int H, int Lq, int d, int page_size, int max_pages, int n_pages, float scale,
+                uint32_t variant, const attn_params *params, void *stream);
+
+/* Bytes of workspace attn_decode needs (0 on invalid arguments): the split partials, fp32
+   [B*H][n_split][Lq rounded up to 1, 2, 4 or 8] x (d + 2). */
+size_t attn_decode_workspace_size(int B, int H, int Lq, int d, int page_size, int max_pages);
 
 const char *attn_strerror(int code);
 const char *attn_last_error(void);

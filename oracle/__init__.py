@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the attention forward and backward passes.
+"""fp64 CPU oracle for the attention forward and backward passes and paged decoding.
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check in __graft_entry__ and by the
 CPU-baseline leg of bench.py, never by the HIP path.  It shares no code with that path.
@@ -6,8 +6,10 @@ CPU-baseline leg of bench.py, never by the HIP path.  It shares no code with tha
 from .attention import (MASKS, allowed, allowed_pair_count, attention, attention_blocked,
                         decode_bf16, doc_index, scores)
 from .backward import attention_backward, backward_magnitudes, backward_row_dot
+from .decode import decode_attention, gather_sequence
 from .tiles import tile_class_counts, tile_table
 
 __all__ = ["MASKS", "allowed", "allowed_pair_count", "attention", "attention_backward",
-           "attention_blocked", "backward_magnitudes", "backward_row_dot", "decode_bf16", "doc_index", "scores",
+           "attention_blocked", "backward_magnitudes", "backward_row_dot", "decode_attention",
+           "decode_bf16", "doc_index", "gather_sequence", "scores",
            "tile_class_counts", "tile_table"]

@@ -240,3 +240,79 @@ def test_bwd_rejects_small_workspace():
 @pytest.mark.skipif(_gpu_present(), reason="only meaningful on a host without a GPU")
 def test_bwd_valid_call_without_gpu_reports_unsupported_device():
     assert _call_bwd() == attn.ATTN_ERR_UNSUPPORTED_DEVICE
+
+
+# --- paged decoding entry point ---------------------------------------------------------------
+def test_decode_workspace_size():
+    # fp32 partials [B*H][n_split][Lq padded to 1/2/4/8] x d, then m and l; about 8192
+    # workgroups over all (sequence, head) pairs, no split shorter than 256 positions.
+    al = lambda x: (x + 255) // 256 * 256
+    for (B, H, Lq, d, page, max_pages) in [(16, 32, 1, 128, 64, 256), (1, 1, 3, 64, 32, 4),
+                                           (2, 8, 8, 128, 16, 1000)]:
+        rows = 256 // (d // 8)
+        max_len = max_pages * page
+        ns = min(-(-8192 // (B * H)), -(-max_len // 256))
+        kps = -(-(-(-max_len // ns)) // rows) * rows
+        nsplit = -(-max_len // kps)
+        lqp = 1 if Lq <= 1 else 2 if Lq <= 2 else 4 if Lq <= 4 else 8
+        parts = B * H * nsplit * lqp
+        want = al(parts * d * 4) + 2 * al(parts * 4)
+        assert attn.attn_decode_workspace_size(B, H, Lq, d, page, max_pages) == want
+
+
+@pytest.mark.parametrize("args", [
+    (0, 1, 1, 128, 64, 4), (1, 1, 0, 128, 64, 4), (1, 1, 9, 128, 64, 4), (1, 1, 1, 96, 64, 4),
+    (1, 1, 1, 128, 8, 4), (1, 1, 1, 64, 16, 4), (1, 1, 1, 128, 48, 4), (1, 1, 1, 128, 8192, 4),
+    (1, 1, 1, 128, 64, 0), (300, 300, 1, 128, 64, 4), (1, 1, 1, 128, 4096, 1 << 13),
+])
+def test_decode_workspace_size_rejects(args):
+    assert attn.attn_decode_workspace_size(*args) == 0
+
+
+def _call_decode(ptrs=None, B=1, H=1, Lq=1, d=128, page=64, max_pages=4, n_pages=4, scale=0.1,
+                 variant=1, params="default"):
+    L = attn.lib()
+    p = attn.attn_params()
+    p.workspace = 256
+    p.workspace_bytes = 1 << 40
+    pp = ctypes.byref(p) if params == "default" else params
+    args = {"q": 16, "k": 16, "v": 16, "table": 16, "lens": 16, "o": 16, "lse": 16}
+    args.update(ptrs or {})
+    return L.attn_decode(args["q"], args["k"], args["v"], args["table"], args["lens"], args["o"],
+                         args["lse"], B, H, Lq, d, page, max_pages, n_pages, scale, variant, pp,
+                         None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"ptrs": {"q": None}}, attn.ATTN_ERR_INVALID_ARG),
+    ({"ptrs": {"table": None}}, attn.ATTN_ERR_INVALID_ARG),
+    ({"ptrs": {"lens": None}}, attn.ATTN_ERR_INVALID_ARG),
+    ({"ptrs": {"k": 8}}, attn.ATTN_ERR_INVALID_ARG),
+    ({"ptrs": {"table": 2}}, attn.ATTN_ERR_INVALID_ARG),
+    ({"ptrs": {"lse": 6}}, attn.ATTN_ERR_INVALID_ARG),
+    ({"Lq": 9}, attn.ATTN_ERR_INVALID_ARG),
+    ({"page": 24}, attn.ATTN_ERR_INVALID_ARG),
+    ({"n_pages": 0}, attn.ATTN_ERR_INVALID_ARG),
+    ({"variant": attn.ATTN_MASK_SLIDING_WINDOW}, attn.ATTN_ERR_INVALID_ARG),
+    ({"variant": attn.ATTN_MASK_CAUSAL | attn.ATTN_MOD_ALIBI}, attn.ATTN_ERR_INVALID_ARG),
+    ({"scale": float("inf")}, attn.ATTN_ERR_INVALID_ARG),
+    ({"params": None}, attn.ATTN_ERR_INVALID_ARG),
+])
+def test_decode_rejects_invalid_arguments(kw, code):
+    assert _call_decode(**kw) == code
+    assert attn.lib().attn_last_error() != b""
+
+
+def test_decode_rejects_small_workspace():
+    p = attn.attn_params()
+    p.workspace, p.workspace_bytes = 256, 100
+    assert _call_decode(params=ctypes.byref(p)) == attn.ATTN_ERR_WORKSPACE
+    p.workspace, p.workspace_bytes = 16, 1 << 40
+    assert _call_decode(params=ctypes.byref(p)) == attn.ATTN_ERR_WORKSPACE
+
+
+@pytest.mark.skipif(_gpu_present(), reason="only meaningful on a host without a GPU")
+def test_decode_valid_call_without_gpu_reports_unsupported_device():
+    assert _call_decode() == attn.ATTN_ERR_UNSUPPORTED_DEVICE
+    assert _call_decode(variant=attn.ATTN_MASK_NONE, ptrs={"lse": None}) == \
+        attn.ATTN_ERR_UNSUPPORTED_DEVICE
