@@ -211,6 +211,30 @@ __global__ __launch_bounds__(512) void mixed_fma(float *out, float seed) {
   if (s == 1234.5f) out[threadIdx.x] = s;
 }
 
+// Read-only stream: 8 independent 16-byte loads in flight per lane, XOR-folded.
+__global__ __launch_bounds__(256) void read_kernel(const f32x4 *__restrict__ src, size_t n,
+                                                   float *out) {
+  constexpr int UN = 8;
+  f32x4 acc = {};
+  const size_t stride = (size_t)gridDim.x * 256 * UN;
+  for (size_t base = (size_t)blockIdx.x * 256 * UN + threadIdx.x; base < n; base += stride) {
+    f32x4 v[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) v[u] = (base + u * 256 < n) ? src[base + u * 256] : f32x4{};
+#pragma unroll
+    for (int u = 0; u < UN; ++u) acc += v[u];
+  }
+  if (acc[0] + acc[1] + acc[2] + acc[3] == 1234.5f) out[blockIdx.x & 4095] = acc[0];  // out holds 4096 floats
+}
+
+// 4 KB blocks (256 x 16 bytes) read in the order perm gives, one workgroup per block.
+__global__ __launch_bounds__(256) void read_blocks_kernel(const f32x4 *__restrict__ src,
+                                                          const int *perm, int nblk, float *out) {
+  f32x4 acc = {};
+  for (int bb = blockIdx.x; bb < nblk; bb += gridDim.x) acc += src[(size_t)perm[bb] * 256 + threadIdx.x];
+  if (acc[0] + acc[1] + acc[2] + acc[3] == 1234.5f) out[blockIdx.x & 4095] = acc[0];  // out holds 4096 floats
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(const f32x4 *__restrict__ src,
                                                    f32x4 *__restrict__ dst, size_t n) {
   for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
@@ -327,6 +351,23 @@ int main() {
     CHECK(hipMemset(a, 0, n * sizeof(f32x4)));
     const float ms = time_ms([&] { copy_kernel<<<cus * 16, 256>>>(a, b, n); }, 10);
     printf("HBM copy 1 GiB: %.1f GB/s (read + write)\n", 2.0 * n * sizeof(f32x4) / ms / 1e6);
+    const float ms_r = time_ms([&] { read_kernel<<<cus * 8, 256>>>(a, n, out); }, 10);
+    printf("HBM read 1 GiB: %.1f GB/s (8 loads in flight per lane)\n", n * sizeof(f32x4) / ms_r / 1e6);
+    const int nblk = (int)(n / 256);
+    std::vector<int> hp(nblk);
+    for (int i = 0; i < nblk; ++i) hp[i] = i;
+    unsigned x = 12345u;  // Fisher-Yates with a fixed LCG: a reproducible block order
+    for (int i = nblk - 1; i > 0; --i) {
+      x = x * 1664525u + 1013904223u;
+      std::swap(hp[i], hp[x % (unsigned)(i + 1)]);
+    }
+    int *perm;
+    CHECK(hipMalloc(&perm, nblk * sizeof(int)));
+    CHECK(hipMemcpy(perm, hp.data(), nblk * sizeof(int), hipMemcpyHostToDevice));
+    const float ms_p = time_ms([&] { read_blocks_kernel<<<cus * 32, 256>>>(a, perm, nblk, out); }, 10);
+    printf("HBM read 1 GiB as 4 KB blocks in a random order: %.1f GB/s\n",
+           n * sizeof(f32x4) / ms_p / 1e6);
+    CHECK(hipFree(perm));
     CHECK(hipFree(a));
     CHECK(hipFree(b));
   }
