@@ -31,7 +31,8 @@ MASK_BITS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
 
 EXPORTS = ("attn_fwd", "attn_workspace_size", "attn_tile_shape", "attn_block_table",
            "attn_block_table_host", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
-           "attn_decode_workspace_size", "attn_strerror", "attn_last_error")
+           "attn_decode_workspace_size", "attn_quantize_fp8", "attn_strerror",
+           "attn_last_error")
 
 
 class attn_params(ctypes.Structure):
@@ -80,6 +81,8 @@ def lib():
         L.attn_decode.restype = c_int
         L.attn_decode_workspace_size.argtypes = [c_int] * 6
         L.attn_decode_workspace_size.restype = ctypes.c_size_t
+        L.attn_quantize_fp8.argtypes = [c_vp, c_vp, c_vp] + [c_int] * 5 + [c_vp]
+        L.attn_quantize_fp8.restype = c_int
         L.attn_strerror.argtypes = [c_int]
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_last_error.argtypes = []
@@ -282,6 +285,24 @@ def attn_decode(q, k_cache, v_cache, page_table, seq_lens, o, lse, scale, causal
                              _ptr(seq_lens), _ptr(o), _ptr(lse), B, H, Lq, d, page, max_pages,
                              n_pages, float(scale), variant, ctypes.byref(p), _stream(stream)))
     return o, lse
+
+
+def attn_quantize_fp8(x, codes, scales, rows, stream=None):
+    """Block quantization of x (bf16 [B,H,N,d]) into codes (uint8, same shape) and scales
+    (fp32 [B,H,ceil(N/rows)])."""
+    import torch
+    B, H, N, d = x.shape
+    if x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [B,H,N,d] tensor")
+    if codes.dtype != torch.uint8 or not codes.is_contiguous() or tuple(codes.shape) != (B, H, N, d):
+        raise ValueError("codes must be a contiguous uint8 [B,H,N,d] tensor")
+    nb = -(-N // rows)
+    if scales.dtype != torch.float32 or not scales.is_contiguous() or \
+            tuple(scales.shape) != (B, H, nb):
+        raise ValueError("scales must be a contiguous fp32 [B,H,ceil(N/rows)] tensor")
+    _check(lib().attn_quantize_fp8(_ptr(x), _ptr(codes), _ptr(scales), B, H, N, d, rows,
+                                   _stream(stream)))
+    return codes, scales
 
 
 def attn_block_table(B, H, N, d, variant, cls, kv_cnt, kv_list, window=0, doc_offsets=None,

@@ -435,6 +435,24 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
   return ATTN_OK;
 }
 
+int attn_quantize_fp8(const void *x, uint8_t *codes, float *scales, int B, int H, int N, int d,
+                      int rows, void *stream) {
+  if (B < 1 || H < 1 || N < 1) return fail(ATTN_ERR_INVALID_ARG, "B, H and N must be >= 1");
+  if ((long long)B * H > 65535) return fail(ATTN_ERR_INVALID_ARG, "B*H must be <= 65535");
+  if (N > (1 << 24)) return fail(ATTN_ERR_INVALID_ARG, "N must be <= 2^24");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_INVALID_ARG, "d must be 64 or 128");
+  if (rows < 1 || rows > 4096) return fail(ATTN_ERR_INVALID_ARG, "rows must be in [1, 4096]");
+  if (!x || !codes || !scales) return fail(ATTN_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+  if (!aligned16(x) || !aligned16(codes)) return fail(ATTN_ERR_INVALID_ARG, "x and codes must be 16-byte aligned");
+  if ((uintptr_t)scales & 3u) return fail(ATTN_ERR_INVALID_ARG, "scales misaligned");
+  int rc = check_device();
+  if (rc) return rc;
+  if (attn::launch_quant_fp8((const uint16_t *)x, codes, scales, B * H, N, d, rows,
+                             (hipStream_t)stream) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "quantization kernel launch failed");
+  return ATTN_OK;
+}
+
 size_t attn_decode_workspace_size(int B, int H, int Lq, int d, int page_size, int max_pages) {
   DecodePlan p;
   if (decode_plan(B, H, Lq, d, page_size, max_pages, p) != ATTN_OK) return 0;

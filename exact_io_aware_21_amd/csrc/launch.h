@@ -74,6 +74,10 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs &a, int d, bool out_f32, hipStream_t stream);
 
+// FP8 block quantization (fp8.hip): codes [BH][N][d] E4M3, scales [BH][ceil(N / rows)].
+hipError_t launch_quant_fp8(const uint16_t *x, uint8_t *codes, float *scales, int BH, int N,
+                            int d, int rows, hipStream_t stream);
+
 hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Npad, int d,
                           hipStream_t stream);
 hipError_t launch_block_table(MaskDesc m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,

@@ -159,6 +159,23 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
 size_t attn_bwd_workspace_size(int B, int H, int N, int d, uint32_t variant);
 
 /*
+ * attn_quantize_fp8 -- the block quantization of the FP8 forward pass (page "FlashAttention/es",
+ * section "Variantes y sucesores": FP8 with per-block scaling; page "FlashAttention-3 y
+ * torch.compile ...", section "FlashAttention-3: Asincronía y Explotación del Silicio Hopper":
+ * a scale estimated from the data at run time).  For each (b, h) and block of `rows` rows:
+ *     scale = amax / 448 (float32; 1 for an all-zero block),  code = E4M3(x / scale)
+ * with a correctly rounded float32 division and round-to-nearest-even to E4M3 (no infinities,
+ * largest finite 448).
+ *   x      : device, bf16 [B][H][N][d], 16-byte aligned.
+ *   codes  : device, uint8 [B][H][N][d] E4M3, 16-byte aligned.
+ *   scales : device, fp32 [B][H][ceil(N / rows)].
+ *   B*H <= 65535, 1 <= N <= 2^24, d 64 or 128, rows 1..4096.
+ * attn_fwd with ATTN_PREC_FP8 applies it to Q (rows = Br) and K (rows = Bc) in its workspace.
+ */
+int attn_quantize_fp8(const void *x, uint8_t *codes, float *scales, int B, int H, int N, int d,
+                      int rows, void *stream);
+
+/*
  * attn_decode -- attention of the last Lq positions of each sequence over a paged key/value
  * cache (decoding).  Page "FlashAttention/es", section "Variantes y sucesores", names
  * PagedAttention: at inference the cache is cut into pages shared by many sequences.  The

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "attn.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -316,3 +316,20 @@ def test_decode_valid_call_without_gpu_reports_unsupported_device():
     assert _call_decode() == attn.ATTN_ERR_UNSUPPORTED_DEVICE
     assert _call_decode(variant=attn.ATTN_MASK_NONE, ptrs={"lse": None}) == \
         attn.ATTN_ERR_UNSUPPORTED_DEVICE
+
+
+# --- FP8 block quantization entry point -------------------------------------------------------
+@pytest.mark.parametrize("args,code", [
+    ((16, 16, 16, 1, 1, 64, 128, 256), attn.ATTN_ERR_UNSUPPORTED_DEVICE),
+    ((None, 16, 16, 1, 1, 64, 128, 256), attn.ATTN_ERR_INVALID_ARG),
+    ((8, 16, 16, 1, 1, 64, 128, 256), attn.ATTN_ERR_INVALID_ARG),
+    ((16, 16, 2, 1, 1, 64, 128, 256), attn.ATTN_ERR_INVALID_ARG),
+    ((16, 16, 16, 1, 1, 0, 128, 256), attn.ATTN_ERR_INVALID_ARG),
+    ((16, 16, 16, 1, 1, 64, 96, 256), attn.ATTN_ERR_INVALID_ARG),
+    ((16, 16, 16, 1, 1, 64, 128, 0), attn.ATTN_ERR_INVALID_ARG),
+    ((16, 16, 16, 1, 1, 64, 128, 5000), attn.ATTN_ERR_INVALID_ARG),
+])
+def test_quantize_fp8_argument_checks(args, code):
+    if code == attn.ATTN_ERR_UNSUPPORTED_DEVICE and _gpu_present():
+        pytest.skip("only meaningful on a host without a GPU")
+    assert attn.lib().attn_quantize_fp8(*args, None) == code
