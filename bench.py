@@ -1,7 +1,7 @@
 """Benchmark of the attention forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--cold] [--pass fwd|bwd]
+                    [--cold] [--pass fwd|bwd|decode] [--fp8]
 
 A step is one attn_fwd call over one batch of seeded synthetic input already resident in HBM:
 the V transpose-pack kernel, the block-table kernel (masked kinds) and the forward kernel.
@@ -20,6 +20,12 @@ the same stream, against the published dense bf16 MFMA peak of MI355X.
 times each call alone with its own event pair: the cold-cache figure for the short, HBM-bound
 workloads.  The default is warm: back-to-back calls.
 
+--fp8 times the FP8 forward pass (ATTN_PREC_FP8: Q K^T from E4M3 codes of Q and K with one
+scale per 256-row Q tile and per 64-key K tile, P V in fp16).  A step then also holds the K
+quantization kernel.  Half of the counted FLOPs (Q K^T) run at the fp8 MFMA rate and half (P V)
+at the fp16 rate, so the kernel's peak is the harmonic mix of the two published peaks:
+1 / (0.5 / 5000 + 0.5 / 2500) = 3333 TFLOP/s.
+
 The "cpu_baseline" object times the fp64 CPU oracle (a plain, untuned reference) on the host
 cores on a bounded sample of the same workload, in the same unit.
 """
@@ -35,6 +41,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
+PEAK_FP8_TFLOPS = 5000.0   # MI355X published dense fp8 MFMA peak
+# FP8 forward: Q K^T (half the FLOPs) on fp8 MFMAs, P V (the other half) on fp16 MFMAs
+PEAK_FP8_FWD_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
 MAX_SCLK_MHZ = 2400.0      # MI355X peak engine clock, the one the MFMA peak is quoted at
 METRIC = "attention fwd TFLOP/s (unmasked FLOPs) and % of MFMA peak, 1 MI355X"
@@ -167,9 +176,10 @@ class SclkSampler:
                 "source": self.path}
 
 
-def cpu_baseline(w, inp, budget_s=20.0, chunk=2048):
+def cpu_baseline(w, inp, budget_s=20.0, chunk=2048, fp8=False):
     """The fp64 oracle on host cores, over whole heads in order (query rows in chunks of `chunk`)
-    until `budget_s` has elapsed.  Throughput in the metric's unit (unmasked TFLOP/s)."""
+    until `budget_s` has elapsed.  Throughput in the metric's unit (unmasked TFLOP/s).  fp8: Q and
+    K of each head are block-quantized and dequantized by the oracle first (timed as well)."""
     import numpy as np
     import oracle
     try:
@@ -187,6 +197,9 @@ def cpu_baseline(w, inp, budget_s=20.0, chunk=2048):
         q = oracle.decode_bf16(inp["q"][b:b + 1, h:h + 1])
         k = oracle.decode_bf16(inp["k"][b:b + 1, h:h + 1])
         v = oracle.decode_bf16(inp["v"][b:b + 1, h:h + 1])
+        if fp8:
+            q = oracle.dequantize_blocks(*oracle.quantize_blocks(q, 256), 256)
+            k = oracle.dequantize_blocks(*oracle.quantize_blocks(k, 64), 64)
         offs = None if inp["doc_offsets"] is None else inp["doc_offsets"][b:b + 1]
         slopes = None if inp["slopes"] is None else inp["slopes"][h:h + 1]
         for r0 in range(0, w.N, chunk):
@@ -202,7 +215,8 @@ def cpu_baseline(w, inp, budget_s=20.0, chunk=2048):
     dt = time.perf_counter() - t0
     return {"value": 4.0 * w.d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"fp64 oracle on {rows_done // w.N} whole head(s) of {w.name} "
+            "sample": f"fp64 {'FP8 ' if fp8 else ''}oracle on {rows_done // w.N} whole head(s) "
+                      f"of {w.name} "
                       f"({rows_done} query rows x {w.N} keys, {pairs} allowed pairs), "
                       f"{dt:.1f} s wall"}
 
@@ -378,6 +392,8 @@ def main():
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode"), default="fwd",
                     help="bwd: time attn_bwd instead (10 d FLOPs per allowed pair; no CPU leg); "
                          "decode: time attn_decode on a paged-cache workload (GB/s)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 forward pass (ATTN_PREC_FP8; no score modifications)")
     ap.add_argument("--traffic", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH",
                                                     "COPY_WRITE"),
                     help="write profiles/traffic_fwd_<workload>.json from rocprofv3 counter CSVs")
@@ -411,7 +427,9 @@ def main():
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
     slopes = None if inp["slopes"] is None else torch.from_numpy(inp["slopes"]).to(dev)
     offs = None if inp["doc_offsets"] is None else torch.from_numpy(inp["doc_offsets"]).to(dev)
-    var = attn.variant_bits(w.mask, w.alibi, w.softcap > 0)
+    var = attn.variant_bits(w.mask, w.alibi, w.softcap > 0, fp8=args.fp8)
+    if args.fp8 and args.which != "fwd":
+        raise SystemExit("--fp8 applies to the forward pass only")
     ws = attn.alloc_workspace(w.B, w.H, w.N, w.d, var, dev)
     kw = dict(window=w.window, softcap=w.softcap, alibi_slopes=slopes, doc_offsets=offs,
               workspace=ws)
@@ -460,15 +478,19 @@ def main():
     achieved = flops / (kern_ms * 1e-3) / 1e12
     traffic = traffic_from_profile(w.name)
     sclk_rec = sclk.summary()
+    peak = PEAK_FP8_FWD_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
     if sclk_rec:  # the same peak scaled to the clock the device ran at
-        sclk_rec["mfma_peak_at_median_tflops"] = round(PEAK_BF16_TFLOPS * sclk_rec["median"] /
+        sclk_rec["mfma_peak_at_median_tflops"] = round(peak * sclk_rec["median"] /
                                                        MAX_SCLK_MHZ, 1)
         sclk_rec["frac_of_that_peak"] = round(achieved / sclk_rec["mfma_peak_at_median_tflops"], 4)
-    mfma_bound = flops / hbm_bytes > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    mfma_bound = flops / hbm_bytes > peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     if mfma_bound:
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic}
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": None if args.fp8 else traffic}
+        if args.fp8:
+            roof["peak_note"] = ("Q K^T on fp8 MFMAs (5000 TFLOP/s), P V on fp16 MFMAs "
+                                 "(2500 TFLOP/s), half the FLOPs each")
     else:
         gbs = hbm_bytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -477,9 +499,10 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3+fp16" if args.fp8 else "bf16",
         "data": "synthetic (seeded N(0, sigma^2) Q/K/V rounded to bf16)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
+        "config": {"workload": ("fp8_" if args.fp8 else "") + w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
                    "window": w.window, "alibi": w.alibi, "softcap": w.softcap,
                    "unmasked_gflop": round(flops / 1e9, 3),
                    "fwd_kernel_ms": round(kern_ms, 4),
@@ -491,7 +514,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inp)
+        out["cpu_baseline"] = cpu_baseline(w, inp, fp8=args.fp8)
     print(json.dumps(out), flush=True)
 
 

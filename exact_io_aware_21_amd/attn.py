@@ -18,6 +18,7 @@ ATTN_MASK_SLIDING_WINDOW = 2
 ATTN_MASK_DOCUMENT = 3
 ATTN_MOD_ALIBI = 1 << 4
 ATTN_MOD_SOFTCAP = 1 << 5
+ATTN_PREC_FP8 = 1 << 6
 ATTN_O_BF16 = 0
 ATTN_O_F32 = 1
 ATTN_OK = 0
@@ -97,12 +98,14 @@ def _check(rc):
         raise AttnError(rc, f"{L.attn_strerror(rc).decode()}: {L.attn_last_error().decode()}")
 
 
-def variant_bits(mask="none", alibi=False, softcap=False) -> int:
+def variant_bits(mask="none", alibi=False, softcap=False, fp8=False) -> int:
     v = MASK_BITS[mask]
     if alibi:
         v |= ATTN_MOD_ALIBI
     if softcap:
         v |= ATTN_MOD_SOFTCAP
+    if fp8:
+        v |= ATTN_PREC_FP8
     return v
 
 

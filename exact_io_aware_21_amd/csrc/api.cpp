@@ -24,7 +24,7 @@ int fail(int code, const char *fmt, ...) {
   return code;
 }
 
-constexpr uint32_t kKnownBits = 0xFu | ATTN_MOD_ALIBI | ATTN_MOD_SOFTCAP;
+constexpr uint32_t kKnownBits = 0xFu | ATTN_MOD_ALIBI | ATTN_MOD_SOFTCAP | ATTN_PREC_FP8;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
 
@@ -33,6 +33,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Shape {
   int B, H, N, d, n_qt, n_kt, Npad, Bm;
   uint32_t kind;
+  bool fp8;
 };
 
 // Validates the shape and variant bits; fills s.  No HIP call.
@@ -43,6 +44,11 @@ int check_shape(int B, int H, int N, int d, uint32_t variant, Shape &s) {
   if (variant & ~kKnownBits) return fail(ATTN_ERR_INVALID_ARG, "unknown variant bits");
   s.kind = variant & 0xFu;
   if (s.kind > ATTN_MASK_DOCUMENT) return fail(ATTN_ERR_INVALID_ARG, "unknown mask kind");
+  s.fp8 = (variant & ATTN_PREC_FP8) != 0;
+  if (s.fp8 && (variant & (ATTN_MOD_ALIBI | ATTN_MOD_SOFTCAP)))
+    return fail(ATTN_ERR_INVALID_ARG, "ATTN_PREC_FP8 takes no score modification");
+  if (s.fp8 && (long long)B * H > 65535)
+    return fail(ATTN_ERR_INVALID_ARG, "B*H must be <= 65535 with ATTN_PREC_FP8");
   s.B = B;
   s.H = H;
   s.N = N;
@@ -85,7 +91,7 @@ int check_params(const Shape &s, uint32_t variant, const attn_params *p, bool ne
 }
 
 struct WsLayout {
-  size_t vt, cls, cnt, list, total;
+  size_t vt, cls, cnt, list, k8, sk, total;
 };
 
 WsLayout ws_layout(const Shape &s) {
@@ -101,6 +107,12 @@ WsLayout ws_layout(const Shape &s) {
     off = align256(off + rows * 4);
     w.list = off;
     off = align256(off + rows * s.n_kt * 4);
+  }
+  if (s.fp8) {
+    w.k8 = off;
+    off = align256(off + (size_t)s.B * s.H * s.N * s.d);
+    w.sk = off;
+    off = align256(off + (size_t)s.B * s.H * s.n_kt * 4);
   }
   w.total = off;
   return w;
@@ -323,6 +335,16 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
     a.capL = params->softcap * log2e;
   }
   a.slopes = (variant & ATTN_MOD_ALIBI) ? params->alibi_slopes : nullptr;
+  if (s.fp8) {
+    // K to E4M3 codes with one scale per 64-key tile; Q is quantized inside the forward kernel.
+    uint8_t *k8 = (uint8_t *)(ws + wl.k8);
+    float *sk = (float *)(ws + wl.sk);
+    if (attn::launch_quant_fp8((const uint16_t *)k, k8, sk, B * H, N, d, attn::kBc, st) !=
+        hipSuccess)
+      return fail(ATTN_ERR_LAUNCH, "FP8 quantization kernel launch failed");
+    a.k8 = k8;
+    a.sk = sk;
+  }
   a.kind = (int)s.kind;
   a.window = s.kind == ATTN_MASK_SLIDING_WINDOW ? params->window : 0;
   a.max_docs = s.kind == ATTN_MASK_DOCUMENT ? params->max_docs : 0;
@@ -342,6 +364,7 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
   in.softcap = (variant & ATTN_MOD_SOFTCAP) != 0;
   in.pos_scale = !in.alibi && !in.softcap && scale > 0.f;
   in.out_f32 = params->o_dtype == ATTN_O_F32;
+  in.fp8 = s.fp8;
   void *const *ev = params->timing_events;
   if (ev && hipEventRecord((hipEvent_t)ev[0], st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "timing event record failed");
@@ -354,7 +377,7 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
 
 size_t attn_bwd_workspace_size(int B, int H, int N, int d, uint32_t variant) {
   Shape s;
-  if (check_shape(B, H, N, d, variant, s) != ATTN_OK) return 0;
+  if (check_shape(B, H, N, d, variant, s) != ATTN_OK || s.fp8) return 0;
   return bwd_layout(s).total;
 }
 
@@ -364,6 +387,7 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
   Shape s;
   int rc = check_shape(B, H, N, d, variant, s);
   if (rc) return rc;
+  if (s.fp8) return fail(ATTN_ERR_INVALID_ARG, "ATTN_PREC_FP8 is a forward-only variant");
   if ((long long)B * H > 65535) return fail(ATTN_ERR_INVALID_ARG, "B*H must be <= 65535");
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(ATTN_ERR_INVALID_ARG, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL");
@@ -442,8 +466,10 @@ int attn_quantize_fp8(const void *x, uint8_t *codes, float *scales, int B, int H
   if (N > (1 << 24)) return fail(ATTN_ERR_INVALID_ARG, "N must be <= 2^24");
   if (d != 64 && d != 128) return fail(ATTN_ERR_INVALID_ARG, "d must be 64 or 128");
   if (rows < 1 || rows > 4096) return fail(ATTN_ERR_INVALID_ARG, "rows must be in [1, 4096]");
-  if (!x || !codes || !scales) return fail(ATTN_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
-  if (!aligned16(x) || !aligned16(codes)) return fail(ATTN_ERR_INVALID_ARG, "x and codes must be 16-byte aligned");
+  if (!x || !codes || !scales)
+    return fail(ATTN_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+  if (!aligned16(x) || !aligned16(codes))
+    return fail(ATTN_ERR_INVALID_ARG, "x and codes must be 16-byte aligned");
   if ((uintptr_t)scales & 3u) return fail(ATTN_ERR_INVALID_ARG, "scales misaligned");
   int rc = check_device();
   if (rc) return rc;

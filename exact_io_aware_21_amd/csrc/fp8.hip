@@ -48,14 +48,10 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t *__restri
     const u32x4 v = *(const u32x4 *)(src + (size_t)ci * 8);
     uint32_t out[2];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float lo = __uint_as_float(v[w] << 16) / s;
-      const float hi = __uint_as_float(v[w] & 0xFFFF0000u) / s;
-      const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(lo, hi, 0, false) & 0xFFFFu;
-      if (w & 1)
-        out[w >> 1] |= pk << 16;
-      else
-        out[w >> 1] = pk;
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t w0 = v[2 * h], w1 = v[2 * h + 1];
+      out[h] = pack_e4m3x4(__uint_as_float(w0 << 16) / s, __uint_as_float(w0 & 0xFFFF0000u) / s,
+                           __uint_as_float(w1 << 16) / s, __uint_as_float(w1 & 0xFFFF0000u) / s);
     }
     *(uint2 *)(dst + (size_t)ci * 8) = make_uint2(out[0], out[1]);
   }

@@ -129,7 +129,13 @@ __global__ __launch_bounds__(256) void block_table_kernel(MaskDesc m, const int3
 // so on every SIMD one wave keeps the matrix core busy while the other does the softmax.
 // K_t and V_{t-1} are the LDS tiles read in slots 2t and 2t+1; K_{t+1} and V_t are fetched into
 // VGPRs at the start of slot 2t and written to the idle LDS buffers at the end of slot 2t+1.
-template <int D, bool ALIBI, bool SOFTCAP, bool POS, bool OUTF32>
+//
+// FP8 instances (FP8 = true) form the scores from E4M3 codes with v_mfma_scale_f32_32x32x64_f8f6f4:
+// the workgroup quantizes its own 256 Q rows (one scale s_q for the tile) and reads K as codes
+// with one scale s_k per 64-key tile (quantized by quant_fp8_kernel beforehand), so the score
+// block is s_q s_k (Q8 K8^T); the factor s_q s_k is folded into the base-2 scale of the V-phase.
+// K8 rows take D + 16 bytes in LDS (the same bank spread as the bf16 rows); P V is unchanged.
+template <int D, bool ALIBI, bool SOFTCAP, bool POS, bool OUTF32, bool FP8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     FwdArgs a) {
   constexpr int NT = 512;                // threads per workgroup
@@ -141,8 +147,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int NDB = D / 32;            // 32-column blocks of O
   constexpr int KP = pitch(D);           // LDS pitch of a K row (keys x D)
   constexpr int VP = pitch(kBc);         // LDS pitch of a V^T row (D x keys)
+  constexpr int KP8 = D + 16;            // LDS pitch of an FP8 K row, bytes
+  constexpr int KCH8 = D / 16;           // 16-byte chunks per FP8 K row
+  constexpr int NK8 = kBc * KCH8;        // 16-byte chunks per FP8 K tile
+  constexpr int KLDN = FP8 ? (NK8 + NT - 1) / NT : KLD;  // K chunks per thread per tile
+  constexpr int NKS8 = D / 64;           // k-steps of the FP8 score product
   static_assert(kBr == 256 && kBc == 64, "kernel is written for 256 x 64 tiles");
   static_assert(KLD >= 1 && VLD >= 1, "tile loads must cover the workgroup");
+  static_assert(!FP8 || (!ALIBI && !SOFTCAP), "FP8 instances take no score modification");
+  static_assert(kBc * KP8 <= kBc * pitch(D) * 2, "FP8 K tile must fit the K buffer");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBc * KP];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VP];
 
@@ -151,6 +164,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // group 0 and the other group 1 (SIMD id from the HW_ID register).  Correctness does not
   // depend on this choice, only the overlap of matrix-core and vector work does.
   __shared__ int simd_of[8];
+  __shared__ float qmax[8];
   if (lane == 0) simd_of[wave] = __builtin_amdgcn_s_getreg(kHwRegSimdId) & 3;
   __syncthreads();
   int grp = 0;
@@ -179,9 +193,55 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     hi = row_hi(md, qrow);
   }
 
-  // Q^T fragments (B operand): lane holds Q[qrow][16*ks + 8*hf .. +7].
-  bf16x8 qf[NKS];
-  {
+  // Q^T fragments (B operand): lane holds Q[qrow][16*ks + 8*hf .. +7]; FP8: lane holds the
+  // codes of Q[qrow][64*ks + 32*hf .. +31].
+  bf16x8 qf[FP8 ? 1 : NKS];
+  i32x8 q8f[FP8 ? NKS8 : 1];
+  float cq = a.c;  // base-2 score scale; FP8: times s_q
+  if constexpr (FP8) {
+    u32x4 xq[NKS8][4];
+    const uint16_t *qp = a.q + ((size_t)bh * N + (q_ok ? qrow : 0)) * D + hf * 32;
+#pragma unroll
+    for (int ks = 0; ks < NKS8; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (q_ok) x = *(const u32x4 *)(qp + ks * 64 + u * 8);
+        xq[ks][u] = x;
+      }
+    // s_q = amax / 448 over the workgroup's rows (rows beyond N hold zeros).
+    float mx = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS8; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mx = fmaxf(mx, fabsf(__uint_as_float(xq[ks][u][e] << 16)));
+          mx = fmaxf(mx, fabsf(__uint_as_float(xq[ks][u][e] & 0xFFFF0000u)));
+        }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    if (lane == 0) qmax[wave] = mx;
+    __syncthreads();
+    float amax = qmax[0];
+#pragma unroll
+    for (int w2 = 1; w2 < 8; ++w2) amax = fmaxf(amax, qmax[w2]);
+    const float sq = amax > 0.f ? amax / 448.0f : 1.0f;
+    // code = E4M3(x / s_q), a correctly rounded division then round-to-nearest-even.
+#pragma unroll
+    for (int ks = 0; ks < NKS8; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const uint32_t w0 = xq[ks][u][2 * h2], w1 = xq[ks][u][2 * h2 + 1];
+          q8f[ks][2 * u + h2] = (int32_t)pack_e4m3x4(
+              __uint_as_float(w0 << 16) / sq, __uint_as_float(w0 & 0xFFFF0000u) / sq,
+              __uint_as_float(w1 << 16) / sq, __uint_as_float(w1 & 0xFFFF0000u) / sq);
+        }
+    cq = a.c * sq;
+  } else {
     const uint16_t *qp = a.q + ((size_t)bh * N + (q_ok ? qrow : 0)) * D + hf * 8;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -209,10 +269,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto kt_of = [&](int t) -> int { return lst ? lst[t] : t; };
 
   const uint16_t *kbase = a.k + (size_t)bh * N * D;
+  const uint8_t *k8base = FP8 ? a.k8 + (size_t)bh * N * D : nullptr;
   const uint16_t *vbase = a.vt + (size_t)bh * D * a.Npad;
-  u32x4 kpre[KLD], vpre[VLD];
+  u32x4 kpre[KLDN], vpre[VLD];
   auto gload_k = [&](int kt) {
     const bool in_range = (kt + 1) * kBc <= N;  // uniform: only the last tile can be ragged
+    if constexpr (FP8) {
+#pragma unroll
+      for (int u = 0; u < KLDN; ++u) {
+        const int c = tid + NT * u, key = c / KCH8, ch = c % KCH8, j = kt * kBc + key;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if ((NK8 % NT == 0 || c < NK8) && (in_range || j < N))
+          x = *(const u32x4 *)(k8base + (size_t)j * D + ch * 16);
+        kpre[u] = x;
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < KLD; ++u) {
       const int c = tid + NT * u, key = c / KCH, ch = c % KCH, j = kt * kBc + key;
@@ -229,6 +301,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
   auto lstore_k = [&](int buf) {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int u = 0; u < KLDN; ++u) {
+        const int c = tid + NT * u, key = c / KCH8, ch = c % KCH8;
+        if (NK8 % NT == 0 || c < NK8)
+          *(u32x4 *)((uint8_t *)sK[buf] + pi_key(key) * KP8 + ch * 16) = kpre[u];
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < KLD; ++u) {
       const int c = tid + NT * u, key = c / KCH, ch = c % KCH;
@@ -243,7 +324,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  const float c = a.c;
   const float slopeL = ALIBI ? a.slopes[h] * 1.4426950408889634f : 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 oacc[NDB];
@@ -258,7 +338,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // fragment of step i + kDepth is read from LDS while step i runs, so LDS latency stays hidden
   // behind the matrix core.
   constexpr int kDepth = 4;
-  auto mphase = [&](int t) {
+  auto mphase_bf16 = [&](int t) {
     constexpr int NPV = 4 * NDB;
     constexpr int NST = NPV + 2 * NKS;
     const uint16_t *vbuf = &sV[(t - 1) & 1][l32 * VP + hf * 8];
@@ -296,6 +376,68 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (i + kDepth < NST) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
+  // The FP8 M-phase: the same P V steps, then 2 * D / 64 score steps (k-step ks, key block blk),
+  // each fed by two 16-byte LDS reads of K8 (bytes 64*ks + 32*hf .. +31 of the lane's key row).
+  // The LDS reads form one stream, kDepth reads ahead of the MFMA that consumes them.
+  auto mphase_fp8 = [&](int t) {
+    constexpr int NPV = 4 * NDB;
+    constexpr int NSS = 2 * NKS8;      // score MFMAs
+    constexpr int NR = NPV + 2 * NSS;  // LDS reads
+    const uint16_t *vbuf = &sV[(t - 1) & 1][l32 * VP + hf * 8];
+    const uint8_t *kbuf = (const uint8_t *)sK[t & 1] + l32 * KP8 + hf * 32;
+    auto frag = [&](int r) -> u32x4 {
+      if (r < NPV) {
+        const int kk = r / NDB, db = r % NDB;
+        return *(const u32x4 *)(vbuf + db * 32 * VP + kk * 16);
+      }
+      const int j = r - NPV, st = j >> 1, half = j & 1, ks = st >> 1, blk = st & 1;
+      return *(const u32x4 *)(kbuf + blk * 32 * KP8 + ks * 64 + half * 16);
+    };
+    u32x4 win[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) win[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const u32x4 cur = win[i % kDepth];
+      if (i + kDepth < NR) win[i % kDepth] = frag(i + kDepth);
+      const int kk = i / NDB, db = i % NDB;
+      oacc[db] = mfma32(__builtin_bit_cast(f16x8, cur), pb[kk], oacc[db]);
+    }
+#pragma unroll
+    for (int st = 0; st < NSS; ++st) {
+      const int r0 = NPV + 2 * st, ks = st >> 1, blk = st & 1;
+      const u32x4 a0 = win[r0 % kDepth];
+      if (r0 + kDepth < NR) win[r0 % kDepth] = frag(r0 + kDepth);
+      const u32x4 a1 = win[(r0 + 1) % kDepth];
+      if (r0 + 1 + kDepth < NR) win[(r0 + 1) % kDepth] = frag(r0 + 1 + kDepth);
+      const i32x8 kf = {(int32_t)a0[0], (int32_t)a0[1], (int32_t)a0[2], (int32_t)a0[3],
+                        (int32_t)a1[0], (int32_t)a1[1], (int32_t)a1[2], (int32_t)a1[3]};
+      s[blk] = mfma32_fp8(kf, q8f[ks], ks == 0 ? f32x16{} : s[blk]);
+    }
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int st = 0; st < NSS; ++st) {
+      const int r0 = NPV + 2 * st;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (r0 + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (r0 + 1 + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  auto mphase = [&](int t) {
+    if constexpr (FP8)
+      mphase_fp8(t);
+    else
+      mphase_bf16(t);
+    // Keep the score MFMAs in this slot: without a use here the compiler sinks the last ones
+    // past the barrier into the (conditional) V-phase that reads them.
+    __asm__ volatile("" ::"v"(s[0]), "v"(s[1]));
+  };
 
   // Zero P and the V buffer read by the first M-phase (its P V step then adds exactly 0).
 #pragma unroll
@@ -309,6 +451,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // V-phase of tile t: score modifications, mask, online softmax, P_t in fp16.
   auto vphase = [&](int kt) {
+    // Base-2 score scale of this tile; FP8: times s_k of the key tile (read-only here, written
+    // by the quantization kernel before this launch: a scalar load).
+    float c = cq;
+    if constexpr (FP8) c = cq * ((const_f32 *)a.sk)[(size_t)bh * a.n_kt + kt];
     // Register r of block blk is key kt*Bc + 32*blk + 16*(r/8) + 8*hf + r%8.
     const int kb = kt * kBc + 8 * hf;
     if constexpr (!POS) {
@@ -451,17 +597,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-template <int D, bool ALIBI, bool SOFTCAP, bool POS>
+template <int D, bool ALIBI, bool SOFTCAP, bool POS, bool FP8 = false>
 hipError_t launch_out(bool out_f32, const FwdArgs &a, dim3 grid, hipStream_t s) {
   if (out_f32)
-    fwd_kernel<D, ALIBI, SOFTCAP, POS, true><<<grid, 512, 0, s>>>(a);
+    fwd_kernel<D, ALIBI, SOFTCAP, POS, true, FP8><<<grid, 512, 0, s>>>(a);
   else
-    fwd_kernel<D, ALIBI, SOFTCAP, POS, false><<<grid, 512, 0, s>>>(a);
+    fwd_kernel<D, ALIBI, SOFTCAP, POS, false, FP8><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdInstance &in, const FwdArgs &a, dim3 grid, hipStream_t s) {
+  if (in.fp8) {
+    if (in.alibi || in.softcap) return hipErrorInvalidValue;
+    if (in.pos_scale) return launch_out<D, false, false, true, true>(in.out_f32, a, grid, s);
+    return launch_out<D, false, false, false, true>(in.out_f32, a, grid, s);
+  }
   if (in.alibi && in.softcap) return launch_out<D, true, true, false>(in.out_f32, a, grid, s);
   if (in.alibi) return launch_out<D, true, false, false>(in.out_f32, a, grid, s);
   if (in.softcap) return launch_out<D, false, true, false>(in.out_f32, a, grid, s);

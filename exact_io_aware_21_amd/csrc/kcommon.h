@@ -1,6 +1,6 @@
-// Device helpers shared by the forward and backward kernels: operand types of the gfx950
-// 32x32x16 MFMAs, the register-layout permutations that let MFMA results feed the next MFMA
-// directly, and lane-pair reductions.
+// Device helpers shared by the kernels: operand types of the gfx950 32x32x16 and 32x32x64
+// MFMAs, FP8 E4M3 packing, the register-layout permutations that let MFMA results feed the
+// next MFMA directly, and lane-pair reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,7 +15,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(4))) const int32_t const_i32;
+typedef __attribute__((address_space(4))) const float const_f32;
 
 constexpr float kLn2 = 0.69314718055994531f;
 // s_getreg operand for HW_ID.SIMD_ID: register 4, bit offset 4, 2 bits.
@@ -63,6 +65,22 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x64 product on FP8 E4M3 operands (cbsz = blgp = 0) with unit block scales (E8M0 code
+// 127 = 2^0).  Lane l holds row (A) or column (B) l % 32 and the 32 consecutive k values
+// 32 * (l / 32) .. +31, one byte each, lowest k in the lowest byte; the result has the layout of
+// the 32x32x16 products.
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Four float32 values -> four E4M3 codes, value i in byte i: round to nearest even, no
+// saturation (past 448 gives the NaN code).
+__device__ __forceinline__ uint32_t pack_e4m3x4(float x0, float x1, float x2, float x3) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false) & 0xFFFFu;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, 0, false) & 0xFFFFu;
+  return lo | (hi << 16);
 }
 
 // bf16 bits -> fp16 bits; exact for |x| in [2^-14, 65504], saturating beyond (NaN stays NaN).

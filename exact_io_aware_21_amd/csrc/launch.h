@@ -24,6 +24,8 @@ struct FwdArgs {
   const int8_t *cls;     // block table (null for the unmasked kind)
   const int32_t *cnt;
   const int32_t *list;
+  const uint8_t *k8;  // FP8 instances: K as E4M3 codes [BH][N][D]
+  const float *sk;    // FP8 instances: K scales [BH][n_kt], one per 64-key tile
 };
 
 // Variant switches that select a kernel instance.
@@ -33,10 +35,9 @@ struct FwdInstance {
   bool softcap;
   bool pos_scale;  // scale > 0 and no score modification: max is taken on raw scores
   bool out_f32;
+  bool fp8;        // scores from E4M3 codes of Q (quantized in the kernel) and K (a.k8, a.sk)
 };
 
-// X [BH][N][d] bf16 -> X^T [BH][d][Npad], keys contiguous, zero beyond N, d rows permuted within
-// 32-blocks (sigma_d); fp16 (saturating) or bf16 values.
 // Backward pass (bwd.hip).
 struct BwdArgs {
   const uint16_t *q, *k, *v, *dout;  // bf16 [BH][N][D]
@@ -78,6 +79,8 @@ hipError_t launch_decode(const DecodeArgs &a, int d, bool out_f32, hipStream_t s
 hipError_t launch_quant_fp8(const uint16_t *x, uint8_t *codes, float *scales, int BH, int N,
                             int d, int rows, hipStream_t stream);
 
+// V [BH][N][d] bf16 -> V^T [BH][d][Npad] fp16 (saturating), keys contiguous, zero beyond N,
+// d rows permuted within 32-blocks (sigma_d).
 hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Npad, int d,
                           hipStream_t stream);
 hipError_t launch_block_table(MaskDesc m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,

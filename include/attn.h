@@ -54,7 +54,8 @@ enum {
   ATTN_MASK_SLIDING_WINDOW = 2,
   ATTN_MASK_DOCUMENT = 3, /* mask kind: bits 0-3 */
   ATTN_MOD_ALIBI = 1u << 4,
-  ATTN_MOD_SOFTCAP = 1u << 5
+  ATTN_MOD_SOFTCAP = 1u << 5,
+  ATTN_PREC_FP8 = 1u << 6 /* attn_fwd only: scores from FP8 E4M3 codes of Q and K, see attn_fwd */
 };
 
 /* return codes */
@@ -94,19 +95,26 @@ typedef struct {
  *   B, H, N : >= 1, N <= 2^24, B*H*ceil(N/Br) < 2^31.
  *   d       : 64 or 128.
  *   scale   : finite (1/sqrt(d) for the standard scaling).
- *   variant : one mask kind, optionally OR-ed with ATTN_MOD_ALIBI and/or ATTN_MOD_SOFTCAP.
+ *   variant : one mask kind, optionally OR-ed with ATTN_MOD_ALIBI and/or ATTN_MOD_SOFTCAP, or
+ *             with ATTN_PREC_FP8 (no score modification; B*H <= 65535).
  *   params  : required (it carries the workspace).
  * A query row with no allowed key (impossible for the masks above with valid arguments) gets
  * O = 0 and L = -inf.
  * Precision: Q K^T is formed from the bf16 inputs with fp32 accumulation; probabilities and V
  * enter the P V product as fp16 (V converted exactly for |v| in [2^-14, 65504]; larger
  * magnitudes saturate to +-65504), accumulated in fp32; l is summed from fp32 probabilities.
+ * With ATTN_PREC_FP8 (page "FlashAttention/es", section "Variantes y sucesores": FP8 with
+ * per-block scaling), Q and K are first block-quantized as attn_quantize_fp8 does, Q with
+ * rows = Br (inside the forward kernel) and K with rows = Bc (into the workspace), and
+ * S = scale * (s_q Q8)(s_k K8)^T is formed from the E4M3 codes with fp32 accumulation; V and
+ * the P V product are as above.  Inputs must be finite.
  */
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
              int d, float scale, uint32_t variant, const attn_params *params, void *stream);
 
 /* Bytes of workspace attn_fwd needs for this shape and variant (0 on invalid arguments).
-   It holds a key-transposed copy of V and the block table. */
+   It holds a key-transposed copy of V, the block table and, with ATTN_PREC_FP8, the E4M3
+   codes of K ([B][H][N][d] bytes) and their scales (fp32 [B][H][ceil(N/Bc)]). */
 size_t attn_workspace_size(int B, int H, int N, int d, uint32_t variant);
 
 /* Tile shape (Br query rows x Bc keys) the forward kernel uses for (d, variant); the block table
@@ -143,7 +151,8 @@ int attn_block_table_host(int B, int H, int N, int d, uint32_t variant, const at
  *   dout    : device, bf16, [B][H][N][d], 16-byte aligned.
  *   dq, dk, dv : device outputs, [B][H][N][d], bf16 or fp32 per params->o_dtype, 16-byte
  *             aligned; every element is written (deterministically: no atomics).
- *   B, H, N, d, scale, variant : as for attn_fwd; additionally B*H <= 65535.
+ *   B, H, N, d, scale, variant : as for attn_fwd; additionally B*H <= 65535 and no
+ *             ATTN_PREC_FP8 (the backward pass is bf16 only).
  *   params  : required; workspace of >= attn_bwd_workspace_size() bytes, 256-byte aligned.
  *             timing_events, if set, bracket the two main backward kernels.
  * Precision: all products are bf16 MFMAs with fp32 accumulation; P (<= 1) and dS are rounded
@@ -170,7 +179,8 @@ size_t attn_bwd_workspace_size(int B, int H, int N, int d, uint32_t variant);
  *   codes  : device, uint8 [B][H][N][d] E4M3, 16-byte aligned.
  *   scales : device, fp32 [B][H][ceil(N / rows)].
  *   B*H <= 65535, 1 <= N <= 2^24, d 64 or 128, rows 1..4096.
- * attn_fwd with ATTN_PREC_FP8 applies it to Q (rows = Br) and K (rows = Bc) in its workspace.
+ * attn_fwd with ATTN_PREC_FP8 applies the same quantization to Q (rows = Br, inside the forward
+ * kernel) and to K (rows = Bc, into its workspace).
  */
 int attn_quantize_fp8(const void *x, uint8_t *codes, float *scales, int B, int H, int N, int d,
                       int rows, void *stream);

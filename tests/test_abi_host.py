@@ -56,6 +56,11 @@ def test_workspace_size():
     assert attn.attn_workspace_size(B, H, N, d, attn.ATTN_MASK_DOCUMENT) == exp_doc
     assert attn.attn_workspace_size(1, 1, 0, 64, 0) == 0
     assert attn.attn_workspace_size(1, 1, 16, 80, 0) == 0
+    # FP8: plus the E4M3 codes of K (B*H*N*d bytes) and one fp32 scale per 64-key tile
+    assert attn.attn_workspace_size(B, H, N, d, attn.ATTN_MASK_CAUSAL | attn.ATTN_PREC_FP8) == \
+        exp + al(B * H * N * d) + al(B * H * 16 * 4)
+    assert attn.attn_workspace_size(B, H, N, d, attn.ATTN_PREC_FP8 | attn.ATTN_MOD_ALIBI) == 0
+    assert attn.attn_tile_shape(128, attn.ATTN_PREC_FP8) == (256, 64)
 
 
 def _call_fwd(q=16, k=16, v=16, o=16, lse=None, B=1, H=1, N=64, d=64, scale=0.125, variant=0,
@@ -88,6 +93,9 @@ def _call_fwd(q=16, k=16, v=16, o=16, lse=None, B=1, H=1, N=64, d=64, scale=0.12
     ({"variant": 1 << 8}, attn.ATTN_ERR_INVALID_ARG),
     ({"params": None}, attn.ATTN_ERR_INVALID_ARG),
     ({"B": 40000, "H": 40000, "N": 1000}, attn.ATTN_ERR_INVALID_ARG),
+    ({"variant": (1 << 6) | (1 << 4)}, attn.ATTN_ERR_INVALID_ARG),  # FP8 with ALiBi
+    ({"variant": (1 << 6) | (1 << 5)}, attn.ATTN_ERR_INVALID_ARG),  # FP8 with soft-capping
+    ({"variant": 1 << 6, "B": 300, "H": 300}, attn.ATTN_ERR_INVALID_ARG),  # FP8, B*H > 65535
 ])
 def test_fwd_rejects_invalid_arguments(kw, code):
     assert _call_fwd(**kw) == code
@@ -200,6 +208,7 @@ def test_bwd_workspace_size():
     assert attn.attn_bwd_workspace_size(B, H, N, d, attn.ATTN_MASK_CAUSAL) == \
         base + al(rows * 16) + al(rows * 4) + al(rows * 16 * 4)
     assert attn.attn_bwd_workspace_size(1, 1, 16, 80, 0) == 0
+    assert attn.attn_bwd_workspace_size(B, H, N, d, attn.ATTN_PREC_FP8) == 0  # forward only
 
 
 def _call_bwd(ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, variant=0, params="default"):
@@ -225,6 +234,7 @@ def _call_bwd(ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, variant=0, params="d
     ({"B": 300, "H": 300}, attn.ATTN_ERR_INVALID_ARG),
     ({"scale": float("nan")}, attn.ATTN_ERR_INVALID_ARG),
     ({"params": None}, attn.ATTN_ERR_INVALID_ARG),
+    ({"variant": 1 << 6}, attn.ATTN_ERR_INVALID_ARG),  # FP8 is forward only
 ])
 def test_bwd_rejects_invalid_arguments(kw, code):
     assert _call_bwd(**kw) == code
