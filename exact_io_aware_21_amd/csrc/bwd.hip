@@ -36,9 +36,6 @@ namespace attn {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-// Word 3 of a raw (unformatted, stride 0) buffer resource on gfx9-family parts: 32-bit data
-// format, no swizzle.  Loads past the resource's byte size return zero.
-constexpr int kBufferWord3 = 0x00020000;
 
 // D_i = sum_c dO_ic O_ic (fp32).  One group of D/8 lanes per row, 16-byte loads.
 template <int D>

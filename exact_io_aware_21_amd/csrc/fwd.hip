@@ -268,61 +268,52 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   auto kt_of = [&](int t) -> int { return lst ? lst[t] : t; };
 
-  const uint16_t *kbase = a.k + (size_t)bh * N * D;
-  const uint8_t *k8base = FP8 ? a.k8 + (size_t)bh * N * D : nullptr;
+  // Tile staging.  Per tile pair each thread moves NI 16-byte chunks: items 0 .. KLDN-1 are
+  // chunks of the next K tile, items KLDN .. NI-1 chunks of the current V^T tile.  Loads are
+  // buffer loads at lane-constant offsets from a per-tile base (K rows past N read as zero), so
+  // an item is one instruction and no branch.  The loads of an iteration are spread over its
+  // first slot and the LDS stores over its second, between the other work of the wave, rather
+  // than issued by every wave in one burst at a slot boundary.
+  constexpr int KROW = FP8 ? D : 2 * D;  // bytes per K row in memory
+  constexpr int KCHR = KROW / 16;        // 16-byte chunks per K row
+  constexpr int NKC = kBc * KCHR;        // chunks per K tile
+  constexpr int KPB = FP8 ? KP8 : 2 * KP;  // bytes per K row in LDS
+  constexpr int NI = KLDN + VLD;
+  static_assert(KLDN * NT >= NKC && VLD * NT == D * VCH, "staging must cover both tiles");
+  const char *kbytes = FP8 ? (const char *)(a.k8 + (size_t)bh * N * D)
+                           : (const char *)(a.k + (size_t)bh * N * D);
   const uint16_t *vbase = a.vt + (size_t)bh * D * a.Npad;
-  u32x4 kpre[KLDN], vpre[VLD];
-  auto gload_k = [&](int kt) {
-    const bool in_range = (kt + 1) * kBc <= N;  // uniform: only the last tile can be ragged
-    if constexpr (FP8) {
-#pragma unroll
-      for (int u = 0; u < KLDN; ++u) {
-        const int c = tid + NT * u, key = c / KCH8, ch = c % KCH8, j = kt * kBc + key;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if ((NK8 % NT == 0 || c < NK8) && (in_range || j < N))
-          x = *(const u32x4 *)(k8base + (size_t)j * D + ch * 16);
-        kpre[u] = x;
-      }
-      return;
-    }
-#pragma unroll
-    for (int u = 0; u < KLD; ++u) {
-      const int c = tid + NT * u, key = c / KCH, ch = c % KCH, j = kt * kBc + key;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (in_range || j < N) x = *(const u32x4 *)(kbase + (size_t)j * D + ch * 8);
-      kpre[u] = x;
-    }
-  };
-  auto gload_v = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < VLD; ++u) {
-      const int c = tid + NT * u, row = c / VCH, ch = c % VCH;
-      vpre[u] = *(const u32x4 *)(vbase + (size_t)row * a.Npad + (size_t)kt * kBc + ch * 8);
+  // Lane-constant byte offsets of chunk u = 0: item u adds u * (NT / KCHR) rows (K) or
+  // u * (NT / VCH) rows (V^T) to both, a scalar or immediate offset.  For FP8 with d = 64 the
+  // 512 threads cover the 256 chunks of a K tile twice (identical writes).
+  const int c0 = tid % NKC;
+  const int kgo = (c0 / KCHR) * KROW + (c0 % KCHR) * 16;
+  const int klo = pi_key(c0 / KCHR) * KPB + (c0 % KCHR) * 16;
+  const int vgo = (tid / VCH) * a.Npad * 2 + (tid % VCH) * 16;  // < 2^31: tid / VCH < 64
+  const int vlo = (tid / VCH) * VP * 2 + (tid % VCH) * 16;
+  constexpr int KRU = NT / KCHR;  // K rows per item
+  constexpr int VRU = NT / VCH;   // V^T rows per item
+  static_assert(KLDN == 1 || NKC % NT == 0, "K items must tile the K tile");
+  u32x4 stg[NI];
+  auto load_item = [&](int j, int kt_k, int kt_v) {
+    if (j < KLDN) {
+      const int rows = min(kBc, N - kt_k * kBc);
+      stg[j] = buffer_load16(kbytes + (size_t)kt_k * kBc * KROW, (uint32_t)(rows * KROW), kgo,
+                             j * KRU * KROW);
+    } else {
+      const size_t left = ((size_t)D * a.Npad - (size_t)kt_v * kBc) * 2;
+      stg[j] = buffer_load16(vbase + (size_t)kt_v * kBc,
+                             (uint32_t)(left < 0xFFFFFFFFull ? left : 0xFFFFFFFFull), vgo,
+                             (int)((uint32_t)((j - KLDN) * VRU) * (uint32_t)a.Npad * 2u));
     }
   };
-  auto lstore_k = [&](int buf) {
-    if constexpr (FP8) {
-#pragma unroll
-      for (int u = 0; u < KLDN; ++u) {
-        const int c = tid + NT * u, key = c / KCH8, ch = c % KCH8;
-        if (NK8 % NT == 0 || c < NK8)
-          *(u32x4 *)((uint8_t *)sK[buf] + pi_key(key) * KP8 + ch * 16) = kpre[u];
-      }
-      return;
-    }
-#pragma unroll
-    for (int u = 0; u < KLD; ++u) {
-      const int c = tid + NT * u, key = c / KCH, ch = c % KCH;
-      *(u32x4 *)&sK[buf][pi_key(key) * KP + ch * 8] = kpre[u];
-    }
+  auto store_item = [&](int j, int kb, int vb) {
+    if (j < KLDN)
+      *(u32x4 *)((char *)sK[kb] + klo + j * KRU * KPB) = stg[j];
+    else
+      *(u32x4 *)((char *)sV[vb] + vlo + (j - KLDN) * VRU * VP * 2) = stg[j];
   };
-  auto lstore_v = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < VLD; ++u) {
-      const int c = tid + NT * u, row = c / VCH, ch = c % VCH;
-      *(u32x4 *)&sV[buf][row * VP + ch * 8] = vpre[u];
-    }
-  };
+
 
   const float slopeL = ALIBI ? a.slopes[h] * 1.4426950408889634f : 0.f;
   float m_run = -INFINITY, l_run = 0.f;
@@ -337,8 +328,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // that consecutive MFMAs write different accumulators.  The A
   // fragment of step i + kDepth is read from LDS while step i runs, so LDS latency stays hidden
   // behind the matrix core.
+  // Staging item j (`item(j)`: the LDS store of chunk j, then the buffer load of chunk j of the
+  // next tile pair into the same registers) goes after MFMA step 1 + j * NST / NI.
   constexpr int kDepth = 4;
-  auto mphase_bf16 = [&](int t) {
+  auto mphase_bf16 = [&](int t, auto item) {
     constexpr int NPV = 4 * NDB;
     constexpr int NST = NPV + 2 * NKS;
     const uint16_t *vbuf = &sV[(t - 1) & 1][l32 * VP + hf * 8];
@@ -366,22 +359,33 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int j = i - NPV, ks = j >> 1, blk = j & 1;
         s[blk] = mfma32(__builtin_bit_cast(bf16x8, cur), qf[ks], ks == 0 ? f32x16{} : s[blk]);
       }
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        if (i == 1 + j * NST / NI) item(j);
     }
-    // Pin that order for the scheduler: kDepth LDS reads, then MFMA / LDS read pairs.
+    // Pin that order for the scheduler: kDepth LDS reads, then MFMA / LDS read pairs, with the
+    // staging items in between.
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        if (i == 1 + j * NST / NI) {
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
       if (i + kDepth < NST) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
   // The FP8 M-phase: the same P V steps, then 2 * D / 64 score steps (k-step ks, key block blk),
   // each fed by two 16-byte LDS reads of K8 (bytes 64*ks + 32*hf .. +31 of the lane's key row).
   // The LDS reads form one stream, kDepth reads ahead of the MFMA that consumes them.
-  auto mphase_fp8 = [&](int t) {
+  auto mphase_fp8 = [&](int t, auto item) {
     constexpr int NPV = 4 * NDB;
     constexpr int NSS = 2 * NKS8;      // score MFMAs
+    constexpr int NST = NPV + NSS;     // MFMAs
     constexpr int NR = NPV + 2 * NSS;  // LDS reads
     const uint16_t *vbuf = &sV[(t - 1) & 1][l32 * VP + hf * 8];
     const uint8_t *kbuf = (const uint8_t *)sK[t & 1] + l32 * KP8 + hf * 32;
@@ -402,6 +406,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (i + kDepth < NR) win[i % kDepth] = frag(i + kDepth);
       const int kk = i / NDB, db = i % NDB;
       oacc[db] = mfma32(__builtin_bit_cast(f16x8, cur), pb[kk], oacc[db]);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        if (i == 1 + j * NST / NI) item(j);
     }
 #pragma unroll
     for (int st = 0; st < NSS; ++st) {
@@ -413,30 +420,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const i32x8 kf = {(int32_t)a0[0], (int32_t)a0[1], (int32_t)a0[2], (int32_t)a0[3],
                         (int32_t)a1[0], (int32_t)a1[1], (int32_t)a1[2], (int32_t)a1[3]};
       s[blk] = mfma32_fp8(kf, q8f[ks], ks == 0 ? f32x16{} : s[blk]);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        if (NPV + st == 1 + j * NST / NI) item(j);
     }
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        if (i == 1 + j * NST / NI) {
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
       if (i + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
     for (int st = 0; st < NSS; ++st) {
       const int r0 = NPV + 2 * st;
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        if (NPV + st == 1 + j * NST / NI) {
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
       if (r0 + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       if (r0 + 1 + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  auto mphase = [&](int t) {
+  auto mphase = [&](int t, auto item) {
     if constexpr (FP8)
-      mphase_fp8(t);
+      mphase_fp8(t, item);
     else
-      mphase_bf16(t);
+      mphase_bf16(t, item);
     // Keep the score MFMAs in this slot: without a use here the compiler sinks the last ones
     // past the barrier into the (conditional) V-phase that reads them.
-    __asm__ volatile("" ::"v"(s[0]), "v"(s[1]));
+    const f32x16 s0 = s[0], s1 = s[1];
+    __asm__ volatile("" ::"v"(s0), "v"(s1));
   };
 
   // Zero P and the V buffer read by the first M-phase (its P V step then adds exactly 0).
@@ -444,8 +467,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int g = 0; g < 4; ++g) pb[g] = f16x8{};
   for (int i = tid; i < D * VP / 8; i += NT) *(u32x4 *)&sV[1][i * 8] = u32x4{0u, 0u, 0u, 0u};
   if (T > 0) {
-    gload_k(kt_of(0));
-    lstore_k(0);
+#pragma unroll
+    for (int j = 0; j < KLDN; ++j) load_item(j, kt_of(0), 0);
+#pragma unroll
+    for (int j = 0; j < KLDN; ++j) store_item(j, 0, 0);
   }
   __syncthreads();
 
@@ -526,46 +551,47 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
   };
-  // kt of tiles k - 1, k, k + 1 are kept in scalars; tile k + 2's is read one iteration ahead.
+  // kt of tiles k - 1 .. k + 2 are kept in scalars; tile k + 3's is read one iteration ahead.
+  // Past the last tile they are 0 (a valid tile: its data is staged but never used).
   int kt_prev = 0, kt_cur = T > 0 ? kt_of(0) : 0, kt_next = T > 1 ? kt_of(1) : 0;
-  auto slot_a_loads = [&](int k) {
-    if (k + 1 < T) gload_k(kt_next);
-    if (k < T) gload_v(kt_cur);
-  };
-  auto slot_b_stores = [&](int k) {
-    if (k + 1 < T) lstore_k((k + 1) & 1);
-    if (k < T) lstore_v(k & 1);
-  };
+  int kt_n2 = T > 2 ? kt_of(2) : 0;
   auto advance = [&](int k) {
-    const int kt_nn = k + 2 < T ? kt_of(k + 2) : 0;
+    const int kt_n3 = k + 3 < T ? kt_of(k + 3) : 0;
     kt_prev = kt_cur;
     kt_cur = kt_next;
-    kt_next = kt_nn;
+    kt_next = kt_n2;
+    kt_n2 = kt_n3;
   };
+  // The chunks of K_1 and V_0, written in iteration 0.
+#pragma unroll
+  for (int j = 0; j < NI; ++j) load_item(j, kt_next, kt_cur);
 
   // Two slots per iteration k.  Slot A: group 0 runs M-phase k, group 1 V-phase k-1.  Slot B:
-  // group 0 runs V-phase k, group 1 M-phase k.  K_k and V_{k-1} are read in both slots; K_{k+1}
-  // and V_k, fetched at the start of slot A, are written to the idle buffers at the end of slot B.
-  // Both groups execute the same 2T + 2 barriers.  In M-phase 0, P = 0 against a zeroed V
-  // buffer adds nothing; in M-phase T the score product reads a stale (finite, in-bounds) K
-  // buffer and its result is never used.
+  // group 0 runs V-phase k, group 1 M-phase k.  K_k and V_{k-1} are read in both slots.  Each
+  // wave stages its chunks inside its own M-phase, between the MFMAs: it writes the chunks of
+  // K_{k+1} and V_k (fetched one iteration earlier) to the idle buffers, which no step of
+  // iteration k reads, and fetches those of K_{k+2} and V_{k+1}.  Both groups execute the same
+  // 2T + 2 barriers.  In M-phase 0, P = 0 against a zeroed V buffer adds nothing; in M-phase T
+  // the score product reads a stale K buffer and its result is never used.
+  auto stage = [&](int k) {
+    return [&, k](int j) {
+      store_item(j, (k + 1) & 1, k & 1);
+      load_item(j, kt_n2, kt_next);
+    };
+  };
   if (grp == 0) {
     for (int k = 0; k <= T; ++k) {
-      slot_a_loads(k);
-      mphase(k);
+      mphase(k, stage(k));
       __syncthreads();
       if (k < T) vphase(kt_cur);
-      slot_b_stores(k);
       advance(k);
       __syncthreads();
     }
   } else {
     for (int k = 0; k <= T; ++k) {
-      slot_a_loads(k);
       if (k >= 1) vphase(kt_prev);
       __syncthreads();
-      mphase(k);
-      slot_b_stores(k);
+      mphase(k, stage(k));
       advance(k);
       __syncthreads();
     }

@@ -23,6 +23,15 @@ constexpr float kLn2 = 0.69314718055994531f;
 // s_getreg operand for HW_ID.SIMD_ID: register 4, bit offset 4, 2 bits.
 constexpr int kHwRegSimdId = (4) | (4 << 6) | ((2 - 1) << 11);
 constexpr float kTau = 8.0f;
+// Word 3 of a raw (unformatted, stride 0) buffer resource on gfx9-family parts: 32-bit data
+// format, no swizzle.  Loads past the resource's byte size return zero.
+constexpr int kBufferWord3 = 0x00020000;
+
+// A compile-time integer passed to generic lambdas (scheduling masks must be constants).
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 
 // Key permutation inside a 64-key tile: swap bits 2 and 3 (an involution).
 __device__ __forceinline__ int pi_key(int x) {
@@ -81,6 +90,15 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float x0, float x1, float x2, fl
   const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false) & 0xFFFFu;
   const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, 0, false) & 0xFFFFu;
   return lo | (hi << 16);
+}
+
+// 16 bytes at byte offset voff + soff (voff per lane, soff wave-uniform) of a buffer of `bytes`
+// bytes at base (zero past its end).  A free function: buffer built-ins inside a kernel's
+// lambdas break its host-side stub.
+__device__ __forceinline__ u32x4 buffer_load16(const void *base, uint32_t bytes, int voff,
+                                               int soff) {
+  const auto r = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)bytes, kBufferWord3);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
 // bf16 bits -> fp16 bits; exact for |x| in [2^-14, 65504], saturating beyond (NaN stays NaN).
