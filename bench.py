@@ -48,9 +48,9 @@ PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
 MAX_SCLK_MHZ = 2400.0      # MI355X peak engine clock, the one the MFMA peak is quoted at
 METRIC = "attention fwd TFLOP/s (unmasked FLOPs) and % of MFMA peak, 1 MI355X"
 DEFAULT_WORKLOAD = "causal_h32_n16384_d128"
-KERNEL_SOURCES = ["exact_io_aware_21_amd/csrc/fwd.hip", "exact_io_aware_21_amd/csrc/kcommon.h",
-                  "exact_io_aware_21_amd/csrc/tiles.h",
-                  "exact_io_aware_21_amd/csrc/launch.h"]
+KERNEL_SOURCES = ["exact_io_aware_21_amd/csrc/fwd.hip", "exact_io_aware_21_amd/csrc/fwd_kernel.h",
+                  "exact_io_aware_21_amd/csrc/kcommon.h", "exact_io_aware_21_amd/csrc/tiles.h",
+                  "exact_io_aware_21_amd/csrc/launch.h", "exact_io_aware_21_amd/csrc/hipdefs.h"]
 
 
 def allowed_pairs(w, doc_offsets=None):

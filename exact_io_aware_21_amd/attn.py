@@ -26,13 +26,17 @@ ATTN_ERR_INVALID_ARG = -1
 ATTN_ERR_UNSUPPORTED_DEVICE = -2
 ATTN_ERR_LAUNCH = -3
 ATTN_ERR_WORKSPACE = -4
+ATTN_ERR_COMPILE = -5
+ATTN_MODF_SCORE = 1
+ATTN_MODF_MASK = 2
 
 MASK_BITS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
              "window": ATTN_MASK_SLIDING_WINDOW, "document": ATTN_MASK_DOCUMENT}
 
 EXPORTS = ("attn_fwd", "attn_workspace_size", "attn_tile_shape", "attn_block_table",
            "attn_block_table_host", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
-           "attn_decode_workspace_size", "attn_quantize_fp8", "attn_strerror",
+           "attn_decode_workspace_size", "attn_quantize_fp8", "attn_mod_create",
+           "attn_mod_destroy", "attn_mod_workspace_size", "attn_fwd_mod", "attn_strerror",
            "attn_last_error")
 
 
@@ -84,6 +88,15 @@ def lib():
         L.attn_decode_workspace_size.restype = ctypes.c_size_t
         L.attn_quantize_fp8.argtypes = [c_vp, c_vp, c_vp] + [c_int] * 5 + [c_vp]
         L.attn_quantize_fp8.restype = c_int
+        L.attn_mod_create.argtypes = [ctypes.c_char_p, c_u32, c_int,
+                                       ctypes.POINTER(c_vp), c_vp, ctypes.c_size_t]
+        L.attn_mod_create.restype = c_int
+        L.attn_mod_destroy.argtypes = [c_vp]
+        L.attn_mod_destroy.restype = None
+        L.attn_mod_workspace_size.argtypes = [c_vp, c_int, c_int, c_int]
+        L.attn_mod_workspace_size.restype = ctypes.c_size_t
+        L.attn_fwd_mod.argtypes = [c_vp] * 6 + [c_int] * 3 + [c_f, c_vp, P, c_vp]
+        L.attn_fwd_mod.restype = c_int
         L.attn_strerror.argtypes = [c_int]
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_last_error.argtypes = []
@@ -335,3 +348,74 @@ def attn_block_table_host(B, H, N, d, variant, window=0, doc_offsets=None):
     _check(lib().attn_block_table_host(B, H, N, d, variant, ctypes.byref(p), cls.ctypes.data,
                                        cnt.ctypes.data, lst.ctypes.data))
     return cls, cnt, lst
+
+
+class AttnMod:
+    """A runtime-compiled score / mask modification (attn_mod_create).  `source` is HIP C++
+    defining attn_score_mod and/or attn_mask_mod (see include/attn.h); `flags` names which.
+    Compilation needs no GPU.  The compiler's messages are in `.log`."""
+
+    def __init__(self, source: str, flags: int, d: int):
+        self._h = None
+        buf = ctypes.create_string_buffer(1 << 16)
+        h = ctypes.c_void_p()
+        rc = lib().attn_mod_create(source.encode(), flags, d, ctypes.byref(h), buf, len(buf))
+        self.log = buf.value.decode(errors="replace")
+        if rc != ATTN_OK:
+            L = lib()
+            raise AttnError(rc, f"{L.attn_strerror(rc).decode()}: {self.log or L.attn_last_error().decode()}")
+        self._h, self.flags, self.d = h, flags, d
+
+    def close(self):
+        if self._h is not None:
+            lib().attn_mod_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self, B: int, H: int, N: int) -> int:
+        return int(lib().attn_mod_workspace_size(self._h, B, H, N))
+
+    def alloc_workspace(self, B, H, N, device="cuda"):
+        import torch
+        n = self.workspace_size(B, H, N)
+        if n == 0:
+            raise AttnError(ATTN_ERR_INVALID_ARG, "invalid shape for attn_mod_workspace_size")
+        return torch.empty(n, dtype=torch.uint8, device=device)
+
+    def fwd(self, q, k, v, o, lse, scale, mod_params=None, workspace=None, stream=None,
+            timing_events=None):
+        """attn_fwd_mod on torch tensors: q, k, v bf16 [B,H,N,d]; o bf16 or fp32; lse fp32
+        [B,H,N] or None; mod_params a device fp32 tensor or None."""
+        import torch
+        B, H, N, d = q.shape
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != (B, H, N, d):
+                raise ValueError(f"{name} must be a contiguous bf16 [B,H,N,d] tensor")
+        if o.dtype not in (torch.bfloat16, torch.float32) or not o.is_contiguous() \
+                or tuple(o.shape) != (B, H, N, d):
+            raise ValueError("o must be a contiguous bf16/fp32 [B,H,N,d] tensor")
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                                or tuple(lse.shape) != (B, H, N)):
+            raise ValueError("lse must be a contiguous fp32 [B,H,N] tensor")
+        if mod_params is not None and (mod_params.dtype != torch.float32
+                                       or not mod_params.is_contiguous()):
+            raise ValueError("mod_params must be a contiguous fp32 tensor")
+        if workspace is None:
+            workspace = self.alloc_workspace(B, H, N, q.device)
+        p = make_params(o_dtype=ATTN_O_F32 if o.dtype == torch.float32 else ATTN_O_BF16,
+                        workspace=workspace)
+        ev = None
+        if timing_events is not None:
+            if not (timing_events[0].cuda_event and timing_events[1].cuda_event):
+                raise ValueError("timing events must have been recorded once before use")
+            ev = (ctypes.c_void_p * 2)(timing_events[0].cuda_event, timing_events[1].cuda_event)
+            p.timing_events = ctypes.cast(ev, ctypes.c_void_p)
+        _check(lib().attn_fwd_mod(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N,
+                                  float(scale), _ptr(mod_params), ctypes.byref(p),
+                                  _stream(stream)))
+        return o, lse

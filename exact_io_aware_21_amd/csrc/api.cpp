@@ -3,12 +3,16 @@
 #include "attn.h"
 
 #include <hip/hip_runtime.h>
+#include <hip/hiprtc.h>
 
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
 
 #include "launch.h"
 
@@ -219,6 +223,82 @@ attn::MaskDesc mask_desc(const Shape &s, const attn_params *p) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// ---------------------------------------------------------------------------------------------
+// Runtime-compiled score / mask modifications (attn_mod_*).  The kernel headers are embedded in
+// the library (rtc_sources.s); hipRTC compiles them with the user's source into a gfx950 code
+// object, which each device loads on first use.
+extern "C" const char attn_rtc_hipdefs_h[], attn_rtc_kcommon_h[], attn_rtc_tiles_h[],
+    attn_rtc_launch_h[], attn_rtc_fwd_kernel_h[];
+
+struct ModLayout {
+  size_t vt, cls, cnt, list, total;
+};
+
+ModLayout mod_layout(const Shape &s, bool mask) {
+  ModLayout w{};
+  size_t off = 0;
+  w.vt = off;
+  off = align256(off + (size_t)s.B * s.H * s.d * s.Npad * 2);
+  if (mask) {
+    const size_t rows = (size_t)s.B * s.n_qt;
+    w.cls = off;
+    off = align256(off + rows * s.n_kt);
+    w.cnt = off;
+    off = align256(off + rows * 4);
+    w.list = off;
+    off = align256(off + rows * s.n_kt * 4);
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+struct attn_mod_s {
+  std::string code;  // gfx950 code object
+  uint32_t flags = 0;
+  int d = 0;
+  std::mutex mu;
+  hipModule_t module[kMaxDevices] = {};
+  hipFunction_t fwd[kMaxDevices][2] = {};  // bf16 O, fp32 O
+  hipFunction_t cls[kMaxDevices] = {}, list[kMaxDevices] = {};
+};
+
+namespace {
+
+// The code object of m loaded on device dev (once), its kernels in m's per-device tables.
+int mod_load(attn_mod *m, int dev) {
+  std::lock_guard<std::mutex> g(m->mu);
+  if (m->module[dev]) return ATTN_OK;
+  hipModule_t mod = nullptr;
+  if (hipModuleLoadData(&mod, m->code.data()) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ATTN_ERR_LAUNCH, "loading the compiled modification on device %d failed", dev);
+  }
+  hipFunction_t f16 = nullptr, f32 = nullptr, fc = nullptr, fl = nullptr;
+  bool ok = hipModuleGetFunction(&f16, mod, "attn_mod_fwd_bf16") == hipSuccess &&
+            hipModuleGetFunction(&f32, mod, "attn_mod_fwd_f32") == hipSuccess;
+  if (ok && (m->flags & ATTN_MODF_MASK))
+    ok = hipModuleGetFunction(&fc, mod, "attn_mod_class") == hipSuccess &&
+         hipModuleGetFunction(&fl, mod, "attn_mod_list") == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    (void)hipModuleUnload(mod);
+    return fail(ATTN_ERR_LAUNCH, "compiled modification lacks its kernels");
+  }
+  m->fwd[dev][0] = f16;
+  m->fwd[dev][1] = f32;
+  m->cls[dev] = fc;
+  m->list[dev] = fl;
+  m->module[dev] = mod;
+  return ATTN_OK;
+}
+
+void copy_log(const char *text, char *log, size_t log_size) {
+  if (!log || log_size == 0) return;
+  std::snprintf(log, log_size, "%s", text ? text : "");
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,6 +310,7 @@ const char *attn_strerror(int code) {
     case ATTN_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case ATTN_ERR_COMPILE: return "runtime compilation of the modification failed";
     default: return "unknown error code";
   }
 }
@@ -541,6 +622,182 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
     return fail(ATTN_ERR_LAUNCH, "timing event record failed");
   if (attn::launch_decode(a, d, params->o_dtype == ATTN_O_F32, st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "decode kernel launch failed");
+  if (ev && hipEventRecord((hipEvent_t)ev[1], st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "timing event record failed");
+  return ATTN_OK;
+}
+
+int attn_mod_create(const char *source, uint32_t flags, int d, attn_mod **out, char *log,
+                    size_t log_size) {
+  copy_log("", log, log_size);
+  if (!out) return fail(ATTN_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!source) return fail(ATTN_ERR_INVALID_ARG, "source is NULL");
+  if (flags == 0 || (flags & ~(uint32_t)(ATTN_MODF_SCORE | ATTN_MODF_MASK)))
+    return fail(ATTN_ERR_INVALID_ARG, "flags must be a non-empty set of ATTN_MODF_SCORE, ATTN_MODF_MASK");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_INVALID_ARG, "d must be 64 or 128");
+  std::string prog = "#include \"fwd_kernel.h\"\n#line 1 \"attn_mod_source\"\n";
+  prog += source;
+  char tail[1024];
+  std::snprintf(tail, sizeof tail,
+                "\n#line 1 \"attn_mod_kernels\"\n"
+                "extern \"C\" __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))"
+                " void attn_mod_fwd_bf16(attn::FwdArgs a) {"
+                " attn::fwd_body<%d, false, false, false, false, false, %u>(a); }\n"
+                "extern \"C\" __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))"
+                " void attn_mod_fwd_f32(attn::FwdArgs a) {"
+                " attn::fwd_body<%d, false, false, false, true, false, %u>(a); }\n",
+                d, flags, d, flags);
+  prog += tail;
+  if (flags & ATTN_MODF_MASK)
+    prog +=
+        "extern \"C\" __global__ __launch_bounds__(256) void attn_mod_class(attn::ModTableArgs t) {"
+        " attn::mod_class_body(t); }\n"
+        "extern \"C\" __global__ __launch_bounds__(256) void attn_mod_list(attn::ModTableArgs t) {"
+        " attn::mod_list_body(t); }\n";
+  const char *hdrs[] = {attn_rtc_hipdefs_h, attn_rtc_kcommon_h, attn_rtc_tiles_h, attn_rtc_launch_h,
+                        attn_rtc_fwd_kernel_h};
+  const char *names[] = {"hipdefs.h", "kcommon.h", "tiles.h", "launch.h", "fwd_kernel.h"};
+  hiprtcProgram p;
+  if (hiprtcCreateProgram(&p, prog.c_str(), "attn_mod.hip", 5, hdrs, names) != HIPRTC_SUCCESS)
+    return fail(ATTN_ERR_COMPILE, "hiprtcCreateProgram failed");
+  // Packed fp32 VALU instructions are disabled, as for the library's own kernels.
+  const char *opts[] = {"--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+                        "-Xclang", "-packed-fp32-ops"};
+  const hiprtcResult rc = hiprtcCompileProgram(p, 7, opts);
+  size_t n = 0;
+  std::vector<char> text(1, 0);
+  if (hiprtcGetProgramLogSize(p, &n) == HIPRTC_SUCCESS && n > 0) {
+    text.assign(n + 1, 0);
+    (void)hiprtcGetProgramLog(p, text.data());
+  }
+  copy_log(text.data(), log, log_size);
+  if (rc != HIPRTC_SUCCESS) {
+    (void)hiprtcDestroyProgram(&p);
+    return fail(ATTN_ERR_COMPILE, "compilation failed: %.200s", text.data());
+  }
+  size_t cs = 0;
+  std::string code;
+  if (hiprtcGetCodeSize(p, &cs) == HIPRTC_SUCCESS && cs > 0) {
+    code.resize(cs);
+    if (hiprtcGetCode(p, &code[0]) != HIPRTC_SUCCESS) code.clear();
+  }
+  (void)hiprtcDestroyProgram(&p);
+  if (code.empty()) return fail(ATTN_ERR_COMPILE, "no code object produced");
+  attn_mod *m = new attn_mod;
+  m->code = std::move(code);
+  m->flags = flags;
+  m->d = d;
+  *out = m;
+  return ATTN_OK;
+}
+
+void attn_mod_destroy(attn_mod *m) {
+  if (!m) return;
+  int cur = -1;
+  const bool have = hipGetDevice(&cur) == hipSuccess;
+  for (int dev = 0; dev < kMaxDevices; ++dev) {
+    if (!m->module[dev]) continue;
+    if (hipSetDevice(dev) == hipSuccess) (void)hipModuleUnload(m->module[dev]);
+  }
+  if (have) (void)hipSetDevice(cur);
+  (void)hipGetLastError();
+  delete m;
+}
+
+size_t attn_mod_workspace_size(const attn_mod *m, int B, int H, int N) {
+  if (!m) return 0;
+  Shape s;
+  if (check_shape(B, H, N, m->d, ATTN_MASK_NONE, s) != ATTN_OK) return 0;
+  if ((long long)B * s.n_qt > 65535 && (m->flags & ATTN_MODF_MASK)) return 0;
+  return mod_layout(s, (m->flags & ATTN_MODF_MASK) != 0).total;
+}
+
+int attn_fwd_mod(const attn_mod *mc, const void *q, const void *k, const void *v, void *o,
+                 float *lse, int B, int H, int N, float scale, const float *mod_params,
+                 const attn_params *params, void *stream) {
+  attn_mod *m = const_cast<attn_mod *>(mc);
+  if (!m) return fail(ATTN_ERR_INVALID_ARG, "mod is NULL");
+  const int d = m->d;
+  Shape s;
+  int rc = check_shape(B, H, N, d, ATTN_MASK_NONE, s);
+  if (rc) return rc;
+  const bool mask = (m->flags & ATTN_MODF_MASK) != 0;
+  if (mask && (long long)B * s.n_qt > 65535)
+    return fail(ATTN_ERR_INVALID_ARG, "B*ceil(N/Br) must be <= 65535 with a mask modification");
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (lse && ((uintptr_t)lse & 3u)) return fail(ATTN_ERR_INVALID_ARG, "lse misaligned");
+  if ((uintptr_t)mod_params & 3u) return fail(ATTN_ERR_INVALID_ARG, "mod_params misaligned");
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+  if (!params) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (params->o_dtype != ATTN_O_BF16 && params->o_dtype != ATTN_O_F32)
+    return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_O_BF16 or ATTN_O_F32");
+  const ModLayout wl = mod_layout(s, mask);
+  if (!params->workspace || ((uintptr_t)params->workspace & 255u))
+    return fail(ATTN_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (params->workspace_bytes < wl.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", params->workspace_bytes,
+                wl.total);
+  if ((rc = check_device())) return rc;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device index out of range");
+  if ((rc = mod_load(m, dev))) return rc;
+
+  const hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)params->workspace;
+  uint16_t *vt = (uint16_t *)(ws + wl.vt);
+  if (attn::launch_vt_pack((const uint16_t *)v, vt, B * H, N, s.Npad, d, st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "V transpose kernel launch failed");
+  attn::FwdArgs a{};
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.vt = vt;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.Npad = s.Npad;
+  a.n_qt = s.n_qt;
+  a.n_kt = s.n_kt;
+  a.c = scale * 1.4426950408889634f;
+  a.scale = scale;
+  a.mod_params = mod_params;
+  a.kind = ATTN_MASK_NONE;
+  if (mask) {
+    attn::ModTableArgs t{};
+    t.N = N;
+    t.n_qt = s.n_qt;
+    t.n_kt = s.n_kt;
+    t.params = mod_params;
+    t.cls = (int8_t *)(ws + wl.cls);
+    t.cnt = (int32_t *)(ws + wl.cnt);
+    t.list = (int32_t *)(ws + wl.list);
+    void *targs[] = {&t};
+    if (hipModuleLaunchKernel(m->cls[dev], (unsigned)s.n_kt, (unsigned)(B * s.n_qt), 1, 256, 1,
+                              1, 0, st, targs, nullptr) != hipSuccess ||
+        hipModuleLaunchKernel(m->list[dev], (unsigned)(B * s.n_qt), 1, 1, 256, 1, 1, 0, st, targs,
+                              nullptr) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(ATTN_ERR_LAUNCH, "mask table kernel launch failed");
+    }
+    a.cls = t.cls;
+    a.cnt = t.cnt;
+    a.list = t.list;
+  }
+  void *const *ev = params->timing_events;
+  if (ev && hipEventRecord((hipEvent_t)ev[0], st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "timing event record failed");
+  void *fargs[] = {&a};
+  if (hipModuleLaunchKernel(m->fwd[dev][params->o_dtype == ATTN_O_F32 ? 1 : 0],
+                            (unsigned)(s.n_qt * B * H), 1, 1, 512, 1, 1, 0, st, fargs,
+                            nullptr) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ATTN_ERR_LAUNCH, "forward kernel launch failed");
+  }
   if (ev && hipEventRecord((hipEvent_t)ev[1], st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "timing event record failed");
   return ATTN_OK;

@@ -1,45 +1,7 @@
-// gfx950 kernels of the FlashAttention forward pass.
-//
-// The tiled forward pass with the online softmax follows page "FlashAttention/es" (marovi.ai),
-// section "El algoritmo FlashAttention": Q is split into blocks of Br rows that stay on chip,
-// K and V are streamed block by block (Bc keys) through on-chip memory, each score block is
-// formed and reduced while the running maximum m and normaliser l are carried along, the output
-// is rescaled by e^{m_old - m_new} when the maximum moves, and at the end O is divided by l and
-// L = m + ln(l) is written.  The loop order (outer over query blocks, one workgroup each; inner
-// over key blocks) is the one the section "Variantes y sucesores" credits to the second version.
-// The N x N score matrix never leaves registers.
-//
-// gfx950 mapping (one workgroup = 8 wave64s = Br = 256 query rows, 32 per wave; the two waves
-// on each SIMD alternate between matrix-core and vector phases, see fwd_kernel):
-//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K is the A operand
-//    read from LDS, Q^T the B operand held in VGPRs for the whole kernel.  In the 32x32 result
-//    each lane owns one query (lane % 32) and 16 keys, so a row maximum is an in-lane max plus a
-//    single exchange with lane ^ 32, and the running m, l live in one VGPR per lane.
-//  * K rows are stored in LDS with key bits 2 and 3 swapped.  After that permutation the 16
-//    score registers of a lane hold keys {16*(r/8) + 8*(lane/32) + r%8}, i.e. two runs of 8
-//    consecutive keys, which is exactly the B-operand layout of the P V product: P^T feeds
-//    O^T = V^T P^T straight from registers, with no LDS round trip.
-//  * V^T (d rows, keys contiguous) is the A operand of that product.  A small pack kernel
-//    writes V^T into the workspace once per call, with the d rows of each 32-block permuted so
-//    that each lane's 16 accumulator registers hold 16 consecutive output columns.
-//  * The P V product runs on fp16 operands (v_mfma_f32_32x32x16_f16, the same rate as bf16):
-//    bf16 V converts to fp16 exactly inside the pack kernel, and P <= 2^8 (see below) keeps
-//    11 significant bits instead of bf16's 8.  With bf16 P the rounding of a dominant
-//    probability alone moves O by up to 2^-9 |v|, which exceeds 1e-2 for |v| near 8.
-//    Q K^T stays on bf16 operands, which are the exact input values.
-//  * K and V^T tiles are double-buffered in LDS and prefetched into VGPRs two phases ahead.  Each
-//    LDS row is padded by 16 bytes, so the 8 (or 16) lanes of one ds_read_b128 phase, which read
-//    the same column of 8 (16) consecutive rows, hit distinct banks, while every operand address
-//    stays lane base + compile-time offset (no per-read address arithmetic).
-//  * Scores are kept in base-2 units (scale * log2 e folded in), so each probability costs one
-//    v_exp_f32; L is converted back to natural log in the epilogue.
-//  * The running maximum is only moved when a tile's maximum exceeds it by more than 8 (base 2):
-//    the output and l are then rescaled, otherwise probabilities are formed against the older
-//    maximum and stay below 2^8.  Both are exact rewritings of the same sums.
-//  * Fully masked tiles never reach the kernel: it walks the per-q-tile list of non-empty tiles
-//    from the block table, and evaluates the element mask only on partial tiles.
-#include "kcommon.h"
-#include "launch.h"
+// gfx950 kernels of the FlashAttention forward pass: the V transpose-pack kernel, the block-table
+// kernel and the instances of the forward kernel (whose body is in fwd_kernel.h), with their
+// launch functions.
+#include "fwd_kernel.h"
 
 namespace attn {
 namespace {
@@ -119,508 +81,10 @@ __global__ __launch_bounds__(256) void block_table_kernel(MaskDesc m, const int3
   if (tid == 0) cnt[row] = base;
 }
 
-// ---------------------------------------------------------------------------------------------
-// The forward kernel.  One workgroup = 8 wave64s over Br = 256 query rows (32 rows per wave).
-// Waves w and w + 4 run on the same SIMD; they form two groups (w < 4 and w >= 4) that work one
-// phase apart:
-//   M-phase of tile t : O^T += V_{t-1}^T P_{t-1}^T, then S_t^T = K_t Q^T   (MFMA + LDS reads)
-//   V-phase of tile t : mask, row max, lazy rescale, P_t = exp2(S_t - m)   (VALU)
-// Slot s (between two barriers) runs the M-phase of group (s & 1) and the V-phase of the other,
-// so on every SIMD one wave keeps the matrix core busy while the other does the softmax.
-// K_t and V_{t-1} are the LDS tiles read in slots 2t and 2t+1; K_{t+1} and V_t are fetched into
-// VGPRs at the start of slot 2t and written to the idle LDS buffers at the end of slot 2t+1.
-//
-// FP8 instances (FP8 = true) form the scores from E4M3 codes with v_mfma_scale_f32_32x32x64_f8f6f4:
-// the workgroup quantizes its own 256 Q rows (one scale s_q for the tile) and reads K as codes
-// with one scale s_k per 64-key tile (quantized by quant_fp8_kernel beforehand), so the score
-// block is s_q s_k (Q8 K8^T); the factor s_q s_k is folded into the base-2 scale of the V-phase.
-// K8 rows take D + 16 bytes in LDS (the same bank spread as the bf16 rows); P V is unchanged.
 template <int D, bool ALIBI, bool SOFTCAP, bool POS, bool OUTF32, bool FP8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     FwdArgs a) {
-  constexpr int NT = 512;                // threads per workgroup
-  constexpr int KCH = D / 8;             // 16-byte chunks per K row
-  constexpr int VCH = kBc / 8;           // 16-byte chunks per V^T row
-  constexpr int KLD = kBc * KCH / NT;    // K chunks loaded per thread per tile
-  constexpr int VLD = D * VCH / NT;      // V^T chunks loaded per thread per tile
-  constexpr int NKS = D / 16;            // k-steps of the score product
-  constexpr int NDB = D / 32;            // 32-column blocks of O
-  constexpr int KP = pitch(D);           // LDS pitch of a K row (keys x D)
-  constexpr int VP = pitch(kBc);         // LDS pitch of a V^T row (D x keys)
-  constexpr int KP8 = D + 16;            // LDS pitch of an FP8 K row, bytes
-  constexpr int KCH8 = D / 16;           // 16-byte chunks per FP8 K row
-  constexpr int NK8 = kBc * KCH8;        // 16-byte chunks per FP8 K tile
-  constexpr int KLDN = FP8 ? (NK8 + NT - 1) / NT : KLD;  // K chunks per thread per tile
-  constexpr int NKS8 = D / 64;           // k-steps of the FP8 score product
-  static_assert(kBr == 256 && kBc == 64, "kernel is written for 256 x 64 tiles");
-  static_assert(KLD >= 1 && VLD >= 1, "tile loads must cover the workgroup");
-  static_assert(!FP8 || (!ALIBI && !SOFTCAP), "FP8 instances take no score modification");
-  static_assert(kBc * KP8 <= kBc * pitch(D) * 2, "FP8 K tile must fit the K buffer");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBc * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VP];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  // Phase group: of the two waves the dispatcher placed on a SIMD, the lower-numbered one is
-  // group 0 and the other group 1 (SIMD id from the HW_ID register).  Correctness does not
-  // depend on this choice, only the overlap of matrix-core and vector work does.
-  __shared__ int simd_of[8];
-  __shared__ float qmax[8];
-  if (lane == 0) simd_of[wave] = __builtin_amdgcn_s_getreg(kHwRegSimdId) & 3;
-  __syncthreads();
-  int grp = 0;
-  for (int w2 = 0; w2 < wave; ++w2) grp += simd_of[w2] == simd_of[wave];
-  grp = __builtin_amdgcn_readfirstlane(grp > 1 ? 1 : grp);  // wave-uniform: scalar branches
-
-  // Workgroups are dispatched round-robin over the 8 XCDs; remap so that consecutive logical
-  // blocks (the q-tiles of one head, sharing K and V) run on the same XCD and its L2.
-  const int nblk = gridDim.x, w = blockIdx.x;
-  const int n8 = nblk & ~7;
-  const int lb = (w < n8) ? (w & 7) * (n8 >> 3) + (w >> 3) : w;
-  const int bh = lb / a.n_qt;
-  const int qx = lb - bh * a.n_qt;
-  // Masked kinds have longer key lists for later q-tiles: start those first.
-  const int qt = (a.kind != kMaskNone) ? a.n_qt - 1 - qx : qx;
-  const int b = bh / a.H, h = bh - b * a.H;
-  const int N = a.N;
-
-  const int qrow = qt * kBr + wave * 32 + l32;
-  const bool q_ok = qrow < N;
-  const MaskDesc md{a.kind, N, a.window, a.offs ? a.offs + (size_t)b * (a.max_docs + 1) : nullptr,
-                    a.max_docs};
-  int lo = 1, hi = 0;  // empty interval for rows beyond N
-  if (q_ok) {
-    lo = row_lo(md, qrow);
-    hi = row_hi(md, qrow);
-  }
-
-  // Q^T fragments (B operand): lane holds Q[qrow][16*ks + 8*hf .. +7]; FP8: lane holds the
-  // codes of Q[qrow][64*ks + 32*hf .. +31].
-  bf16x8 qf[FP8 ? 1 : NKS];
-  i32x8 q8f[FP8 ? NKS8 : 1];
-  float cq = a.c;  // base-2 score scale; FP8: times s_q
-  if constexpr (FP8) {
-    u32x4 xq[NKS8][4];
-    const uint16_t *qp = a.q + ((size_t)bh * N + (q_ok ? qrow : 0)) * D + hf * 32;
-#pragma unroll
-    for (int ks = 0; ks < NKS8; ++ks)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (q_ok) x = *(const u32x4 *)(qp + ks * 64 + u * 8);
-        xq[ks][u] = x;
-      }
-    // s_q = amax / 448 over the workgroup's rows (rows beyond N hold zeros).
-    float mx = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS8; ++ks)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          mx = fmaxf(mx, fabsf(__uint_as_float(xq[ks][u][e] << 16)));
-          mx = fmaxf(mx, fabsf(__uint_as_float(xq[ks][u][e] & 0xFFFF0000u)));
-        }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    if (lane == 0) qmax[wave] = mx;
-    __syncthreads();
-    float amax = qmax[0];
-#pragma unroll
-    for (int w2 = 1; w2 < 8; ++w2) amax = fmaxf(amax, qmax[w2]);
-    const float sq = amax > 0.f ? amax / 448.0f : 1.0f;
-    // code = E4M3(x / s_q), a correctly rounded division then round-to-nearest-even.
-#pragma unroll
-    for (int ks = 0; ks < NKS8; ++ks)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const uint32_t w0 = xq[ks][u][2 * h2], w1 = xq[ks][u][2 * h2 + 1];
-          q8f[ks][2 * u + h2] = (int32_t)pack_e4m3x4(
-              __uint_as_float(w0 << 16) / sq, __uint_as_float(w0 & 0xFFFF0000u) / sq,
-              __uint_as_float(w1 << 16) / sq, __uint_as_float(w1 & 0xFFFF0000u) / sq);
-        }
-    cq = a.c * sq;
-  } else {
-    const uint16_t *qp = a.q + ((size_t)bh * N + (q_ok ? qrow : 0)) * D + hf * 8;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (q_ok) x = *(const u32x4 *)(qp + ks * 16);
-      qf[ks] = __builtin_bit_cast(bf16x8, x);
-    }
-    // Settle the Q loads here, once, so no memory wait is charged to the first MFMA of every
-    // loop iteration.
-    __builtin_amdgcn_s_waitcnt(0);
-  }
-
-  // The key-tile list of this q-tile (written by the table kernel before this launch, so it is
-  // read-only here): read through the constant address space, i.e. with scalar loads.
-  int T;
-  const_i32 *lst = nullptr;
-  if (a.list) {
-    const int bm = (a.kind == kMaskDocument) ? b : 0;
-    const size_t row = (size_t)bm * a.n_qt + qt;
-    T = ((const_i32 *)a.cnt)[row];
-    lst = (const_i32 *)a.list + row * a.n_kt;
-  } else {
-    T = a.n_kt;
-  }
-  auto kt_of = [&](int t) -> int { return lst ? lst[t] : t; };
-
-  // Tile staging.  Per tile pair each thread moves NI 16-byte chunks: items 0 .. KLDN-1 are
-  // chunks of the next K tile, items KLDN .. NI-1 chunks of the current V^T tile.  Loads are
-  // buffer loads at lane-constant offsets from a per-tile base (K rows past N read as zero), so
-  // an item is one instruction and no branch.  The loads of an iteration are spread over its
-  // first slot and the LDS stores over its second, between the other work of the wave, rather
-  // than issued by every wave in one burst at a slot boundary.
-  constexpr int KROW = FP8 ? D : 2 * D;  // bytes per K row in memory
-  constexpr int KCHR = KROW / 16;        // 16-byte chunks per K row
-  constexpr int NKC = kBc * KCHR;        // chunks per K tile
-  constexpr int KPB = FP8 ? KP8 : 2 * KP;  // bytes per K row in LDS
-  constexpr int NI = KLDN + VLD;
-  static_assert(KLDN * NT >= NKC && VLD * NT == D * VCH, "staging must cover both tiles");
-  const char *kbytes = FP8 ? (const char *)(a.k8 + (size_t)bh * N * D)
-                           : (const char *)(a.k + (size_t)bh * N * D);
-  const uint16_t *vbase = a.vt + (size_t)bh * D * a.Npad;
-  // Lane-constant byte offsets of chunk u = 0: item u adds u * (NT / KCHR) rows (K) or
-  // u * (NT / VCH) rows (V^T) to both, a scalar or immediate offset.  For FP8 with d = 64 the
-  // 512 threads cover the 256 chunks of a K tile twice (identical writes).
-  const int c0 = tid % NKC;
-  const int kgo = (c0 / KCHR) * KROW + (c0 % KCHR) * 16;
-  const int klo = pi_key(c0 / KCHR) * KPB + (c0 % KCHR) * 16;
-  const int vgo = (tid / VCH) * a.Npad * 2 + (tid % VCH) * 16;  // < 2^31: tid / VCH < 64
-  const int vlo = (tid / VCH) * VP * 2 + (tid % VCH) * 16;
-  constexpr int KRU = NT / KCHR;  // K rows per item
-  constexpr int VRU = NT / VCH;   // V^T rows per item
-  static_assert(KLDN == 1 || NKC % NT == 0, "K items must tile the K tile");
-  u32x4 stg[NI];
-  auto load_item = [&](int j, int kt_k, int kt_v) {
-    if (j < KLDN) {
-      const int rows = min(kBc, N - kt_k * kBc);
-      stg[j] = buffer_load16(kbytes + (size_t)kt_k * kBc * KROW, (uint32_t)(rows * KROW), kgo,
-                             j * KRU * KROW);
-    } else {
-      const size_t left = ((size_t)D * a.Npad - (size_t)kt_v * kBc) * 2;
-      stg[j] = buffer_load16(vbase + (size_t)kt_v * kBc,
-                             (uint32_t)(left < 0xFFFFFFFFull ? left : 0xFFFFFFFFull), vgo,
-                             (int)((uint32_t)((j - KLDN) * VRU) * (uint32_t)a.Npad * 2u));
-    }
-  };
-  auto store_item = [&](int j, int kb, int vb) {
-    if (j < KLDN)
-      *(u32x4 *)((char *)sK[kb] + klo + j * KRU * KPB) = stg[j];
-    else
-      *(u32x4 *)((char *)sV[vb] + vlo + (j - KLDN) * VRU * VP * 2) = stg[j];
-  };
-
-
-  const float slopeL = ALIBI ? a.slopes[h] * 1.4426950408889634f : 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 oacc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
-  f32x16 s[2];
-  f16x8 pb[4];
-
-  // One M-phase as a single software-pipelined sequence of MFMA steps: the P V steps
-  // (key group kk, d block db) and then the score steps (k-step ks, key block blk), ordered so
-  // that consecutive MFMAs write different accumulators.  The A
-  // fragment of step i + kDepth is read from LDS while step i runs, so LDS latency stays hidden
-  // behind the matrix core.
-  // Staging item j (`item(j)`: the LDS store of chunk j, then the buffer load of chunk j of the
-  // next tile pair into the same registers) goes after MFMA step 1 + j * NST / NI.
-  constexpr int kDepth = 4;
-  auto mphase_bf16 = [&](int t, auto item) {
-    constexpr int NPV = 4 * NDB;
-    constexpr int NST = NPV + 2 * NKS;
-    const uint16_t *vbuf = &sV[(t - 1) & 1][l32 * VP + hf * 8];
-    const uint16_t *kbuf = &sK[t & 1][l32 * KP + hf * 8];
-    auto frag = [&](int i) -> u32x4 {
-      if (i < NPV) {
-        const int kk = i / NDB, db = i % NDB;
-        return *(const u32x4 *)(vbuf + db * 32 * VP + kk * 16);
-      }
-      const int j = i - NPV, ks = j >> 1, blk = j & 1;
-      return *(const u32x4 *)(kbuf + blk * 32 * KP + ks * 16);
-    };
-    u32x4 win[kDepth];
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i)
-      if (i < NST) win[i] = frag(i);
-#pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      const u32x4 cur = win[i % kDepth];
-      if (i + kDepth < NST) win[i % kDepth] = frag(i + kDepth);
-      if (i < NPV) {
-        const int kk = i / NDB, db = i % NDB;
-        oacc[db] = mfma32(__builtin_bit_cast(f16x8, cur), pb[kk], oacc[db]);
-      } else {
-        const int j = i - NPV, ks = j >> 1, blk = j & 1;
-        s[blk] = mfma32(__builtin_bit_cast(bf16x8, cur), qf[ks], ks == 0 ? f32x16{} : s[blk]);
-      }
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-        if (i == 1 + j * NST / NI) item(j);
-    }
-    // Pin that order for the scheduler: kDepth LDS reads, then MFMA / LDS read pairs, with the
-    // staging items in between.
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-        if (i == 1 + j * NST / NI) {
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-      if (i + kDepth < NST) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  };
-  // The FP8 M-phase: the same P V steps, then 2 * D / 64 score steps (k-step ks, key block blk),
-  // each fed by two 16-byte LDS reads of K8 (bytes 64*ks + 32*hf .. +31 of the lane's key row).
-  // The LDS reads form one stream, kDepth reads ahead of the MFMA that consumes them.
-  auto mphase_fp8 = [&](int t, auto item) {
-    constexpr int NPV = 4 * NDB;
-    constexpr int NSS = 2 * NKS8;      // score MFMAs
-    constexpr int NST = NPV + NSS;     // MFMAs
-    constexpr int NR = NPV + 2 * NSS;  // LDS reads
-    const uint16_t *vbuf = &sV[(t - 1) & 1][l32 * VP + hf * 8];
-    const uint8_t *kbuf = (const uint8_t *)sK[t & 1] + l32 * KP8 + hf * 32;
-    auto frag = [&](int r) -> u32x4 {
-      if (r < NPV) {
-        const int kk = r / NDB, db = r % NDB;
-        return *(const u32x4 *)(vbuf + db * 32 * VP + kk * 16);
-      }
-      const int j = r - NPV, st = j >> 1, half = j & 1, ks = st >> 1, blk = st & 1;
-      return *(const u32x4 *)(kbuf + blk * 32 * KP8 + ks * 64 + half * 16);
-    };
-    u32x4 win[kDepth];
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) win[i] = frag(i);
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      const u32x4 cur = win[i % kDepth];
-      if (i + kDepth < NR) win[i % kDepth] = frag(i + kDepth);
-      const int kk = i / NDB, db = i % NDB;
-      oacc[db] = mfma32(__builtin_bit_cast(f16x8, cur), pb[kk], oacc[db]);
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-        if (i == 1 + j * NST / NI) item(j);
-    }
-#pragma unroll
-    for (int st = 0; st < NSS; ++st) {
-      const int r0 = NPV + 2 * st, ks = st >> 1, blk = st & 1;
-      const u32x4 a0 = win[r0 % kDepth];
-      if (r0 + kDepth < NR) win[r0 % kDepth] = frag(r0 + kDepth);
-      const u32x4 a1 = win[(r0 + 1) % kDepth];
-      if (r0 + 1 + kDepth < NR) win[(r0 + 1) % kDepth] = frag(r0 + 1 + kDepth);
-      const i32x8 kf = {(int32_t)a0[0], (int32_t)a0[1], (int32_t)a0[2], (int32_t)a0[3],
-                        (int32_t)a1[0], (int32_t)a1[1], (int32_t)a1[2], (int32_t)a1[3]};
-      s[blk] = mfma32_fp8(kf, q8f[ks], ks == 0 ? f32x16{} : s[blk]);
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-        if (NPV + st == 1 + j * NST / NI) item(j);
-    }
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-        if (i == 1 + j * NST / NI) {
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-      if (i + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int st = 0; st < NSS; ++st) {
-      const int r0 = NPV + 2 * st;
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-        if (NPV + st == 1 + j * NST / NI) {
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-      if (r0 + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (r0 + 1 + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  };
-  auto mphase = [&](int t, auto item) {
-    if constexpr (FP8)
-      mphase_fp8(t, item);
-    else
-      mphase_bf16(t, item);
-    // Keep the score MFMAs in this slot: without a use here the compiler sinks the last ones
-    // past the barrier into the (conditional) V-phase that reads them.
-    const f32x16 s0 = s[0], s1 = s[1];
-    __asm__ volatile("" ::"v"(s0), "v"(s1));
-  };
-
-  // Zero P and the V buffer read by the first M-phase (its P V step then adds exactly 0).
-#pragma unroll
-  for (int g = 0; g < 4; ++g) pb[g] = f16x8{};
-  for (int i = tid; i < D * VP / 8; i += NT) *(u32x4 *)&sV[1][i * 8] = u32x4{0u, 0u, 0u, 0u};
-  if (T > 0) {
-#pragma unroll
-    for (int j = 0; j < KLDN; ++j) load_item(j, kt_of(0), 0);
-#pragma unroll
-    for (int j = 0; j < KLDN; ++j) store_item(j, 0, 0);
-  }
-  __syncthreads();
-
-  // V-phase of tile t: score modifications, mask, online softmax, P_t in fp16.
-  auto vphase = [&](int kt) {
-    // Base-2 score scale of this tile; FP8: times s_k of the key tile (read-only here, written
-    // by the quantization kernel before this launch: a scalar load).
-    float c = cq;
-    if constexpr (FP8) c = cq * ((const_f32 *)a.sk)[(size_t)bh * a.n_kt + kt];
-    // Register r of block blk is key kt*Bc + 32*blk + 16*(r/8) + 8*hf + r%8.
-    const int kb = kt * kBc + 8 * hf;
-    if constexpr (!POS) {
-      const float abase = ALIBI ? slopeL * (float)(kb - qrow) : 0.f;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = s[blk][r];
-          float tt;
-          if constexpr (SOFTCAP) {
-            const float e = __builtin_amdgcn_exp2f(x * a.cap_c1);
-            tt = fmaf(-2.f * a.capL, __builtin_amdgcn_rcpf(1.f + e), a.capL);
-          } else {
-            tt = x * c;
-          }
-          if constexpr (ALIBI)
-            tt += fmaf(slopeL, (float)(32 * blk + 16 * (r >> 3) + (r & 7)), abase);
-          s[blk][r] = tt;
-        }
-      }
-    }
-    // Element mask only when some row of this wave does not allow all 64 keys of the tile
-    // (hi <= N - 1 always, so a fully allowed row also has the tile in range).
-    if (__builtin_amdgcn_ballot_w64(!(lo <= kt * kBc && hi >= kt * kBc + kBc - 1))) {
-      keep_branch();
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kb + 32 * blk + 16 * (r >> 3) + (r & 7);
-          if (j < lo || j > hi) s[blk][r] = -INFINITY;
-        }
-      }
-    }
-    // Tile row maximum: in-lane over 32 keys, then with the lane that shares the query.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
-    mx = pair_max(mx);
-    const float m_tile = POS ? mx * c : mx;
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kTau)) {
-      keep_branch();
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float psum[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x8 pv;
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = s[g >> 1][8 * (g & 1) + e];
-        const float p = POS ? __builtin_amdgcn_exp2f(fmaf(x, c, -m_use))
-                            : __builtin_amdgcn_exp2f(x - m_use);
-        pv[e] = p;
-        acc += p;
-      }
-      psum[g] = acc;
-      pb[g] = __builtin_convertvector(pv, f16x8);
-    }
-    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
-  };
-  // kt of tiles k - 1 .. k + 2 are kept in scalars; tile k + 3's is read one iteration ahead.
-  // Past the last tile they are 0 (a valid tile: its data is staged but never used).
-  int kt_prev = 0, kt_cur = T > 0 ? kt_of(0) : 0, kt_next = T > 1 ? kt_of(1) : 0;
-  int kt_n2 = T > 2 ? kt_of(2) : 0;
-  auto advance = [&](int k) {
-    const int kt_n3 = k + 3 < T ? kt_of(k + 3) : 0;
-    kt_prev = kt_cur;
-    kt_cur = kt_next;
-    kt_next = kt_n2;
-    kt_n2 = kt_n3;
-  };
-  // The chunks of K_1 and V_0, written in iteration 0.
-#pragma unroll
-  for (int j = 0; j < NI; ++j) load_item(j, kt_next, kt_cur);
-
-  // Two slots per iteration k.  Slot A: group 0 runs M-phase k, group 1 V-phase k-1.  Slot B:
-  // group 0 runs V-phase k, group 1 M-phase k.  K_k and V_{k-1} are read in both slots.  Each
-  // wave stages its chunks inside its own M-phase, between the MFMAs: it writes the chunks of
-  // K_{k+1} and V_k (fetched one iteration earlier) to the idle buffers, which no step of
-  // iteration k reads, and fetches those of K_{k+2} and V_{k+1}.  Both groups execute the same
-  // 2T + 2 barriers.  In M-phase 0, P = 0 against a zeroed V buffer adds nothing; in M-phase T
-  // the score product reads a stale K buffer and its result is never used.
-  auto stage = [&](int k) {
-    return [&, k](int j) {
-      store_item(j, (k + 1) & 1, k & 1);
-      load_item(j, kt_n2, kt_next);
-    };
-  };
-  if (grp == 0) {
-    for (int k = 0; k <= T; ++k) {
-      mphase(k, stage(k));
-      __syncthreads();
-      if (k < T) vphase(kt_cur);
-      advance(k);
-      __syncthreads();
-    }
-  } else {
-    for (int k = 0; k <= T; ++k) {
-      if (k >= 1) vphase(kt_prev);
-      __syncthreads();
-      mphase(k, stage(k));
-      advance(k);
-      __syncthreads();
-    }
-  }
-
-  // Epilogue: O = O / l, L = (m + log2 l) * ln 2.
-  const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q_ok) {
-    const size_t obase = ((size_t)bh * N + qrow) * D + 16 * hf;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const f32x16 o = oacc[db] * inv;
-      if constexpr (OUTF32) {
-        float *op = (float *)a.o + obase + 32 * db;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *(f32x4 *)(op + 4 * i) = f32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
-      } else {
-        uint16_t *op = (uint16_t *)a.o + obase + 32 * db;
-        const f32x8 o0 = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
-        const f32x8 o1 = {o[8], o[9], o[10], o[11], o[12], o[13], o[14], o[15]};
-        *(bf16x8 *)op = __builtin_convertvector(o0, bf16x8);
-        *(bf16x8 *)(op + 8) = __builtin_convertvector(o1, bf16x8);
-      }
-    }
-    if (a.lse && hf == 0)
-      a.lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  }
+  fwd_body<D, ALIBI, SOFTCAP, POS, OUTF32, FP8, 0>(a);
 }
 
 template <int D, bool ALIBI, bool SOFTCAP, bool POS, bool FP8 = false>

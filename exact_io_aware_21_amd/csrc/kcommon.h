@@ -3,8 +3,7 @@
 // next MFMA directly, and lane-pair reductions.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "hipdefs.h"
 
 namespace attn {
 namespace {

@@ -1,8 +1,7 @@
 // Internal launch interface between the C-ABI layer (api.cpp) and the kernels (fwd.hip).
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "hipdefs.h"
 
 #include "tiles.h"
 
@@ -26,6 +25,17 @@ struct FwdArgs {
   const int32_t *list;
   const uint8_t *k8;  // FP8 instances: K as E4M3 codes [BH][N][D]
   const float *sk;    // FP8 instances: K scales [BH][n_kt], one per 64-key tile
+  float scale;               // runtime-compiled modifications: the natural-units score scale
+  const float *mod_params;   // runtime-compiled modifications: the caller's parameters
+};
+
+// Block table of a runtime-compiled mask: cls [B][n_qt][n_kt], cnt [B][n_qt], list [B][n_qt][n_kt].
+struct ModTableArgs {
+  int N, n_qt, n_kt;
+  const float *params;
+  int8_t *cls;
+  int32_t *cnt;
+  int32_t *list;
 };
 
 // Variant switches that select a kernel instance.

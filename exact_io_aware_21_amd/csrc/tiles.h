@@ -15,8 +15,7 @@
 // FlashAttention-4 ..." (section "Limitaciones actuales").
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "hipdefs.h"
 
 namespace attn {
 

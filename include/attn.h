@@ -64,7 +64,8 @@ enum {
   ATTN_ERR_INVALID_ARG = -1,        /* a pointer, size, alignment or variant field is invalid */
   ATTN_ERR_UNSUPPORTED_DEVICE = -2, /* no HIP device, or the current device is not gfx950 */
   ATTN_ERR_LAUNCH = -3,             /* a kernel launch was rejected by the runtime */
-  ATTN_ERR_WORKSPACE = -4           /* workspace missing, misaligned or smaller than needed */
+  ATTN_ERR_WORKSPACE = -4,          /* workspace missing, misaligned or smaller than needed */
+  ATTN_ERR_COMPILE = -5             /* attn_mod_create: the modification did not compile */
 };
 
 /* output dtype of O */
@@ -226,6 +227,60 @@ size_t attn_decode_workspace_size(int B, int H, int Lq, int d, int page_size, in
 
 const char *attn_strerror(int code);
 const char *attn_last_error(void);
+
+/*
+ * Runtime-compiled score and mask modifications.  Page "El FlexAttention de PyTorch con
+ * FlashAttention-4 ..." (opening paragraph): FlexAttention lets the user write the score
+ * modification and the mask as small functions that are compiled into the attention kernel.
+ * Here they are HIP C++ device functions, compiled with hipRTC into the same forward kernel the
+ * fixed variants use (its tiles, block-sparse skip and online softmax):
+ *     __device__ float attn_score_mod(float s, int b, int h, int i, int j, const float *p);
+ *         the score of query i and key j of batch entry b, head h, from the scaled score
+ *         s = scale * q_i . k_j (natural units); p = the caller's mod_params;
+ *     __device__ bool attn_mask_mod(int b, int i, int j, const float *p);
+ *         whether key j is allowed for query i (the same for every head; a head-dependent
+ *         mask can return -INFINITY from attn_score_mod instead, without tile skipping).
+ * The source defines the ones named by `flags` and may hold other device code.
+ */
+typedef struct attn_mod_s attn_mod;
+enum { ATTN_MODF_SCORE = 1, ATTN_MODF_MASK = 2 };
+
+/*
+ * attn_mod_create -- compiles `source` (NUL-terminated) for head dimension d (64 or 128) and
+ * the functions named by flags (ATTN_MODF_SCORE and/or ATTN_MODF_MASK) into a gfx950 code
+ * object held by *out (host memory; each device loads it on first use).  Needs no GPU.
+ * log (optional, log_size bytes) receives the compiler's messages, NUL-terminated.
+ * Returns ATTN_OK, ATTN_ERR_INVALID_ARG or ATTN_ERR_COMPILE (*out = NULL).
+ */
+int attn_mod_create(const char *source, uint32_t flags, int d, attn_mod **out, char *log,
+                    size_t log_size);
+
+/* Releases a modification and its loaded code (NULL is ignored).  Not while a call using it
+   is being enqueued; kernels already launched keep running. */
+void attn_mod_destroy(attn_mod *m);
+
+/* Bytes of workspace attn_fwd_mod needs (0 on invalid arguments): the key-transposed V and,
+   with a mask, the block table ([B][ceil(N/Br)] rows of ceil(N/Bc) tiles). */
+size_t attn_mod_workspace_size(const attn_mod *m, int B, int H, int N);
+
+/*
+ * attn_fwd_mod -- the forward pass with a runtime-compiled modification: O = softmax(S) V and
+ * L as for attn_fwd, with S_ij = attn_score_mod(scale * q_i . k_j, b, h, i, j, p) (or the scaled
+ * score without ATTN_MODF_SCORE) and S_ij = -inf where attn_mask_mod(b, i, j, p) is false.
+ *   q, k, v, o, lse, B, H, N, scale : as for attn_fwd, d = the mod's d; with a mask
+ *             additionally B * ceil(N/Br) <= 65535.
+ *   mod_params : device pointer (4-byte aligned) passed to the functions as p; may be NULL if
+ *             they do not read it.  Not validated.
+ *   params  : required: workspace (>= attn_mod_workspace_size bytes, 256-byte aligned),
+ *             o_dtype, timing_events (bracket the forward kernel); other fields are ignored.
+ * With a mask, the call first evaluates attn_mask_mod on every (i, j) to classify the tiles
+ * (the attn_block_table classes, per batch entry) and skips the empty ones; on partial tiles it
+ * evaluates the mask per element.  A row with no allowed key gets O = 0, L = -inf.
+ * Precision as attn_fwd (the score function runs in fp32).
+ */
+int attn_fwd_mod(const attn_mod *m, const void *q, const void *k, const void *v, void *o,
+                 float *lse, int B, int H, int N, float scale, const float *mod_params,
+                 const attn_params *params, void *stream);
 
 #ifdef __cplusplus
 }

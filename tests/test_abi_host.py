@@ -343,3 +343,88 @@ def test_quantize_fp8_argument_checks(args, code):
     if code == attn.ATTN_ERR_UNSUPPORTED_DEVICE and _gpu_present():
         pytest.skip("only meaningful on a host without a GPU")
     assert attn.lib().attn_quantize_fp8(*args, None) == code
+
+
+# --- runtime-compiled modifications -----------------------------------------------------------
+MOD_SRC = """__device__ float attn_score_mod(float s, int b, int h, int i, int j, const float *p) {
+  return s - p[h] * (float)(i - j); }
+__device__ bool attn_mask_mod(int b, int i, int j, const float *p) { return j <= i; }"""
+
+
+@pytest.fixture(scope="module")
+def alibi_causal_mod():
+    m = attn.AttnMod(MOD_SRC, attn.ATTN_MODF_SCORE | attn.ATTN_MODF_MASK, 128)
+    yield m
+    m.close()
+
+
+def test_mod_compiles_without_gpu_and_sizes_its_workspace(alibi_causal_mod):
+    m = alibi_causal_mod
+    al = lambda x: (x + 255) // 256 * 256
+    B, H, N, d = 2, 3, 1000, 128
+    n_qt, n_kt = 4, 16
+    rows = B * n_qt
+    assert m.workspace_size(B, H, N) == al(B * H * d * n_kt * 64 * 2) + al(rows * n_kt) + \
+        al(rows * 4) + al(rows * n_kt * 4)
+    assert m.workspace_size(1, 1, 0) == 0
+    assert m.workspace_size(300, 1, 1 << 16) == 0  # B * ceil(N/Br) > 65535 with a mask
+    score_only = attn.AttnMod(MOD_SRC.split("__device__ bool")[0], attn.ATTN_MODF_SCORE, 64)
+    assert score_only.workspace_size(B, H, N) == al(B * H * 64 * n_kt * 64 * 2)
+    score_only.close()
+
+
+@pytest.mark.parametrize("src,flags,d", [
+    (MOD_SRC, 0, 128), (MOD_SRC, 4, 128), (MOD_SRC, 3, 96), (None, 3, 128)])
+def test_mod_create_rejects_invalid_arguments(src, flags, d):
+    h = ctypes.c_void_p()
+    rc = attn.lib().attn_mod_create(None if src is None else src.encode(), flags, d,
+                                    ctypes.byref(h), None, 0)
+    assert rc == attn.ATTN_ERR_INVALID_ARG and not h.value
+
+
+@pytest.mark.parametrize("src,flags", [
+    ("__device__ float attn_score_mod(float s, int b, int h, int i, int j, const float *p) { return s + ; }", 1),
+    # the declared signature is not defined: the link step fails
+    ("__device__ float attn_score_mod(float s) { return s; }", 1),
+    ("__device__ float attn_score_mod(float s, int b, int h, int i, int j, const float *p) { return s; }", 2),
+])
+def test_mod_compile_errors_are_reported(src, flags):
+    with pytest.raises(attn.AttnError) as e:
+        attn.AttnMod(src, flags, 64)
+    assert e.value.code == attn.ATTN_ERR_COMPILE and "error" in str(e.value)
+
+
+def _call_fwd_mod(m, q=16, k=16, v=16, o=16, lse=None, B=1, H=1, N=64, scale=0.125, mp=None,
+                  params="default"):
+    p = attn.attn_params()
+    p.workspace = 256
+    p.workspace_bytes = 1 << 40
+    pp = ctypes.byref(p) if params == "default" else params
+    return attn.lib().attn_fwd_mod(m, q, k, v, o, lse, B, H, N, scale, mp, pp, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, attn.ATTN_ERR_INVALID_ARG),
+    ({"k": 8}, attn.ATTN_ERR_INVALID_ARG),
+    ({"lse": 2}, attn.ATTN_ERR_INVALID_ARG),
+    ({"mp": 2}, attn.ATTN_ERR_INVALID_ARG),
+    ({"N": 0}, attn.ATTN_ERR_INVALID_ARG),
+    ({"scale": float("inf")}, attn.ATTN_ERR_INVALID_ARG),
+    ({"params": None}, attn.ATTN_ERR_INVALID_ARG),
+    ({"B": 300, "N": 1 << 16}, attn.ATTN_ERR_INVALID_ARG),
+])
+def test_fwd_mod_rejects_invalid_arguments(alibi_causal_mod, kw, code):
+    assert _call_fwd_mod(alibi_causal_mod._h, **kw) == code
+    assert attn.lib().attn_last_error() != b""
+
+
+def test_fwd_mod_rejects_null_mod_and_small_workspace(alibi_causal_mod):
+    assert _call_fwd_mod(None) == attn.ATTN_ERR_INVALID_ARG
+    p = attn.attn_params()
+    p.workspace, p.workspace_bytes = 256, 100
+    assert _call_fwd_mod(alibi_causal_mod._h, params=ctypes.byref(p)) == attn.ATTN_ERR_WORKSPACE
+
+
+@pytest.mark.skipif(_gpu_present(), reason="only meaningful on a host without a GPU")
+def test_fwd_mod_valid_call_without_gpu_reports_unsupported_device(alibi_causal_mod):
+    assert _call_fwd_mod(alibi_causal_mod._h) == attn.ATTN_ERR_UNSUPPORTED_DEVICE
