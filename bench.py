@@ -1,7 +1,7 @@
 """Benchmark of the attention forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--cold] [--pass fwd|bwd|decode] [--fp8]
+                    [--cold] [--pass fwd|bwd|decode] [--fp8] [--mod]
 
 A step is one attn_fwd call over one batch of seeded synthetic input already resident in HBM:
 the V transpose-pack kernel, the block-table kernel (masked kinds) and the forward kernel.
@@ -25,6 +25,10 @@ scale per 256-row Q tile and per 64-key K tile, P V in fp16).  A step then also 
 quantization kernel.  Half of the counted FLOPs (Q K^T) run at the fp8 MFMA rate and half (P V)
 at the fp16 rate, so the kernel's peak is the harmonic mix of the two published peaks:
 1 / (0.5 / 5000 + 0.5 / 2500) = 3333 TFLOP/s.
+
+--mod runs the same workload through a runtime-compiled modification (attn_mod_create /
+attn_fwd_mod): the workload's score variant and mask written as HIP C++ functions, compiled by
+hipRTC when the benchmark starts.  A step then also holds the two mask-table kernels.
 
 The "cpu_baseline" object times the fp64 CPU oracle (a plain, untuned reference) on the host
 cores on a bounded sample of the same workload, in the same unit.
@@ -174,6 +178,36 @@ class SclkSampler:
         x = sorted(self.samples)
         return {"median": x[len(x) // 2], "min": x[0], "max": x[-1], "samples": len(x),
                 "source": self.path}
+
+
+def mod_source(w):
+    """The workload's variant as a runtime-compiled modification: (source, flags, params), params
+    an fp32 array (ALiBi slopes; nothing else is needed by these variants)."""
+    import numpy as np
+    from exact_io_aware_21_amd import inputs
+    score, mask = [], None
+    if w.softcap:
+        score.append(f"s = {float(w.softcap)!r}f * tanhf(s / {float(w.softcap)!r}f);")
+    if w.alibi:
+        score.append("s -= p[h] * (float)(i - j);")
+    if w.mask == "causal":
+        mask = "return j <= i;"
+    elif w.mask == "window":
+        mask = f"return j <= i && i - j < {int(w.window)};"
+    elif w.mask != "none":
+        raise SystemExit(f"--mod: no runtime-compiled form of the {w.mask} mask in this benchmark")
+    src, flags = "", 0
+    if score:
+        src += ("__device__ float attn_score_mod(float s, int b, int h, int i, int j, "
+                "const float *p) { " + " ".join(score) + " return s; }\n")
+        flags |= 1
+    if mask:
+        src += "__device__ bool attn_mask_mod(int b, int i, int j, const float *p) { " + mask + " }\n"
+        flags |= 2
+    if not flags:
+        raise SystemExit("--mod: the workload has no score modification or mask")
+    params = inputs.alibi_slopes(w.H) if w.alibi else np.zeros(1, dtype=np.float32)
+    return src, flags, params
 
 
 def cpu_baseline(w, inp, budget_s=20.0, chunk=2048, fp8=False):
@@ -392,6 +426,8 @@ def main():
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode"), default="fwd",
                     help="bwd: time attn_bwd instead (10 d FLOPs per allowed pair; no CPU leg); "
                          "decode: time attn_decode on a paged-cache workload (GB/s)")
+    ap.add_argument("--mod", action="store_true",
+                    help="run the workload's variant as a runtime-compiled modification")
     ap.add_argument("--fp8", action="store_true",
                     help="time the FP8 forward pass (ATTN_PREC_FP8; no score modifications)")
     ap.add_argument("--traffic", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH",
@@ -438,8 +474,26 @@ def main():
         bench_bwd(args, w, inp, q, k, v, o, lse, var, slopes, offs, dev)
         return
 
+    compile_s = None
+    if args.mod:
+        if args.fp8:
+            raise SystemExit("--mod and --fp8 are separate paths")
+        src, flags, params = mod_source(w)
+        t0 = time.perf_counter()
+        mod = attn.AttnMod(src, flags, w.d)
+        compile_s = time.perf_counter() - t0
+        mparams = torch.from_numpy(params).to(dev)
+        mws = mod.alloc_workspace(w.B, w.H, w.N, dev)
+
+        def call(timing_events=None):
+            mod.fwd(q, k, v, o, lse, inp["scale"], mparams, workspace=mws,
+                    timing_events=timing_events)
+    else:
+        def call(timing_events=None):
+            attn.attn_fwd(q, k, v, o, lse, inp["scale"], var, timing_events=timing_events, **kw)
+
     for _ in range(args.warmup):
-        attn.attn_fwd(q, k, v, o, lse, inp["scale"], var, **kw)
+        call()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -460,7 +514,7 @@ def main():
             if args.cold:
                 flush.fill_(i & 255)
                 cev[i][0].record()
-            attn.attn_fwd(q, k, v, o, lse, inp["scale"], var, timing_events=kev[i], **kw)
+            call(kev[i])
             if args.cold:
                 cev[i][1].record()
         end.record()
@@ -502,7 +556,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3+fp16" if args.fp8 else "bf16",
         "data": "synthetic (seeded N(0, sigma^2) Q/K/V rounded to bf16)",
-        "config": {"workload": ("fp8_" if args.fp8 else "") + w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
+        "config": {"workload": ("fp8_" if args.fp8 else "mod_" if args.mod else "") + w.name,
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
                    "window": w.window, "alibi": w.alibi, "softcap": w.softcap,
                    "unmasked_gflop": round(flops / 1e9, 3),
                    "fwd_kernel_ms": round(kern_ms, 4),
@@ -510,7 +565,9 @@ def main():
                    "fwd_kernel_ms_min": round(kern[0], 4),
                    "cache": "cold: 512 MiB written before each call" if args.cold else "warm",
                    "compulsory_hbm_bytes": hbm_bytes,
-                   "sclk_mhz": sclk_rec},
+                   "sclk_mhz": sclk_rec,
+                   **({"runtime_compiled_modification": {"compile_s": round(compile_s, 2)}}
+                      if args.mod else {})},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -231,7 +231,7 @@ extern "C" const char attn_rtc_hipdefs_h[], attn_rtc_kcommon_h[], attn_rtc_tiles
     attn_rtc_launch_h[], attn_rtc_fwd_kernel_h[];
 
 struct ModLayout {
-  size_t vt, cls, cnt, list, total;
+  size_t vt, cls, cnt, list, wfull, total;
 };
 
 ModLayout mod_layout(const Shape &s, bool mask) {
@@ -247,6 +247,8 @@ ModLayout mod_layout(const Shape &s, bool mask) {
     off = align256(off + rows * 4);
     w.list = off;
     off = align256(off + rows * s.n_kt * 4);
+    w.wfull = off;
+    off = align256(off + rows * s.n_kt);
   }
   w.total = off;
   return w;
@@ -643,10 +645,10 @@ int attn_mod_create(const char *source, uint32_t flags, int d, attn_mod **out, c
                 "\n#line 1 \"attn_mod_kernels\"\n"
                 "extern \"C\" __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))"
                 " void attn_mod_fwd_bf16(attn::FwdArgs a) {"
-                " attn::fwd_body<%d, false, false, false, false, false, %u>(a); }\n"
+                " attn::fwd_body<%d, false, false, true, false, false, %u>(a); }\n"
                 "extern \"C\" __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))"
                 " void attn_mod_fwd_f32(attn::FwdArgs a) {"
-                " attn::fwd_body<%d, false, false, false, true, false, %u>(a); }\n",
+                " attn::fwd_body<%d, false, false, true, true, false, %u>(a); }\n",
                 d, flags, d, flags);
   prog += tail;
   if (flags & ATTN_MODF_MASK)
@@ -763,7 +765,7 @@ int attn_fwd_mod(const attn_mod *mc, const void *q, const void *k, const void *v
   a.Npad = s.Npad;
   a.n_qt = s.n_qt;
   a.n_kt = s.n_kt;
-  a.c = scale * 1.4426950408889634f;
+  a.c = 1.4426950408889634f;  // scores reach the softmax in natural units (see fwd_kernel.h)
   a.scale = scale;
   a.mod_params = mod_params;
   a.kind = ATTN_MASK_NONE;
@@ -776,6 +778,7 @@ int attn_fwd_mod(const attn_mod *mc, const void *q, const void *k, const void *v
     t.cls = (int8_t *)(ws + wl.cls);
     t.cnt = (int32_t *)(ws + wl.cnt);
     t.list = (int32_t *)(ws + wl.list);
+    t.wfull = (uint8_t *)(ws + wl.wfull);
     void *targs[] = {&t};
     if (hipModuleLaunchKernel(m->cls[dev], (unsigned)s.n_kt, (unsigned)(B * s.n_qt), 1, 256, 1,
                               1, 0, st, targs, nullptr) != hipSuccess ||
@@ -787,6 +790,7 @@ int attn_fwd_mod(const attn_mod *mc, const void *q, const void *k, const void *v
     a.cls = t.cls;
     a.cnt = t.cnt;
     a.list = t.list;
+    a.wfull = t.wfull;
   }
   void *const *ev = params->timing_events;
   if (ev && hipEventRecord((hipEvent_t)ev[0], st) != hipSuccess)

@@ -58,7 +58,6 @@ namespace {
 
 constexpr int kModScore = 1;  // MOD bit: attn_score_mod replaces the scaled score
 constexpr int kModMask = 2;   // MOD bit: attn_mask_mod decides the element mask
-constexpr float kLog2eF = 1.4426950408889634f;
 
 // The forward kernel body.  One workgroup = 8 wave64s over Br = 256 query rows (32 rows per wave).
 // Waves w and w + 4 run on the same SIMD; they form two groups (w < 4 and w >= 4) that work one
@@ -94,6 +93,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   static_assert(kBr == 256 && kBc == 64, "kernel is written for 256 x 64 tiles");
   static_assert(KLD >= 1 && VLD >= 1, "tile loads must cover the workgroup");
   static_assert(!FP8 || (!ALIBI && !SOFTCAP), "FP8 instances take no score modification");
+  static_assert(MOD == 0 || (POS && !ALIBI && !SOFTCAP && !FP8),
+                "modification instances take natural-units scores on the POS path");
   static_assert(kBc * KP8 <= kBc * pitch(D) * 2, "FP8 K tile must fit the K buffer");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBc * KP];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VP];
@@ -419,14 +420,20 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     if constexpr (FP8) c = cq * ((const_f32 *)a.sk)[(size_t)bh * a.n_kt + kt];
     // Register r of block blk is key kt*Bc + 32*blk + 16*(r/8) + 8*hf + r%8.
     const int kb = kt * kBc + 8 * hf;
-    if constexpr ((MOD & kModScore) != 0) {
-      // The user's modification of the natural-units score, then to base 2.
+    if constexpr (MOD != 0) {
+      // Natural-units scores, modified by the user's function; these instances run with
+      // POS = true and c = log2(e), so the conversion to base 2 rides on the exponent's FMA.
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = kb + 32 * blk + 16 * (r >> 3) + (r & 7);
-          s[blk][r] = attn_score_mod(s[blk][r] * a.scale, b, h, qrow, j, a.mod_params) * kLog2eF;
+          const float x = s[blk][r] * a.scale;
+          if constexpr ((MOD & kModScore) != 0) {
+            const int j = kb + 32 * blk + 16 * (r >> 3) + (r & 7);
+            s[blk][r] = attn_score_mod(x, b, h, qrow, j, a.mod_params);
+          } else {
+            s[blk][r] = x;
+          }
         }
       }
     } else if constexpr (!POS) {
@@ -450,10 +457,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       }
     }
     if constexpr ((MOD & kModMask) != 0) {
-      // The user's mask on every element of a tile the table does not mark full (class 2).
+      // The user's mask on every element, unless the table marks this wave's 32 rows of the
+      // tile fully allowed (bit `wave` of its row-block byte).
       const size_t ci = ((size_t)b * a.n_qt + qt) * a.n_kt + kt;
-      const int cls = (((const_i32 *)a.cls)[ci >> 2] >> (8 * (int)(ci & 3))) & 0xFF;
-      if (cls != 2) {
+      const int wf = (((const_i32 *)a.wfull)[ci >> 2] >> (8 * (int)(ci & 3))) & 0xFF;
+      if (!((wf >> wave) & 1)) {
         keep_branch();
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
@@ -599,12 +607,15 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
 
 // ---------------------------------------------------------------------------------------------
 // Block table of a user mask (MOD & kModMask): the classes of the kernel's tiles, from the mask
-// evaluated on every pair.  One workgroup of 256 threads per tile (kt, row = b * n_qt + qt);
+// evaluated on every pair, and per tile a byte whose bit w says that rows 32w .. 32w + 31 of the
+// tile are all in range and allowed against all its keys (the forward kernel's wave w then
+// skips the element mask).  One workgroup of 256 threads per tile (kt, row = b * n_qt + qt);
 // thread t tests query row qt * Br + t against the tile's 64 keys.  Class 0: no allowed
 // in-range pair; 2: all Br * Bc pairs in range and allowed; 1: otherwise (the convention of the
 // built-in table).
 __device__ __forceinline__ void mod_class_body(const ModTableArgs &t) {
   __shared__ int flags[4][2];
+  __shared__ int wfull[4];
   const int kt = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = row / t.n_qt, qt = row - b * t.n_qt;
   const int i = qt * kBr + tid;
@@ -619,12 +630,16 @@ __device__ __forceinline__ void mod_class_body(const ModTableArgs &t) {
   if (lane == 0) {
     flags[wave][0] = bany != 0;
     flags[wave][1] = bnot == 0;
+    // the forward kernel's waves hold 32 rows: this wave's rows are its waves 2w and 2w + 1
+    wfull[wave] = ((uint32_t)bnot == 0u ? 1 : 0) | ((bnot >> 32) == 0u ? 2 : 0);
   }
   __syncthreads();
   if (tid == 0) {
     const bool A = flags[0][0] | flags[1][0] | flags[2][0] | flags[3][0];
     const bool F = flags[0][1] & flags[1][1] & flags[2][1] & flags[3][1];
     t.cls[(size_t)row * t.n_kt + kt] = (int8_t)(A ? (F ? 2 : 1) : 0);
+    t.wfull[(size_t)row * t.n_kt + kt] =
+        (uint8_t)(wfull[0] | (wfull[1] << 2) | (wfull[2] << 4) | (wfull[3] << 6));
   }
 }
 

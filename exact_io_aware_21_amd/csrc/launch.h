@@ -27,15 +27,18 @@ struct FwdArgs {
   const float *sk;    // FP8 instances: K scales [BH][n_kt], one per 64-key tile
   float scale;               // runtime-compiled modifications: the natural-units score scale
   const float *mod_params;   // runtime-compiled modifications: the caller's parameters
+  const uint8_t *wfull;      // runtime-compiled masks: per tile, the fully allowed 32-row blocks
 };
 
-// Block table of a runtime-compiled mask: cls [B][n_qt][n_kt], cnt [B][n_qt], list [B][n_qt][n_kt].
+// Block table of a runtime-compiled mask: cls [B][n_qt][n_kt], cnt [B][n_qt], list [B][n_qt][n_kt],
+// wfull [B][n_qt][n_kt].
 struct ModTableArgs {
   int N, n_qt, n_kt;
   const float *params;
   int8_t *cls;
   int32_t *cnt;
   int32_t *list;
+  uint8_t *wfull;  // [B][n_qt][n_kt]
 };
 
 // Variant switches that select a kernel instance.

@@ -365,7 +365,7 @@ def test_mod_compiles_without_gpu_and_sizes_its_workspace(alibi_causal_mod):
     n_qt, n_kt = 4, 16
     rows = B * n_qt
     assert m.workspace_size(B, H, N) == al(B * H * d * n_kt * 64 * 2) + al(rows * n_kt) + \
-        al(rows * 4) + al(rows * n_kt * 4)
+        al(rows * 4) + al(rows * n_kt * 4) + al(rows * n_kt)
     assert m.workspace_size(1, 1, 0) == 0
     assert m.workspace_size(300, 1, 1 << 16) == 0  # B * ceil(N/Br) > 65535 with a mask
     score_only = attn.AttnMod(MOD_SRC.split("__device__ bool")[0], attn.ATTN_MODF_SCORE, 64)

@@ -126,8 +126,17 @@ def check(name, w, inp, rows=None, heads=None):
         cnt = raw[off:off + rows_t * 4].view(np.int32).reshape(w.B, n_qt)
         off = al(off + rows_t * 4)
         lst = raw[off:off + rows_t * n_kt * 4].view(np.int32).reshape(w.B, n_qt, n_kt)
+        off = al(off + rows_t * n_kt * 4)
+        wfull = raw[off:off + rows_t * n_kt].reshape(w.B, n_qt, n_kt)
         c2, n2, l2 = oracle.mod_tile_table(w.N, w.B, mmod, params.astype(np.float64))
         assert np.array_equal(cls, c2) and np.array_equal(cnt, n2) and np.array_equal(lst, l2)
+        # bit w of a tile's byte: its rows 32w .. 32w + 31 all in range and allowed (32-row
+        # blocks of the same pair-by-pair evaluation)
+        c32, _, _ = oracle.mod_tile_table(w.N, w.B, mmod, params.astype(np.float64), Br=32, Bc=BC)
+        full = np.zeros((w.B, n_qt * 8, n_kt), dtype=bool)
+        full[:, :c32.shape[1]] = c32 == 2
+        ref = (full.reshape(w.B, n_qt, 8, n_kt) * (1 << np.arange(8))[None, None, :, None]).sum(axis=2)
+        assert np.array_equal(wfull, ref.astype(np.uint8))
     o16, l16 = run(name, w, inp, params, False)
     assert torch.equal(o16.cpu(), o32.cpu().to(torch.bfloat16))
     assert torch.equal(l16.cpu(), l32.cpu())
