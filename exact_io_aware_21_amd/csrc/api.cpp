@@ -629,8 +629,12 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
   return ATTN_OK;
 }
 
-int attn_mod_create(const char *source, uint32_t flags, int d, attn_mod **out, char *log,
-                    size_t log_size) {
+}  // extern "C"
+
+namespace {
+
+int mod_create(const char *source, uint32_t flags, int d, attn_mod **out, char *log,
+               size_t log_size) {
   copy_log("", log, log_size);
   if (!out) return fail(ATTN_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
@@ -692,6 +696,20 @@ int attn_mod_create(const char *source, uint32_t flags, int d, attn_mod **out, c
   m->d = d;
   *out = m;
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_mod_create(const char *source, uint32_t flags, int d, attn_mod **out, char *log,
+                    size_t log_size) {
+  try {  // the C ABI does not throw: host allocation failures become an error code
+    return mod_create(source, flags, d, out, log, log_size);
+  } catch (...) {
+    if (out) *out = nullptr;
+    return fail(ATTN_ERR_COMPILE, "host memory exhausted while compiling the modification");
+  }
 }
 
 void attn_mod_destroy(attn_mod *m) {

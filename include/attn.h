@@ -1,6 +1,7 @@
 /*
- * attn.h -- C ABI of the MI355X (gfx950) FlashAttention library (libattn.so): the forward pass,
- * its backward pass, and decoding over a paged key/value cache.
+ * attn.h -- C ABI of the MI355X (gfx950) FlashAttention library (libattn.so): the forward pass
+ * (bf16, or FP8 scores with per-block scales), its backward pass, decoding over a paged
+ * key/value cache, and forward passes with runtime-compiled score and mask modifications.
  *
  * What it computes.  For every batch entry b and head h, with Q, K, V in R^{N x d}:
  *     O = softmax(S) V,   S_ij = modified score of query i and key j,
@@ -28,7 +29,9 @@
  *
  * Memory.  Every pointer is caller-owned device memory unless stated otherwise.  The library
  * allocates nothing on any call and keeps no per-call state; the only state it keeps is a
- * per-device cache of the architecture check.  All launches are asynchronous on `stream`
+ * per-device cache of the architecture check.  The exceptions are the modification objects:
+ * attn_mod_create allocates the compiled code in host memory, and the first attn_fwd_mod call
+ * on a device loads it there; attn_mod_destroy releases both.  All launches are asynchronous on `stream`
  * (a hipStream_t, NULL = the default stream); a kernel fault surfaces at the caller's next
  * synchronisation.  Entry points are reentrant; calls that share a workspace must not overlap.
  *
