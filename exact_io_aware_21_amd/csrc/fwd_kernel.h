@@ -413,11 +413,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   __syncthreads();
 
   // V-phase of tile t: score modifications, mask, online softmax, P_t in fp16.
-  auto vphase = [&](int kt) {
-    // Base-2 score scale of this tile; FP8: times s_k of the key tile (read-only here, written
-    // by the quantization kernel before this launch: a scalar load).
-    float c = cq;
-    if constexpr (FP8) c = cq * ((const_f32 *)a.sk)[(size_t)bh * a.n_kt + kt];
+  auto vphase = [&](int kt, float skt) {
+    // Base-2 score scale of this tile; FP8: times s_k of the key tile (skt, loaded ahead).
+    const float c = FP8 ? cq * skt : cq;
     // Register r of block blk is key kt*Bc + 32*blk + 16*(r/8) + 8*hf + r%8.
     const int kb = kt * kBc + 8 * hf;
     if constexpr (MOD != 0) {
@@ -486,53 +484,93 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
         }
       }
     }
-    // Tile row maximum: in-lane over 32 keys, then with the lane that shares the query.
-    float mx = -INFINITY;
+    // Probabilities against the running maximum m (base 2), which must keep every P <= 2^8
+    // (the range and precision of the fp16 P V operands): the lazy rescale with threshold 8.
+    // Unmodified scores (POS instances without a modification) skip the tile maximum in the
+    // common case: a lane's sum of its 32 probabilities bounds each of them, so while every sum
+    // is <= 2^8 the running m stands.  Otherwise, or for a row with no maximum yet that sees a
+    // finite score, the tile maximum is taken, m moves and the output is rescaled, and the
+    // probabilities are formed again.  Score modifications (ALiBi, soft-cap, user functions)
+    // move the maximum often, so those instances take the tile maximum first, every tile.
+    auto probs = [&](float m_use) -> float {
+      float psum[4];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+      for (int g = 0; g < 4; ++g) {
+        f32x8 pv;
+        float acc = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
-    mx = pair_max(mx);
-    const float m_tile = POS ? mx * c : mx;
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kTau)) {
-      keep_branch();
-      const float m_new = fmaxf(m_run, m_tile);
+        for (int e = 0; e < 8; ++e) {
+          const float x = s[g >> 1][8 * (g & 1) + e];
+          const float p = POS ? __builtin_amdgcn_exp2f(fmaf(x, c, -m_use))
+                              : __builtin_amdgcn_exp2f(x - m_use);
+          pv[e] = p;
+          acc += p;
+        }
+        psum[g] = acc;
+        pb[g] = __builtin_convertvector(pv, f16x8);
+      }
+      return (psum[0] + psum[1]) + (psum[2] + psum[3]);
+    };
+    auto lane_max = [&]() -> float {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
+      return mx;
+    };
+    auto rescale_to = [&](float m_new) {
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
       m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float psum[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x8 pv;
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = s[g >> 1][8 * (g & 1) + e];
-        const float p = POS ? __builtin_amdgcn_exp2f(fmaf(x, c, -m_use))
-                            : __builtin_amdgcn_exp2f(x - m_use);
-        pv[e] = p;
-        acc += p;
+    };
+    if constexpr (!(POS && MOD == 0)) {
+      const float mx = pair_max(lane_max());
+      const float m_tile = POS ? mx * c : mx;
+      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kTau)) {
+        keep_branch();
+        rescale_to(fmaxf(m_run, m_tile));
       }
-      psum[g] = acc;
-      pb[g] = __builtin_convertvector(pv, f16x8);
+      l_run += probs(m_run == -INFINITY ? 0.f : m_run);
+      return;
     }
-    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+    float lsum = probs(m_run == -INFINITY ? 0.f : m_run);
+    bool need = !(lsum <= kPmax);
+    if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
+      keep_branch();
+      need = need || (m_run == -INFINITY && lane_max() > -INFINITY);
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      keep_branch();
+      // Tile row maximum: in-lane over 32 keys, then with the lane that shares the query.
+      const float mx = pair_max(lane_max());
+      rescale_to(fmaxf(m_run, POS ? mx * c : mx));
+      lsum = probs(m_run == -INFINITY ? 0.f : m_run);
+    }
+    l_run += lsum;
   };
   // kt of tiles k - 1 .. k + 3 are kept in scalars; tile k + 4's is read one iteration ahead.
   // Past the last tile they are 0 (a valid tile: its data is staged but never used).
   int kt_prev = 0, kt_cur = T > 0 ? kt_of(0) : 0, kt_next = T > 1 ? kt_of(1) : 0;
   int kt_n2 = T > 2 ? kt_of(2) : 0, kt_n3 = T > 3 ? kt_of(3) : 0;
+  // FP8: the K scales of tiles k - 1 .. k + 1, each read (scalar load) an iteration before use.
+  auto sk_of = [&](int kt) -> float {
+    return FP8 ? ((const_f32 *)a.sk)[(size_t)bh * a.n_kt + kt] : 1.f;
+  };
+  float sk_prev = 1.f, sk_cur = sk_of(kt_cur), sk_next = sk_of(kt_next);
   auto advance = [&](int k) {
     const int kt_n4 = k + 4 < T ? kt_of(k + 4) : 0;
+    const float sk_n2 = sk_of(kt_n2);
     kt_prev = kt_cur;
     kt_cur = kt_next;
     kt_next = kt_n2;
     kt_n2 = kt_n3;
     kt_n3 = kt_n4;
+    sk_prev = sk_cur;
+    sk_cur = sk_next;
+    sk_next = sk_n2;
   };
   // Chunks in flight: stg[] holds those of K_{k+1} and V_k, written in iteration k; with
   // kStageAhead = 2, stg2[] those of K_{k+2} and V_{k+1}, fetched an iteration earlier still.
@@ -565,13 +603,13 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     for (int k = 0; k <= T; ++k) {
       mphase(k, stage(k));
       __syncthreads();
-      if (k < T) vphase(kt_cur);
+      if (k < T) vphase(kt_cur, sk_cur);
       advance(k);
       __syncthreads();
     }
   } else {
     for (int k = 0; k <= T; ++k) {
-      if (k >= 1) vphase(kt_prev);
+      if (k >= 1) vphase(kt_prev, sk_prev);
       __syncthreads();
       mphase(k, stage(k));
       advance(k);

@@ -22,6 +22,7 @@ constexpr float kLn2 = 0.69314718055994531f;
 // s_getreg operand for HW_ID.SIMD_ID: register 4, bit offset 4, 2 bits.
 constexpr int kHwRegSimdId = (4) | (4 << 6) | ((2 - 1) << 11);
 constexpr float kTau = 8.0f;
+constexpr float kPmax = 256.0f;  // 2^kTau: the largest probability the lazy rescale allows
 // Word 3 of a raw (unformatted, stride 0) buffer resource on gfx9-family parts: 32-bit data
 // format, no swizzle.  Loads past the resource's byte size return zero.
 constexpr int kBufferWord3 = 0x00020000;
