@@ -10,7 +10,7 @@
 // The N x N score matrix never leaves registers.
 //
 // gfx950 mapping (one workgroup = 8 wave64s = Br = 256 query rows, 32 per wave; the two waves
-// on each SIMD alternate between matrix-core and vector phases, see fwd_kernel):
+// on each SIMD alternate between matrix-core and vector phases, see fwd_body):
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K is the A operand
 //    read from LDS, Q^T the B operand held in VGPRs for the whole kernel.  In the 32x32 result
 //    each lane owns one query (lane % 32) and 16 keys, so a row maximum is an in-lane max plus a
@@ -27,15 +27,19 @@
 //    11 significant bits instead of bf16's 8.  With bf16 P the rounding of a dominant
 //    probability alone moves O by up to 2^-9 |v|, which exceeds 1e-2 for |v| near 8.
 //    Q K^T stays on bf16 operands, which are the exact input values.
-//  * K and V^T tiles are double-buffered in LDS and prefetched into VGPRs two phases ahead.  Each
-//    LDS row is padded by 16 bytes, so the 8 (or 16) lanes of one ds_read_b128 phase, which read
-//    the same column of 8 (16) consecutive rows, hit distinct banks, while every operand address
-//    stays lane base + compile-time offset (no per-read address arithmetic).
+//  * K and V^T tiles are double-buffered in LDS.  Each wave stages its share of the next tiles
+//    between the MFMAs of its own matrix-core phase, fetched one iteration ahead with buffer
+//    loads into registers and stored to the idle buffers: spread out, not a burst of every
+//    wave's loads and stores at a barrier.  Each LDS row is padded by 16 bytes, so the 8 (or 16)
+//    lanes of one ds_read_b128 phase, which read the same column of 8 (16) consecutive rows, hit
+//    distinct banks, while every operand address stays lane base + compile-time offset.
 //  * Scores are kept in base-2 units (scale * log2 e folded in), so each probability costs one
 //    v_exp_f32; L is converted back to natural log in the epilogue.
-//  * The running maximum is only moved when a tile's maximum exceeds it by more than 8 (base 2):
+//  * The running maximum is only moved when a tile's scores exceed it by more than 8 (base 2):
 //    the output and l are then rescaled, otherwise probabilities are formed against the older
-//    maximum and stay below 2^8.  Both are exact rewritings of the same sums.
+//    maximum and stay below 2^8.  Both are exact rewritings of the same sums.  Without score
+//    modifications the test is made on the probabilities' sum, so the common tile skips its
+//    row maximum altogether.
 //  * Fully masked tiles never reach the kernel: it walks the per-q-tile list of non-empty tiles
 //    from the block table, and evaluates the element mask only on partial tiles.
 //
