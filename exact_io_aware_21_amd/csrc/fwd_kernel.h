@@ -396,6 +396,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     }
   };
   auto mphase = [&](int t, auto item) {
+    // The matrix-core wave issues first: without this the older wave of each SIMD pair wins
+    // issue arbitration in both slots, and the younger one's M-phase ran ~25 % longer than the
+    // older one's (in-kernel timestamps; with the priority both take the same time).
+    __builtin_amdgcn_s_setprio(3);
     if constexpr (FP8)
       mphase_fp8(t, item);
     else
@@ -404,6 +408,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     // past the barrier into the (conditional) V-phase that reads them.
     const f32x16 s0 = s[0], s1 = s[1];
     __asm__ volatile("" ::"v"(s0), "v"(s1));
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Zero P and the V buffer read by the first M-phase (its P V step then adds exactly 0).
