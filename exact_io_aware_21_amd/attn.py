@@ -36,7 +36,8 @@ MASK_BITS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
 EXPORTS = ("attn_fwd", "attn_workspace_size", "attn_tile_shape", "attn_block_table",
            "attn_block_table_host", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
            "attn_decode_workspace_size", "attn_quantize_fp8", "attn_mod_create",
-           "attn_mod_destroy", "attn_mod_workspace_size", "attn_fwd_mod", "attn_strerror",
+           "attn_mod_destroy", "attn_mod_workspace_size", "attn_fwd_mod", "attn_fwd_mod_cached",
+           "attn_strerror",
            "attn_last_error")
 
 
@@ -97,6 +98,8 @@ def lib():
         L.attn_mod_workspace_size.restype = ctypes.c_size_t
         L.attn_fwd_mod.argtypes = [c_vp] * 6 + [c_int] * 3 + [c_f, c_vp, P, c_vp]
         L.attn_fwd_mod.restype = c_int
+        L.attn_fwd_mod_cached.argtypes = L.attn_fwd_mod.argtypes
+        L.attn_fwd_mod_cached.restype = c_int
         L.attn_strerror.argtypes = [c_int]
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_last_error.argtypes = []
@@ -388,10 +391,14 @@ class AttnMod:
         return torch.empty(n, dtype=torch.uint8, device=device)
 
     def fwd(self, q, k, v, o, lse, scale, mod_params=None, workspace=None, stream=None,
-            timing_events=None):
+            timing_events=None, cached_table=False):
         """attn_fwd_mod on torch tensors: q, k, v bf16 [B,H,N,d]; o bf16 or fp32; lse fp32
-        [B,H,N] or None; mod_params a device fp32 tensor or None."""
+        [B,H,N] or None; mod_params a device fp32 tensor or None.  cached_table=True calls
+        attn_fwd_mod_cached, which reuses the block table an earlier call left in `workspace`
+        (same mod, B, N and mod_params values)."""
         import torch
+        if cached_table and workspace is None:
+            raise ValueError("cached_table needs the workspace of an earlier call")
         B, H, N, d = q.shape
         for name, t in (("q", q), ("k", k), ("v", v)):
             if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != (B, H, N, d):
@@ -415,7 +422,7 @@ class AttnMod:
                 raise ValueError("timing events must have been recorded once before use")
             ev = (ctypes.c_void_p * 2)(timing_events[0].cuda_event, timing_events[1].cuda_event)
             p.timing_events = ctypes.cast(ev, ctypes.c_void_p)
-        _check(lib().attn_fwd_mod(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N,
-                                  float(scale), _ptr(mod_params), ctypes.byref(p),
-                                  _stream(stream)))
+        fn = lib().attn_fwd_mod_cached if cached_table else lib().attn_fwd_mod
+        _check(fn(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, float(scale),
+                  _ptr(mod_params), ctypes.byref(p), _stream(stream)))
         return o, lse

@@ -733,9 +733,13 @@ size_t attn_mod_workspace_size(const attn_mod *m, int B, int H, int N) {
   return mod_layout(s, (m->flags & ATTN_MODF_MASK) != 0).total;
 }
 
-int attn_fwd_mod(const attn_mod *mc, const void *q, const void *k, const void *v, void *o,
-                 float *lse, int B, int H, int N, float scale, const float *mod_params,
-                 const attn_params *params, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int fwd_mod(const attn_mod *mc, const void *q, const void *k, const void *v, void *o, float *lse,
+            int B, int H, int N, float scale, const float *mod_params,
+            const attn_params *params, void *stream, bool build_table) {
   attn_mod *m = const_cast<attn_mod *>(mc);
   if (!m) return fail(ATTN_ERR_INVALID_ARG, "mod is NULL");
   const int d = m->d;
@@ -787,7 +791,7 @@ int attn_fwd_mod(const attn_mod *mc, const void *q, const void *k, const void *v
   a.scale = scale;
   a.mod_params = mod_params;
   a.kind = ATTN_MASK_NONE;
-  if (mask) {
+  if (mask) {  // the block table: built here, or left by an earlier call (build_table false)
     attn::ModTableArgs t{};
     t.N = N;
     t.n_qt = s.n_qt;
@@ -798,10 +802,11 @@ int attn_fwd_mod(const attn_mod *mc, const void *q, const void *k, const void *v
     t.list = (int32_t *)(ws + wl.list);
     t.wfull = (uint8_t *)(ws + wl.wfull);
     void *targs[] = {&t};
-    if (hipModuleLaunchKernel(m->cls[dev], (unsigned)s.n_kt, (unsigned)(B * s.n_qt), 1, 256, 1,
-                              1, 0, st, targs, nullptr) != hipSuccess ||
-        hipModuleLaunchKernel(m->list[dev], (unsigned)(B * s.n_qt), 1, 1, 256, 1, 1, 0, st, targs,
-                              nullptr) != hipSuccess) {
+    if (build_table &&
+        (hipModuleLaunchKernel(m->cls[dev], (unsigned)s.n_kt, (unsigned)(B * s.n_qt), 1, 256, 1,
+                               1, 0, st, targs, nullptr) != hipSuccess ||
+         hipModuleLaunchKernel(m->list[dev], (unsigned)(B * s.n_qt), 1, 1, 256, 1, 1, 0, st,
+                               targs, nullptr) != hipSuccess)) {
       (void)hipGetLastError();
       return fail(ATTN_ERR_LAUNCH, "mask table kernel launch failed");
     }
@@ -823,6 +828,22 @@ int attn_fwd_mod(const attn_mod *mc, const void *q, const void *k, const void *v
   if (ev && hipEventRecord((hipEvent_t)ev[1], st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "timing event record failed");
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_mod(const attn_mod *m, const void *q, const void *k, const void *v, void *o,
+                 float *lse, int B, int H, int N, float scale, const float *mod_params,
+                 const attn_params *params, void *stream) {
+  return fwd_mod(m, q, k, v, o, lse, B, H, N, scale, mod_params, params, stream, true);
+}
+
+int attn_fwd_mod_cached(const attn_mod *m, const void *q, const void *k, const void *v, void *o,
+                        float *lse, int B, int H, int N, float scale, const float *mod_params,
+                        const attn_params *params, void *stream) {
+  return fwd_mod(m, q, k, v, o, lse, B, H, N, scale, mod_params, params, stream, false);
 }
 
 }  // extern "C"

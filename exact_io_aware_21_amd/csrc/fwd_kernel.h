@@ -207,10 +207,17 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     const size_t row = (size_t)bm * a.n_qt + qt;
     T = ((const_i32 *)a.cnt)[row];
     lst = (const_i32 *)a.list + row * a.n_kt;
+    // A modification's table may have been left by an earlier call (the caller vouches for it):
+    // clamp what is read from it so that any contents stay in bounds.
+    if constexpr ((MOD & kModMask) != 0) T = min(max(T, 0), a.n_kt);
   } else {
     T = a.n_kt;
   }
-  auto kt_of = [&](int t) -> int { return lst ? lst[t] : t; };
+  auto kt_of = [&](int t) -> int {
+    if (!lst) return t;
+    if constexpr ((MOD & kModMask) != 0) return min(max(lst[t], 0), a.n_kt - 1);
+    return lst[t];
+  };
 
   // Tile staging.  Per tile pair each thread moves NI 16-byte chunks: items 0 .. KLDN-1 are
   // chunks of the next K tile, items KLDN .. NI-1 chunks of the current V^T tile.  Loads are

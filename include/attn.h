@@ -285,6 +285,22 @@ int attn_fwd_mod(const attn_mod *m, const void *q, const void *k, const void *v,
                  float *lse, int B, int H, int N, float scale, const float *mod_params,
                  const attn_params *params, void *stream);
 
+/*
+ * attn_fwd_mod_cached -- attn_fwd_mod without the tile classification: it walks the block table
+ * an earlier attn_fwd_mod call left in the same workspace.  The table depends only on the mask,
+ * B, N and the values mod_params held when it was built (not on q, k, v, H or the score
+ * function), so a caller that repeats a masked forward pass with new inputs (every layer of a
+ * model, every training step) classifies once.  Arguments and errors as attn_fwd_mod; the
+ * caller guarantees that the last attn_fwd_mod call on this workspace used this mod, this B
+ * and N, and mod_params of the same values, and that nothing has written the workspace's table
+ * since.  Otherwise the table is stale: O and L follow that table (allowed tiles it classes
+ * empty are skipped, tiles it classes full are not masked), with no out-of-bounds access as
+ * long as B and N are those of the build.  Without a mask it is attn_fwd_mod.
+ */
+int attn_fwd_mod_cached(const attn_mod *m, const void *q, const void *k, const void *v, void *o,
+                        float *lse, int B, int H, int N, float scale, const float *mod_params,
+                        const attn_params *params, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

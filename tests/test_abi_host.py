@@ -395,12 +395,13 @@ def test_mod_compile_errors_are_reported(src, flags):
 
 
 def _call_fwd_mod(m, q=16, k=16, v=16, o=16, lse=None, B=1, H=1, N=64, scale=0.125, mp=None,
-                  params="default"):
+                  params="default", cached=False):
     p = attn.attn_params()
     p.workspace = 256
     p.workspace_bytes = 1 << 40
     pp = ctypes.byref(p) if params == "default" else params
-    return attn.lib().attn_fwd_mod(m, q, k, v, o, lse, B, H, N, scale, mp, pp, None)
+    fn = attn.lib().attn_fwd_mod_cached if cached else attn.lib().attn_fwd_mod
+    return fn(m, q, k, v, o, lse, B, H, N, scale, mp, pp, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -413,18 +414,29 @@ def _call_fwd_mod(m, q=16, k=16, v=16, o=16, lse=None, B=1, H=1, N=64, scale=0.1
     ({"params": None}, attn.ATTN_ERR_INVALID_ARG),
     ({"B": 300, "N": 1 << 16}, attn.ATTN_ERR_INVALID_ARG),
 ])
-def test_fwd_mod_rejects_invalid_arguments(alibi_causal_mod, kw, code):
-    assert _call_fwd_mod(alibi_causal_mod._h, **kw) == code
+@pytest.mark.parametrize("cached", [False, True], ids=["build", "cached"])
+def test_fwd_mod_rejects_invalid_arguments(alibi_causal_mod, kw, code, cached):
+    assert _call_fwd_mod(alibi_causal_mod._h, cached=cached, **kw) == code
     assert attn.lib().attn_last_error() != b""
 
 
-def test_fwd_mod_rejects_null_mod_and_small_workspace(alibi_causal_mod):
-    assert _call_fwd_mod(None) == attn.ATTN_ERR_INVALID_ARG
+@pytest.mark.parametrize("cached", [False, True], ids=["build", "cached"])
+def test_fwd_mod_rejects_null_mod_and_small_workspace(alibi_causal_mod, cached):
+    assert _call_fwd_mod(None, cached=cached) == attn.ATTN_ERR_INVALID_ARG
     p = attn.attn_params()
     p.workspace, p.workspace_bytes = 256, 100
-    assert _call_fwd_mod(alibi_causal_mod._h, params=ctypes.byref(p)) == attn.ATTN_ERR_WORKSPACE
+    assert _call_fwd_mod(alibi_causal_mod._h, params=ctypes.byref(p),
+                         cached=cached) == attn.ATTN_ERR_WORKSPACE
 
 
 @pytest.mark.skipif(_gpu_present(), reason="only meaningful on a host without a GPU")
-def test_fwd_mod_valid_call_without_gpu_reports_unsupported_device(alibi_causal_mod):
-    assert _call_fwd_mod(alibi_causal_mod._h) == attn.ATTN_ERR_UNSUPPORTED_DEVICE
+@pytest.mark.parametrize("cached", [False, True], ids=["build", "cached"])
+def test_fwd_mod_valid_call_without_gpu_reports_unsupported_device(alibi_causal_mod, cached):
+    assert _call_fwd_mod(alibi_causal_mod._h, cached=cached) == attn.ATTN_ERR_UNSUPPORTED_DEVICE
+
+
+def test_fwd_mod_cached_binding_needs_a_workspace(alibi_causal_mod):
+    import torch
+    x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        alibi_causal_mod.fwd(x, x, x, x.clone(), None, 0.125, cached_table=True)

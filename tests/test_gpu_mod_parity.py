@@ -97,17 +97,37 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
 
 
-def run(name, w, inp, params, out_f32, workspace=None):
+def run(name, w, inp, params, out_f32, workspace=None, cached=False):
     m = compiled(name, w.d)
     o = torch.full((w.B, w.H, w.N, w.d), float("nan"), device=DEV,
                    dtype=torch.float32 if out_f32 else torch.bfloat16)
     lse = torch.full((w.B, w.H, w.N), float("nan"), device=DEV)
     p = torch.from_numpy(params).to(DEV)
-    print(f"[gpu-mod] {name} B={w.B} H={w.H} N={w.N} d={w.d} out_f32={out_f32}", flush=True)
+    print(f"[gpu-mod] {name} B={w.B} H={w.H} N={w.N} d={w.d} out_f32={out_f32} cached={cached}",
+          flush=True)
     m.fwd(dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]), o, lse, inp["scale"], p,
-          workspace=workspace)
+          workspace=workspace, cached_table=cached)
     torch.cuda.synchronize()
     return o, lse
+
+
+def table_of(ws, w):
+    """(cls, cnt, lst, wfull) of the block table in a modification's workspace: after the
+    key-transposed V, 256-byte aligned regions cls int8 [B][n_qt][n_kt], cnt int32 [B][n_qt],
+    lst int32 [B][n_qt][n_kt], wfull uint8 [B][n_qt][n_kt]."""
+    n_qt, n_kt = -(-w.N // BR), -(-w.N // BC)
+    al = lambda x: (x + 255) // 256 * 256
+    off = al(w.B * w.H * w.d * n_kt * BC * 2)
+    rows_t = w.B * n_qt
+    raw = ws.cpu().numpy()
+    cls = raw[off:off + rows_t * n_kt].view(np.int8).reshape(w.B, n_qt, n_kt)
+    off = al(off + rows_t * n_kt)
+    cnt = raw[off:off + rows_t * 4].view(np.int32).reshape(w.B, n_qt)
+    off = al(off + rows_t * 4)
+    lst = raw[off:off + rows_t * n_kt * 4].view(np.int32).reshape(w.B, n_qt, n_kt)
+    off = al(off + rows_t * n_kt * 4)
+    wfull = raw[off:off + rows_t * n_kt].reshape(w.B, n_qt, n_kt)
+    return cls, cnt, lst, wfull
 
 
 def check(name, w, inp, rows=None, heads=None):
@@ -116,18 +136,8 @@ def check(name, w, inp, rows=None, heads=None):
     ws = compiled(name, w.d).alloc_workspace(w.B, w.H, w.N, DEV)
     o32, l32 = run(name, w, inp, params, True, ws)
     if flags & MASK:  # the block table the call left in its workspace
-        n_qt, n_kt = -(-w.N // BR), -(-w.N // BC)
-        al = lambda x: (x + 255) // 256 * 256
-        off = al(w.B * w.H * w.d * n_kt * BC * 2)
-        rows_t = w.B * n_qt
-        raw = ws.cpu().numpy()
-        cls = raw[off:off + rows_t * n_kt].view(np.int8).reshape(w.B, n_qt, n_kt)
-        off = al(off + rows_t * n_kt)
-        cnt = raw[off:off + rows_t * 4].view(np.int32).reshape(w.B, n_qt)
-        off = al(off + rows_t * 4)
-        lst = raw[off:off + rows_t * n_kt * 4].view(np.int32).reshape(w.B, n_qt, n_kt)
-        off = al(off + rows_t * n_kt * 4)
-        wfull = raw[off:off + rows_t * n_kt].reshape(w.B, n_qt, n_kt)
+        cls, cnt, lst, wfull = table_of(ws, w)
+        n_qt, n_kt = cls.shape[1:]
         c2, n2, l2 = oracle.mod_tile_table(w.N, w.B, mmod, params.astype(np.float64))
         assert np.array_equal(cls, c2) and np.array_equal(cnt, n2) and np.array_equal(lst, l2)
         # bit w of a tile's byte: its rows 32w .. 32w + 31 all in range and allowed (32-row
@@ -211,3 +221,25 @@ def test_mod_deterministic():
     a, la = run("alibi_causal", w, inp, params, True)
     b, lb = run("alibi_causal", w, inp, params, True)
     assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_mod_cached_table_reuse():
+    """attn_fwd_mod_cached on new inputs with the table an earlier attn_fwd_mod call left in the
+    workspace: the same O and L, bit for bit, as a call that builds its own table (and within
+    the oracle's tolerance), and the table untouched by the cached call."""
+    name = "prefix_lm"
+    w = inputs.Workload("mod_cache", B=2, H=2, N=900, d=128, seed=2200)
+    params = MODS[name][4](w.H)
+    ws = compiled(name, w.d).alloc_workspace(w.B, w.H, w.N, DEV)
+    run(name, w, inputs.make_inputs(w), params, True, ws)           # builds the table
+    before = [t.copy() for t in table_of(ws, w)]
+    w2 = inputs.Workload("mod_cache2", B=2, H=2, N=900, d=128, seed=2201, sigma=2.0)
+    inp2 = inputs.make_inputs(w2)
+    for out_f32 in (True, False):
+        oc, lc = run(name, w2, inp2, params, out_f32, ws, cached=True)
+        ob, lb = run(name, w2, inp2, params, out_f32)                # builds its own
+        assert torch.equal(oc, ob) and torch.equal(lc, lb)
+    # other parameter values: the cached call neither reads nor rewrites the table from them
+    run(name, w2, inp2, np.array([0.0], dtype=np.float32), True, ws, cached=True)
+    assert all(np.array_equal(a, b) for a, b in zip(before, table_of(ws, w)))
+    check(name, w2, inp2)
