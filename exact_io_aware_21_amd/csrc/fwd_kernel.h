@@ -100,8 +100,20 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   static_assert(MOD == 0 || (POS && !ALIBI && !SOFTCAP && !FP8),
                 "modification instances take natural-units scores on the POS path");
   static_assert(kBc * KP8 <= kBc * pitch(D) * 2, "FP8 K tile must fit the K buffer");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBc * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VP];
+  // LDS tiles: three K and three V^T buffers, each an array of its own so that every access of
+  // the bf16 instances names its buffer statically (the compiler then tracks the buffer-to-LDS
+  // copies in flight per buffer and waits only where a read needs one).  Each buffer ends in a
+  // spare 1 KB row for the copy instructions a wave issues beyond its tile's share, which read
+  // nothing and write zeros there.  FP8 instances use buffers 0 and 1.
+  constexpr int SPK = KP / 8, SPV = VP / 8;                // 16-byte slots per LDS row
+  constexpr int NJK = kBc * SPK / 64, NJV = D * SPV / 64;  // copy instructions per tile
+  static_assert(kBc * SPK % 64 == 0 && D * SPV % 64 == 0, "tiles must fill whole copy rows");
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[(NJK + 1) * 512];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[(NJK + 1) * 512];
+  __shared__ __attribute__((aligned(16))) uint16_t sK2[(NJK + 1) * 512];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[(NJV + 1) * 512];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[(NJV + 1) * 512];
+  __shared__ __attribute__((aligned(16))) uint16_t sV2[(NJV + 1) * 512];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   // Phase group: of the two waves the dispatcher placed on a SIMD, the lower-numbered one is
@@ -260,9 +272,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   };
   auto store_item = [&](int j, int kb, int vb, u32x4 x) {
     if (j < KLDN)
-      *(u32x4 *)((char *)sK[kb] + klo + j * KRU * KPB) = x;
+      *(u32x4 *)((char *)(kb ? sK1 : sK0) + klo + j * KRU * KPB) = x;
     else
-      *(u32x4 *)((char *)sV[vb] + vlo + (j - KLDN) * VRU * VP * 2) = x;
+      *(u32x4 *)((char *)(vb ? sV1 : sV0) + vlo + (j - KLDN) * VRU * VP * 2) = x;
   };
 
 
@@ -282,11 +294,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   // Staging item j (`item(j)`: the LDS store of chunk j, then the buffer load of chunk j of the
   // next tile pair into the same registers) goes after MFMA step 1 + j * NST / NI.
   constexpr int kDepth = 4;
-  auto mphase_bf16 = [&](int t, auto item) {
+  // Items are either register staging (an LDS store and a buffer load) or, with DMA, one
+  // buffer-to-LDS copy instruction.
+  auto mphase_bf16 = [&](const uint16_t *kl, const uint16_t *vl, auto item, auto nitc,
+                         auto dmac) {
     constexpr int NPV = 4 * NDB;
     constexpr int NST = NPV + 2 * NKS;
-    const uint16_t *vbuf = &sV[(t - 1) & 1][l32 * VP + hf * 8];
-    const uint16_t *kbuf = &sK[t & 1][l32 * KP + hf * 8];
+    constexpr int NI = decltype(nitc)::value;
+    constexpr bool DMA = decltype(dmac)::value;
+    const uint16_t *vbuf = vl + l32 * VP + hf * 8;
+    const uint16_t *kbuf = kl + l32 * KP + hf * 8;
     auto frag = [&](int i) -> u32x4 {
       if (i < NPV) {
         const int kk = i / NDB, db = i % NDB;
@@ -324,7 +341,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
 #pragma unroll
       for (int j = 0; j < NI; ++j)
         if (i == 1 + j * NST / NI) {
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          if constexpr (!DMA) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
       if (i + kDepth < NST) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -338,8 +355,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     constexpr int NSS = 2 * NKS8;      // score MFMAs
     constexpr int NST = NPV + NSS;     // MFMAs
     constexpr int NR = NPV + 2 * NSS;  // LDS reads
-    const uint16_t *vbuf = &sV[(t - 1) & 1][l32 * VP + hf * 8];
-    const uint8_t *kbuf = (const uint8_t *)sK[t & 1] + l32 * KP8 + hf * 32;
+    const uint16_t *vbuf = (((t - 1) & 1) ? sV1 : sV0) + l32 * VP + hf * 8;
+    const uint8_t *kbuf = (const uint8_t *)((t & 1) ? sK1 : sK0) + l32 * KP8 + hf * 32;
     auto frag = [&](int r) -> u32x4 {
       if (r < NPV) {
         const int kk = r / NDB, db = r % NDB;
@@ -402,15 +419,12 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       if (r0 + 1 + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  auto mphase = [&](int t, auto item) {
+  auto mphase = [&](auto body) {
     // The matrix-core wave issues first: without this the older wave of each SIMD pair wins
     // issue arbitration in both slots, and the younger one's M-phase ran ~25 % longer than the
     // older one's (in-kernel timestamps; with the priority both take the same time).
     __builtin_amdgcn_s_setprio(3);
-    if constexpr (FP8)
-      mphase_fp8(t, item);
-    else
-      mphase_bf16(t, item);
+    body();
     // Keep the score MFMAs in this slot: without a use here the compiler sinks the last ones
     // past the barrier into the (conditional) V-phase that reads them.
     const f32x16 s0 = s[0], s1 = s[1];
@@ -418,15 +432,19 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // Zero P and the V buffer read by the first M-phase (its P V step then adds exactly 0).
+  // Zero P and the V buffer read by the first M-phase (its P V step then adds exactly 0):
+  // buffer 1 of the two FP8 ones, buffer 2 (= -1 mod 3) of the three bf16 ones.
 #pragma unroll
   for (int g = 0; g < 4; ++g) pb[g] = f16x8{};
-  for (int i = tid; i < D * VP / 8; i += NT) *(u32x4 *)&sV[1][i * 8] = u32x4{0u, 0u, 0u, 0u};
-  if (T > 0) {
+  for (int i = tid; i < D * VP / 8; i += NT)
+    *(u32x4 *)((FP8 ? sV1 : sV2) + i * 8) = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (FP8) {
+    if (T > 0) {
 #pragma unroll
-    for (int j = 0; j < KLDN; ++j) store_item(j, 0, 0, fetch_item(j, kt_of(0), 0));
+      for (int j = 0; j < KLDN; ++j) store_item(j, 0, 0, fetch_item(j, kt_of(0), 0));
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // V-phase of tile t: score modifications, mask, online softmax, P_t in fp16.
   auto vphase = [&](int kt, float skt) {
@@ -588,49 +606,139 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     sk_cur = sk_next;
     sk_next = sk_n2;
   };
-  // Chunks in flight: stg[] holds those of K_{k+1} and V_k, written in iteration k; with
-  // kStageAhead = 2, stg2[] those of K_{k+2} and V_{k+1}, fetched an iteration earlier still.
-  u32x4 stg[NI], stg2[NI];
+  if constexpr (FP8) {
+    // Register staging through two LDS buffers.  Chunks in flight: stg[] holds those of K_{k+1}
+    // and V_k, written in iteration k; with kStageAhead = 2, stg2[] those of K_{k+2} and
+    // V_{k+1}, fetched an iteration earlier still.
+    u32x4 stg[NI], stg2[NI];
 #pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    stg[j] = fetch_item(j, kt_next, kt_cur);
-    if constexpr (kStageAhead == 2) stg2[j] = fetch_item(j, kt_n2, kt_next);
-  }
+    for (int j = 0; j < NI; ++j) {
+      stg[j] = fetch_item(j, kt_next, kt_cur);
+      if constexpr (kStageAhead == 2) stg2[j] = fetch_item(j, kt_n2, kt_next);
+    }
 
-  // Two slots per iteration k.  Slot A: group 0 runs M-phase k, group 1 V-phase k-1.  Slot B:
-  // group 0 runs V-phase k, group 1 M-phase k.  K_k and V_{k-1} are read in both slots.  Each
-  // wave stages its chunks inside its own M-phase, between the MFMAs: it writes the chunks of
-  // K_{k+1} and V_k (fetched one iteration earlier) to the idle buffers, which no step of
-  // iteration k reads, and fetches those of K_{k+2} and V_{k+1}.  Both groups execute the same
-  // 2T + 2 barriers.  In M-phase 0, P = 0 against a zeroed V buffer adds nothing; in M-phase T
-  // the score product reads a stale K buffer and its result is never used.
-  auto stage = [&](int k) {
-    return [&, k](int j) {
-      store_item(j, (k + 1) & 1, k & 1, stg[j]);
-      if constexpr (kStageAhead == 2) {
-        stg[j] = stg2[j];
-        stg2[j] = fetch_item(j, kt_n3, kt_n2);
-      } else {
-        stg[j] = fetch_item(j, kt_n2, kt_next);
-      }
+    // Two slots per iteration k.  Slot A: group 0 runs M-phase k, group 1 V-phase k-1.  Slot B:
+    // group 0 runs V-phase k, group 1 M-phase k.  K_k and V_{k-1} are read in both slots.  Each
+    // wave stages its chunks inside its own M-phase, between the MFMAs: it writes the chunks of
+    // K_{k+1} and V_k (fetched one iteration earlier) to the idle buffers, which no step of
+    // iteration k reads, and fetches those of K_{k+2} and V_{k+1}.  Both groups execute the
+    // same 2T + 2 barriers.  In M-phase 0, P = 0 against a zeroed V buffer adds nothing; in
+    // M-phase T the score product reads a stale K buffer and its result is never used.
+    auto stage = [&](int k) {
+      return [&, k](int j) {
+        store_item(j, (k + 1) & 1, k & 1, stg[j]);
+        if constexpr (kStageAhead == 2) {
+          stg[j] = stg2[j];
+          stg2[j] = fetch_item(j, kt_n3, kt_n2);
+        } else {
+          stg[j] = fetch_item(j, kt_n2, kt_next);
+        }
+      };
     };
-  };
-  if (grp == 0) {
-    for (int k = 0; k <= T; ++k) {
-      mphase(k, stage(k));
-      __syncthreads();
-      if (k < T) vphase(kt_cur, sk_cur);
-      advance(k);
-      __syncthreads();
+    if (grp == 0) {
+      for (int k = 0; k <= T; ++k) {
+        mphase([&] { mphase_fp8(k, stage(k)); });
+        __syncthreads();
+        if (k < T) vphase(kt_cur, sk_cur);
+        advance(k);
+        __syncthreads();
+      }
+    } else {
+      for (int k = 0; k <= T; ++k) {
+        if (k >= 1) vphase(kt_prev, sk_prev);
+        __syncthreads();
+        mphase([&] { mphase_fp8(k, stage(k)); });
+        advance(k);
+        __syncthreads();
+      }
     }
   } else {
-    for (int k = 0; k <= T; ++k) {
-      if (k >= 1) vphase(kt_prev, sk_prev);
-      __syncthreads();
-      mphase(k, stage(k));
-      advance(k);
-      __syncthreads();
+    // Buffer-to-LDS copies through three LDS buffers: K_t in buffer t mod 3, V^T_t in buffer
+    // t mod 3.  In iteration k every wave issues, between the MFMAs of its own M-phase, its
+    // share of the copies of K_{k+2} and V^T_{k+1}, into the buffers last read in iteration
+    // k - 1; before the barrier that ends iteration k + 1 it waits for them (vmcnt counts the
+    // copies in issue order), so iteration k + 2 finds both tiles whole.  The copies are in
+    // flight for a whole iteration and nothing else waits for them: the barriers inside the
+    // loop are bare s_barrier instructions (a workgroup fence would wait for every copy).
+    //
+    // A tile row is SPK (K) or SPV (V^T) 16-byte slots, the last one padding; copy instruction
+    // g of a tile fills slots 64 g .. 64 g + 63.  Wave w issues instructions w, w + 8, ... of
+    // each tile; one past the tile's count reads nothing and writes zeros to the spare row.
+    // Padding slots read the row's last chunk again (the same cache line as their neighbour).
+    constexpr int RK = (NJK + 7) / 8, RV = (NJV + 7) / 8, NDMA = RK + RV;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int dvo[NDMA];
+#pragma unroll
+    for (int r = 0; r < RK; ++r) {
+      const int sl = min(wv + 8 * r, NJK - 1) * 64 + lane, row = sl / SPK, ch = sl % SPK;
+      // LDS row `row` holds key pi(row) (pi is an involution)
+      dvo[r] = pi_key(row) * KROW + min(ch, KCH - 1) * 16;
     }
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+      const int sl = min(wv + 8 * r, NJV - 1) * 64 + lane, row = sl / SPV, ch = sl % SPV;
+      dvo[RK + r] = row * a.Npad * 2 + min(ch, VCH - 1) * 16;  // < 2^31: row < D, Npad <= 2^24
+    }
+    auto copy_item = [&](int r, uint16_t *kw, uint16_t *vw, int ktk, int ktv) {
+      if (r < RK) {
+        const int g = wv + 8 * r;
+        const int rows = min(kBc, N - ktk * kBc);
+        copy16_to_lds(kbytes + (size_t)ktk * kBc * KROW, g < NJK ? (uint32_t)(rows * KROW) : 0u,
+                      dvo[r], kw + min(g, NJK) * 512);
+      } else {
+        const int g = wv + 8 * (r - RK);
+        const size_t left = ((size_t)D * a.Npad - (size_t)ktv * kBc) * 2;
+        const uint32_t vbytes = (uint32_t)(left < 0xFFFFFFFFull ? left : 0xFFFFFFFFull);
+        copy16_to_lds(vbase + (size_t)ktv * kBc, g < NJV ? vbytes : 0u, dvo[r],
+                      vw + min(g, NJV) * 512);
+      }
+    };
+    // K_0, K_1 and V^T_0 before the loop.
+#pragma unroll
+    for (int r = 0; r < NDMA; ++r) copy_item(r, sK0, sV0, kt_cur, kt_cur);
+#pragma unroll
+    for (int r = 0; r < RK; ++r) copy_item(r, sK1, sV0, kt_next, kt_cur);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // Iteration k with B = k mod 3 and phase group G, every buffer named statically.
+    auto iteration = [&](int k, auto bc, auto gc) {
+      constexpr int B = decltype(bc)::value, G = decltype(gc)::value;
+      constexpr int B1 = (B + 1) % 3, B2 = (B + 2) % 3;
+      uint16_t *kr = B == 0 ? sK0 : B == 1 ? sK1 : sK2;      // K_k
+      uint16_t *vr = B2 == 0 ? sV0 : B2 == 1 ? sV1 : sV2;    // V^T_{k-1}
+      uint16_t *kw = B2 == 0 ? sK0 : B2 == 1 ? sK1 : sK2;    // K_{k+2}
+      uint16_t *vw = B1 == 0 ? sV0 : B1 == 1 ? sV1 : sV2;    // V^T_{k+1}
+      auto item = [&](int r) { copy_item(r, kw, vw, kt_n2, kt_next); };
+      auto mp = [&] { mphase_bf16(kr, vr, item, IntC<NDMA>{}, IntC<1>{}); };
+      if constexpr (G == 0) {
+        mphase(mp);
+        __builtin_amdgcn_s_barrier();
+        if (k < T) vphase(kt_cur, sk_cur);
+        advance(k);
+      } else {
+        if (k >= 1) vphase(kt_prev, sk_prev);
+        __builtin_amdgcn_s_barrier();
+        mphase(mp);
+        advance(k);
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));
+      __builtin_amdgcn_s_barrier();
+    };
+    auto run = [&](auto gc) {
+      for (int k = 0;; k += 3) {
+        iteration(k, IntC<0>{}, gc);
+        if (k >= T) break;
+        iteration(k + 1, IntC<1>{}, gc);
+        if (k + 1 >= T) break;
+        iteration(k + 2, IntC<2>{}, gc);
+        if (k + 2 >= T) break;
+      }
+    };
+    if (grp == 0)
+      run(IntC<0>{});
+    else
+      run(IntC<1>{});
   }
 
   // Epilogue: O = O / l, L = (m + log2 l) * ln 2.

@@ -101,6 +101,21 @@ __device__ __forceinline__ u32x4 buffer_load16(const void *base, uint32_t bytes,
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// One buffer-to-LDS copy instruction: the 64 lanes move 16 bytes each, from byte offset voff
+// (per lane) of a buffer of `bytes` bytes at base, into the 1 KB at lds (wave-uniform), lane l to
+// bytes 16 l .. 16 l + 15.  Offsets past `bytes` read as zero (bytes = 0: the instruction reads
+// nothing and writes zeros).  Completion is counted by vmcnt, like a vector load.
+__device__ __forceinline__ void copy16_to_lds(const void *base, uint32_t bytes, int voff,
+                                              uint16_t *lds) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  const auto r = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)bytes, kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of this wave are
+// outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // bf16 bits -> fp16 bits; exact for |x| in [2^-14, 65504], saturating beyond (NaN stays NaN).
 __device__ __forceinline__ uint32_t bf16_to_f16_bits(uint32_t b) {
   float f = __uint_as_float(b << 16);
