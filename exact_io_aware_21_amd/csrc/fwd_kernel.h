@@ -100,20 +100,20 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   static_assert(MOD == 0 || (POS && !ALIBI && !SOFTCAP && !FP8),
                 "modification instances take natural-units scores on the POS path");
   static_assert(kBc * KP8 <= kBc * pitch(D) * 2, "FP8 K tile must fit the K buffer");
-  // LDS tiles: three K and three V^T buffers, each an array of its own so that every access of
-  // the bf16 instances names its buffer statically (the compiler then tracks the buffer-to-LDS
-  // copies in flight per buffer and waits only where a read needs one).  Each buffer ends in a
-  // spare 1 KB row for the copy instructions a wave issues beyond its tile's share, which read
-  // nothing and write zeros there.  FP8 instances use buffers 0 and 1.
+  // LDS tiles: three buffers, each an array of its own holding a K tile, then a V^T tile, then
+  // a spare 1 KB row, so that every access of the bf16 instances names its buffer statically
+  // (the compiler then tracks the buffer-to-LDS copies in flight per buffer and waits only
+  // where a read needs one).  The spare row takes the copy instructions a wave issues beyond
+  // the tiles' share, which read nothing and write zeros.  FP8 instances use buffers 0 and 1.
   constexpr int SPK = KP / 8, SPV = VP / 8;                // 16-byte slots per LDS row
   constexpr int NJK = kBc * SPK / 64, NJV = D * SPV / 64;  // copy instructions per tile
+  constexpr int NJ = NJK + NJV;
   static_assert(kBc * SPK % 64 == 0 && D * SPV % 64 == 0, "tiles must fill whole copy rows");
-  __shared__ __attribute__((aligned(16))) uint16_t sK0[(NJK + 1) * 512];
-  __shared__ __attribute__((aligned(16))) uint16_t sK1[(NJK + 1) * 512];
-  __shared__ __attribute__((aligned(16))) uint16_t sK2[(NJK + 1) * 512];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[(NJV + 1) * 512];
-  __shared__ __attribute__((aligned(16))) uint16_t sV1[(NJV + 1) * 512];
-  __shared__ __attribute__((aligned(16))) uint16_t sV2[(NJV + 1) * 512];
+  __shared__ __attribute__((aligned(16))) uint16_t sB0[(NJ + 1) * 512];
+  __shared__ __attribute__((aligned(16))) uint16_t sB1[(NJ + 1) * 512];
+  __shared__ __attribute__((aligned(16))) uint16_t sB2[(NJ + 1) * 512];
+  uint16_t *const sK0 = sB0, *const sK1 = sB1;
+  uint16_t *const sV0 = sB0 + NJK * 512, *const sV1 = sB1 + NJK * 512;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   // Phase group: of the two waves the dispatcher placed on a SIMD, the lower-numbered one is
@@ -432,13 +432,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // Zero P and the V buffer read by the first M-phase (its P V step then adds exactly 0):
-  // buffer 1 of the two FP8 ones, buffer 2 (= -1 mod 3) of the three bf16 ones.
+  // Zero P and the V buffer read by the first M-phase (its P V step then adds exactly 0).
 #pragma unroll
   for (int g = 0; g < 4; ++g) pb[g] = f16x8{};
-  for (int i = tid; i < D * VP / 8; i += NT)
-    *(u32x4 *)((FP8 ? sV1 : sV2) + i * 8) = u32x4{0u, 0u, 0u, 0u};
   if constexpr (FP8) {
+    for (int i = tid; i < D * VP / 8; i += NT) *(u32x4 *)(sV1 + i * 8) = u32x4{0u, 0u, 0u, 0u};
     if (T > 0) {
 #pragma unroll
       for (int j = 0; j < KLDN; ++j) store_item(j, 0, 0, fetch_item(j, kt_of(0), 0));
@@ -653,64 +651,64 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       }
     }
   } else {
-    // Buffer-to-LDS copies through three LDS buffers: K_t in buffer t mod 3, V^T_t in buffer
-    // t mod 3.  In iteration k every wave issues, between the MFMAs of its own M-phase, its
-    // share of the copies of K_{k+2} and V^T_{k+1}, into the buffers last read in iteration
-    // k - 1; before the barrier that ends iteration k + 1 it waits for them (vmcnt counts the
-    // copies in issue order), so iteration k + 2 finds both tiles whole.  The copies are in
-    // flight for a whole iteration and nothing else waits for them: the barriers inside the
-    // loop are bare s_barrier instructions (a workgroup fence would wait for every copy).
+    // Buffer-to-LDS copies through three LDS buffers: buffer t mod 3 holds the pair
+    // (K_t, V^T_{t-1}), which is what the M-phase of iteration t reads.  In iteration k every
+    // wave issues, between the MFMAs of its own M-phase, its share of the copies of pair k + 2
+    // (K_{k+2}, V^T_{k+1}) into the buffer last read in iteration k - 1; before the barrier that
+    // ends iteration k + 1 it waits for them (vmcnt counts the copies in issue order), so
+    // iteration k + 2 finds the pair whole.  The copies are in flight for a whole iteration and
+    // nothing else waits for them: the barriers inside the loop are bare s_barrier
+    // instructions (a workgroup fence would wait for every copy).
     //
     // A tile row is SPK (K) or SPV (V^T) 16-byte slots, the last one padding; copy instruction
-    // g of a tile fills slots 64 g .. 64 g + 63.  Wave w issues instructions w, w + 8, ... of
-    // each tile; one past the tile's count reads nothing and writes zeros to the spare row.
-    // Padding slots read the row's last chunk again (the same cache line as their neighbour).
-    constexpr int RK = (NJK + 7) / 8, RV = (NJV + 7) / 8, NDMA = RK + RV;
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    // g of a pair fills slots 64 g .. 64 g + 63 of its buffer (K tile first).  Wave w issues
+    // instructions w, w + 8, ...; one past the pair's count reads nothing and writes zeros to
+    // the spare row.  Padding slots read the row's last chunk again (the same cache line as
+    // their neighbour).
+    constexpr int NDMA = (NJ + 7) / 8;
+    const int wv = __builtin_amdgcn_readfirstlane(wave) & 7;  // the range lets most items resolve
     int dvo[NDMA];
 #pragma unroll
-    for (int r = 0; r < RK; ++r) {
-      const int sl = min(wv + 8 * r, NJK - 1) * 64 + lane, row = sl / SPK, ch = sl % SPK;
-      // LDS row `row` holds key pi(row) (pi is an involution)
-      dvo[r] = pi_key(row) * KROW + min(ch, KCH - 1) * 16;
-    }
-#pragma unroll
-    for (int r = 0; r < RV; ++r) {
-      const int sl = min(wv + 8 * r, NJV - 1) * 64 + lane, row = sl / SPV, ch = sl % SPV;
-      dvo[RK + r] = row * a.Npad * 2 + min(ch, VCH - 1) * 16;  // < 2^31: row < D, Npad <= 2^24
-    }
-    auto copy_item = [&](int r, uint16_t *kw, uint16_t *vw, int ktk, int ktv) {
-      if (r < RK) {
-        const int g = wv + 8 * r;
-        const int rows = min(kBc, N - ktk * kBc);
-        copy16_to_lds(kbytes + (size_t)ktk * kBc * KROW, g < NJK ? (uint32_t)(rows * KROW) : 0u,
-                      dvo[r], kw + min(g, NJK) * 512);
+    for (int r = 0; r < NDMA; ++r) {
+      const int g = min(wv + 8 * r, NJ - 1);
+      if (g < NJK) {
+        const int sl = g * 64 + lane, row = sl / SPK, ch = sl % SPK;
+        // LDS row `row` holds key pi(row) (pi is an involution)
+        dvo[r] = pi_key(row) * KROW + min(ch, KCH - 1) * 16;
       } else {
-        const int g = wv + 8 * (r - RK);
-        const size_t left = ((size_t)D * a.Npad - (size_t)ktv * kBc) * 2;
-        const uint32_t vbytes = (uint32_t)(left < 0xFFFFFFFFull ? left : 0xFFFFFFFFull);
-        copy16_to_lds(vbase + (size_t)ktv * kBc, g < NJV ? vbytes : 0u, dvo[r],
-                      vw + min(g, NJV) * 512);
+        const int sl = (g - NJK) * 64 + lane, row = sl / SPV, ch = sl % SPV;
+        dvo[r] = row * a.Npad * 2 + min(ch, VCH - 1) * 16;  // < 2^31: row < D, Npad <= 2^24
       }
+    }
+    // Copy item r of pair (K tile ktk, V^T tile ktv) into buffer buf; vzero: write zeros in
+    // place of the V^T tile.
+    auto copy_item = [&](int r, uint16_t *buf, int ktk, int ktv, bool vzero) {
+      const int g = wv + 8 * r;
+      const int rows = min(kBc, N - ktk * kBc);
+      const size_t left = ((size_t)D * a.Npad - (size_t)ktv * kBc) * 2;
+      const uint32_t vbytes = (uint32_t)(left < 0xFFFFFFFFull ? left : 0xFFFFFFFFull);
+      const bool isk = g < NJK;
+      const char *base = isk ? kbytes + (size_t)ktk * kBc * KROW
+                             : (const char *)(vbase + (size_t)ktv * kBc);
+      const uint32_t bytes = isk ? (uint32_t)(rows * KROW) : (g < NJ && !vzero) ? vbytes : 0u;
+      copy16_to_lds(base, bytes, dvo[r], buf + min(g, NJ) * 512);
     };
-    // K_0, K_1 and V^T_0 before the loop.
+    // Pair 0 (K_0 and a zero V^T_{-1}: P = 0 in the first M-phase) and pair 1 (K_1, V^T_0).
 #pragma unroll
-    for (int r = 0; r < NDMA; ++r) copy_item(r, sK0, sV0, kt_cur, kt_cur);
+    for (int r = 0; r < NDMA; ++r) copy_item(r, sB0, kt_cur, kt_cur, true);
 #pragma unroll
-    for (int r = 0; r < RK; ++r) copy_item(r, sK1, sV0, kt_next, kt_cur);
+    for (int r = 0; r < NDMA; ++r) copy_item(r, sB1, kt_next, kt_cur, false);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // Iteration k with B = k mod 3 and phase group G, every buffer named statically.
     auto iteration = [&](int k, auto bc, auto gc) {
       constexpr int B = decltype(bc)::value, G = decltype(gc)::value;
-      constexpr int B1 = (B + 1) % 3, B2 = (B + 2) % 3;
-      uint16_t *kr = B == 0 ? sK0 : B == 1 ? sK1 : sK2;      // K_k
-      uint16_t *vr = B2 == 0 ? sV0 : B2 == 1 ? sV1 : sV2;    // V^T_{k-1}
-      uint16_t *kw = B2 == 0 ? sK0 : B2 == 1 ? sK1 : sK2;    // K_{k+2}
-      uint16_t *vw = B1 == 0 ? sV0 : B1 == 1 ? sV1 : sV2;    // V^T_{k+1}
-      auto item = [&](int r) { copy_item(r, kw, vw, kt_n2, kt_next); };
-      auto mp = [&] { mphase_bf16(kr, vr, item, IntC<NDMA>{}, IntC<1>{}); };
+      constexpr int B2 = (B + 2) % 3;
+      uint16_t *rb = B == 0 ? sB0 : B == 1 ? sB1 : sB2;     // (K_k, V^T_{k-1})
+      uint16_t *wb = B2 == 0 ? sB0 : B2 == 1 ? sB1 : sB2;   // (K_{k+2}, V^T_{k+1})
+      auto item = [&](int r) { copy_item(r, wb, kt_n2, kt_next, false); };
+      auto mp = [&] { mphase_bf16(rb, rb + NJK * 512, item, IntC<NDMA>{}, IntC<1>{}); };
       if constexpr (G == 0) {
         mphase(mp);
         __builtin_amdgcn_s_barrier();
