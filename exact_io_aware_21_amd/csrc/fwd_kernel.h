@@ -100,7 +100,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   static_assert(MOD == 0 || (POS && !ALIBI && !SOFTCAP && !FP8),
                 "modification instances take natural-units scores on the POS path");
   static_assert(kBc * KP8 <= kBc * pitch(D) * 2, "FP8 K tile must fit the K buffer");
-  // LDS tiles: three buffers, each an array of its own holding a K tile, then a V^T tile, then
+  // LDS tiles: four buffers, each an array of its own holding a K tile, then a V^T tile, then
   // a spare 1 KB row, so that every access of the bf16 instances names its buffer statically
   // (the compiler then tracks the buffer-to-LDS copies in flight per buffer and waits only
   // where a read needs one).  The spare row takes the copy instructions a wave issues beyond
@@ -112,6 +112,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   __shared__ __attribute__((aligned(16))) uint16_t sB0[(NJ + 1) * 512];
   __shared__ __attribute__((aligned(16))) uint16_t sB1[(NJ + 1) * 512];
   __shared__ __attribute__((aligned(16))) uint16_t sB2[(NJ + 1) * 512];
+  __shared__ __attribute__((aligned(16))) uint16_t sB3[(NJ + 1) * 512];
   uint16_t *const sK0 = sB0, *const sK1 = sB1;
   uint16_t *const sV0 = sB0 + NJK * 512, *const sV1 = sB1 + NJK * 512;
 
@@ -296,12 +297,29 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   constexpr int kDepth = 4;
   // Items are either register staging (an LDS store and a buffer load) or, with DMA, one
   // buffer-to-LDS copy instruction.
+  // With DMA the first kDepth fragments are read before the phase (the previous V-phase
+  // issues them into win_pre, see bf16_prefetch) rather than at its start.
+  u32x4 win_pre[kDepth];
+  auto bf16_frag = [&](const uint16_t *kl, const uint16_t *vl, int i) -> u32x4 {
+    constexpr int NPV = 4 * NDB;
+    if (i < NPV) {
+      const int kk = i / NDB, db = i % NDB;
+      return *(const u32x4 *)(vl + l32 * VP + hf * 8 + db * 32 * VP + kk * 16);
+    }
+    const int j = i - NPV, ks = j >> 1, blk = j & 1;
+    return *(const u32x4 *)(kl + l32 * KP + hf * 8 + blk * 32 * KP + ks * 16);
+  };
+  auto bf16_prefetch = [&](const uint16_t *buf) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) win_pre[i] = bf16_frag(buf, buf + NJK * 512, i);
+  };
   auto mphase_bf16 = [&](const uint16_t *kl, const uint16_t *vl, auto item, auto nitc,
                          auto dmac) {
     constexpr int NPV = 4 * NDB;
     constexpr int NST = NPV + 2 * NKS;
     constexpr int NI = decltype(nitc)::value;
     constexpr bool DMA = decltype(dmac)::value;
+    static_assert(NST >= kDepth, "the window must fit the phase");
     const uint16_t *vbuf = vl + l32 * VP + hf * 8;
     const uint16_t *kbuf = kl + l32 * KP + hf * 8;
     auto frag = [&](int i) -> u32x4 {
@@ -314,8 +332,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     };
     u32x4 win[kDepth];
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i)
-      if (i < NST) win[i] = frag(i);
+    for (int i = 0; i < kDepth; ++i) win[i] = DMA ? win_pre[i] : frag(i);
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       const u32x4 cur = win[i % kDepth];
@@ -333,8 +350,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     }
     // Pin that order for the scheduler: kDepth LDS reads, then MFMA / LDS read pairs, with the
     // staging items in between.
+    if constexpr (!DMA) {
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < kDepth; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -651,14 +670,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       }
     }
   } else {
-    // Buffer-to-LDS copies through three LDS buffers: buffer t mod 3 holds the pair
+    // Buffer-to-LDS copies through four LDS buffers: buffer t mod 4 holds the pair
     // (K_t, V^T_{t-1}), which is what the M-phase of iteration t reads.  In iteration k every
-    // wave issues, between the MFMAs of its own M-phase, its share of the copies of pair k + 2
-    // (K_{k+2}, V^T_{k+1}) into the buffer last read in iteration k - 1; before the barrier that
-    // ends iteration k + 1 it waits for them (vmcnt counts the copies in issue order), so
-    // iteration k + 2 finds the pair whole.  The copies are in flight for a whole iteration and
-    // nothing else waits for them: the barriers inside the loop are bare s_barrier
-    // instructions (a workgroup fence would wait for every copy).
+    // wave issues, between the MFMAs of its own M-phase, its share of the copies of pair k + 3
+    // (K_{k+3}, V^T_{k+2}) into the buffer last read in iteration k - 1.  Before the barrier in
+    // the middle of iteration k each wave waits for its copies of pair k + 1 (issued in
+    // iteration k - 2; vmcnt counts the copies in issue order), so after that barrier pair
+    // k + 1 is whole and the wave whose next M-phase reads it issues that phase's first
+    // fragment reads at the end of its V-phase, across the next barrier.  The copies are in
+    // flight for more than an iteration and nothing else waits for them: the barriers inside
+    // the loop are bare s_barrier instructions (a workgroup fence would wait for every copy).
     //
     // A tile row is SPK (K) or SPV (V^T) 16-byte slots, the last one padding; copy instruction
     // g of a pair fills slots 64 g .. 64 g + 63 of its buffer (K tile first).  Wave w issues
@@ -693,44 +714,53 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       const uint32_t bytes = isk ? (uint32_t)(rows * KROW) : (g < NJ && !vzero) ? vbytes : 0u;
       copy16_to_lds(base, bytes, dvo[r], buf + min(g, NJ) * 512);
     };
-    // Pair 0 (K_0 and a zero V^T_{-1}: P = 0 in the first M-phase) and pair 1 (K_1, V^T_0).
+    // Pairs 0 (K_0 and a zero V^T_{-1}: P = 0 in the first M-phase), 1 and 2.
 #pragma unroll
     for (int r = 0; r < NDMA; ++r) copy_item(r, sB0, kt_cur, kt_cur, true);
 #pragma unroll
     for (int r = 0; r < NDMA; ++r) copy_item(r, sB1, kt_next, kt_cur, false);
+#pragma unroll
+    for (int r = 0; r < NDMA; ++r) copy_item(r, sB2, kt_n2, kt_next, false);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (grp == 0) bf16_prefetch(sB0);
 
-    // Iteration k with B = k mod 3 and phase group G, every buffer named statically.
+    // Iteration k with B = k mod 4 and phase group G, every buffer named statically.
     auto iteration = [&](int k, auto bc, auto gc) {
       constexpr int B = decltype(bc)::value, G = decltype(gc)::value;
-      constexpr int B2 = (B + 2) % 3;
-      uint16_t *rb = B == 0 ? sB0 : B == 1 ? sB1 : sB2;     // (K_k, V^T_{k-1})
-      uint16_t *wb = B2 == 0 ? sB0 : B2 == 1 ? sB1 : sB2;   // (K_{k+2}, V^T_{k+1})
-      auto item = [&](int r) { copy_item(r, wb, kt_n2, kt_next, false); };
+      constexpr int B1 = (B + 1) % 4, B3 = (B + 3) % 4;
+      uint16_t *rb = B == 0 ? sB0 : B == 1 ? sB1 : B == 2 ? sB2 : sB3;       // pair k
+      uint16_t *nb = B1 == 0 ? sB0 : B1 == 1 ? sB1 : B1 == 2 ? sB2 : sB3;    // pair k + 1
+      uint16_t *wb = B3 == 0 ? sB0 : B3 == 1 ? sB1 : B3 == 2 ? sB2 : sB3;    // pair k + 3
+      auto item = [&](int r) { copy_item(r, wb, kt_n3, kt_n2, false); };
       auto mp = [&] { mphase_bf16(rb, rb + NJK * 512, item, IntC<NDMA>{}, IntC<1>{}); };
       if constexpr (G == 0) {
         mphase(mp);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NDMA));  // pair k + 1: issued in k - 2
         __builtin_amdgcn_s_barrier();
         if (k < T) vphase(kt_cur, sk_cur);
         advance(k);
+        bf16_prefetch(nb);
       } else {
         if (k >= 1) vphase(kt_prev, sk_prev);
+        bf16_prefetch(rb);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));  // pair k + 1: issued in k - 2
         __builtin_amdgcn_s_barrier();
         mphase(mp);
         advance(k);
       }
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));
       __builtin_amdgcn_s_barrier();
     };
     auto run = [&](auto gc) {
-      for (int k = 0;; k += 3) {
+      for (int k = 0;; k += 4) {
         iteration(k, IntC<0>{}, gc);
         if (k >= T) break;
         iteration(k + 1, IntC<1>{}, gc);
         if (k + 1 >= T) break;
         iteration(k + 2, IntC<2>{}, gc);
         if (k + 2 >= T) break;
+        iteration(k + 3, IntC<3>{}, gc);
+        if (k + 3 >= T) break;
       }
     };
     if (grp == 0)
