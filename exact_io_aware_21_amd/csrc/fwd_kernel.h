@@ -83,29 +83,22 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   constexpr int NT = 512;                // threads per workgroup
   constexpr int KCH = D / 8;             // 16-byte chunks per K row
   constexpr int VCH = kBc / 8;           // 16-byte chunks per V^T row
-  constexpr int KLD = kBc * KCH / NT;    // K chunks loaded per thread per tile
-  constexpr int VLD = D * VCH / NT;      // V^T chunks loaded per thread per tile
   constexpr int NKS = D / 16;            // k-steps of the score product
   constexpr int NDB = D / 32;            // 32-column blocks of O
   constexpr int KP = pitch(D);           // LDS pitch of a K row (keys x D)
   constexpr int VP = pitch(kBc);         // LDS pitch of a V^T row (D x keys)
   constexpr int KP8 = D + 16;            // LDS pitch of an FP8 K row, bytes
-  constexpr int KCH8 = D / 16;           // 16-byte chunks per FP8 K row
-  constexpr int NK8 = kBc * KCH8;        // 16-byte chunks per FP8 K tile
-  constexpr int KLDN = FP8 ? (NK8 + NT - 1) / NT : KLD;  // K chunks per thread per tile
   constexpr int NKS8 = D / 64;           // k-steps of the FP8 score product
   static_assert(kBr == 256 && kBc == 64, "kernel is written for 256 x 64 tiles");
-  static_assert(KLD >= 1 && VLD >= 1, "tile loads must cover the workgroup");
   static_assert(!FP8 || (!ALIBI && !SOFTCAP), "FP8 instances take no score modification");
   static_assert(MOD == 0 || (POS && !ALIBI && !SOFTCAP && !FP8),
                 "modification instances take natural-units scores on the POS path");
-  static_assert(kBc * KP8 <= kBc * pitch(D) * 2, "FP8 K tile must fit the K buffer");
   // LDS tiles: four buffers, each an array of its own holding a K tile, then a V^T tile, then
   // a spare 1 KB row, so that every access of the bf16 instances names its buffer statically
   // (the compiler then tracks the buffer-to-LDS copies in flight per buffer and waits only
   // where a read needs one).  The spare row takes the copy instructions a wave issues beyond
-  // the tiles' share, which read nothing and write zeros.  FP8 instances use buffers 0 and 1.
-  constexpr int SPK = KP / 8, SPV = VP / 8;                // 16-byte slots per LDS row
+  // the tiles' share, which read nothing and write zeros.  FP8 K rows are KP8 bytes.
+  constexpr int SPK = FP8 ? KP8 / 16 : KP / 8, SPV = VP / 8;  // 16-byte slots per LDS row
   constexpr int NJK = kBc * SPK / 64, NJV = D * SPV / 64;  // copy instructions per tile
   constexpr int NJ = NJK + NJV;
   static_assert(kBc * SPK % 64 == 0 && D * SPV % 64 == 0, "tiles must fill whole copy rows");
@@ -113,8 +106,6 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   __shared__ __attribute__((aligned(16))) uint16_t sB1[(NJ + 1) * 512];
   __shared__ __attribute__((aligned(16))) uint16_t sB2[(NJ + 1) * 512];
   __shared__ __attribute__((aligned(16))) uint16_t sB3[(NJ + 1) * 512];
-  uint16_t *const sK0 = sB0, *const sK1 = sB1;
-  uint16_t *const sV0 = sB0 + NJK * 512, *const sV1 = sB1 + NJK * 512;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   // Phase group: of the two waves the dispatcher placed on a SIMD, the lower-numbered one is
@@ -232,52 +223,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     return lst[t];
   };
 
-  // Tile staging.  Per tile pair each thread moves NI 16-byte chunks: items 0 .. KLDN-1 are
-  // chunks of the next K tile, items KLDN .. NI-1 chunks of the current V^T tile.  Loads are
-  // buffer loads at lane-constant offsets from a per-tile base (K rows past N read as zero), so
-  // an item is one instruction and no branch.  The loads of an iteration are spread over its
-  // first slot and the LDS stores over its second, between the other work of the wave, rather
-  // than issued by every wave in one burst at a slot boundary.
   constexpr int KROW = FP8 ? D : 2 * D;  // bytes per K row in memory
   constexpr int KCHR = KROW / 16;        // 16-byte chunks per K row
-  constexpr int NKC = kBc * KCHR;        // chunks per K tile
-  constexpr int KPB = FP8 ? KP8 : 2 * KP;  // bytes per K row in LDS
-  constexpr int NI = KLDN + VLD;
-  static_assert(KLDN * NT >= NKC && VLD * NT == D * VCH, "staging must cover both tiles");
   const char *kbytes = FP8 ? (const char *)(a.k8 + (size_t)bh * N * D)
                            : (const char *)(a.k + (size_t)bh * N * D);
   const uint16_t *vbase = a.vt + (size_t)bh * D * a.Npad;
-  // Lane-constant byte offsets of chunk u = 0: item u adds u * (NT / KCHR) rows (K) or
-  // u * (NT / VCH) rows (V^T) to both, a scalar or immediate offset.  For FP8 with d = 64 the
-  // 512 threads cover the 256 chunks of a K tile twice (identical writes).
-  const int c0 = tid % NKC;
-  const int kgo = (c0 / KCHR) * KROW + (c0 % KCHR) * 16;
-  const int klo = pi_key(c0 / KCHR) * KPB + (c0 % KCHR) * 16;
-  const int vgo = (tid / VCH) * a.Npad * 2 + (tid % VCH) * 16;  // < 2^31: tid / VCH < 64
-  const int vlo = (tid / VCH) * VP * 2 + (tid % VCH) * 16;
-  constexpr int kStageAhead = 1;  // iterations between a chunk's fetch and its LDS store
-  constexpr int KRU = NT / KCHR;  // K rows per item
-  constexpr int VRU = NT / VCH;   // V^T rows per item
-  static_assert(KLDN == 1 || NKC % NT == 0, "K items must tile the K tile");
-  auto fetch_item = [&](int j, int kt_k, int kt_v) -> u32x4 {
-    if (j < KLDN) {
-      const int rows = min(kBc, N - kt_k * kBc);
-      return buffer_load16(kbytes + (size_t)kt_k * kBc * KROW, (uint32_t)(rows * KROW), kgo,
-                             j * KRU * KROW);
-    } else {
-      const size_t left = ((size_t)D * a.Npad - (size_t)kt_v * kBc) * 2;
-      return buffer_load16(vbase + (size_t)kt_v * kBc,
-                             (uint32_t)(left < 0xFFFFFFFFull ? left : 0xFFFFFFFFull), vgo,
-                             (int)((uint32_t)((j - KLDN) * VRU) * (uint32_t)a.Npad * 2u));
-    }
-  };
-  auto store_item = [&](int j, int kb, int vb, u32x4 x) {
-    if (j < KLDN)
-      *(u32x4 *)((char *)(kb ? sK1 : sK0) + klo + j * KRU * KPB) = x;
-    else
-      *(u32x4 *)((char *)(vb ? sV1 : sV0) + vlo + (j - KLDN) * VRU * VP * 2) = x;
-  };
-
 
   const float slopeL = ALIBI ? a.slopes[h] * 1.4426950408889634f : 0.f;
   float m_run = -INFINITY, l_run = 0.f;
@@ -292,34 +242,23 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   // that consecutive MFMAs write different accumulators.  The A
   // fragment of step i + kDepth is read from LDS while step i runs, so LDS latency stays hidden
   // behind the matrix core.
-  // Staging item j (`item(j)`: the LDS store of chunk j, then the buffer load of chunk j of the
-  // next tile pair into the same registers) goes after MFMA step 1 + j * NST / NI.
+  // Staging item j (`item(j)`: one buffer-to-LDS copy instruction of a later tile pair) goes
+  // after MFMA step 1 + j * NST / NI.  The first kDepth fragments are read before the phase:
+  // the wave's previous V-phase issues them into win_pre (see prefetch).
   constexpr int kDepth = 4;
-  // Items are either register staging (an LDS store and a buffer load) or, with DMA, one
-  // buffer-to-LDS copy instruction.
-  // With DMA the first kDepth fragments are read before the phase (the previous V-phase
-  // issues them into win_pre, see bf16_prefetch) rather than at its start.
   u32x4 win_pre[kDepth];
-  auto bf16_frag = [&](const uint16_t *kl, const uint16_t *vl, int i) -> u32x4 {
-    constexpr int NPV = 4 * NDB;
-    if (i < NPV) {
-      const int kk = i / NDB, db = i % NDB;
-      return *(const u32x4 *)(vl + l32 * VP + hf * 8 + db * 32 * VP + kk * 16);
-    }
-    const int j = i - NPV, ks = j >> 1, blk = j & 1;
-    return *(const u32x4 *)(kl + l32 * KP + hf * 8 + blk * 32 * KP + ks * 16);
-  };
-  auto bf16_prefetch = [&](const uint16_t *buf) {
+  // Both M-phases start with P V steps, so the window holds V^T fragments (kDepth <= 4 NDB).
+  static_assert(kDepth <= 4 * NDB, "the first fragments must be V^T fragments");
+  auto prefetch = [&](const uint16_t *buf) {
+    const uint16_t *vl = buf + NJK * 512 + l32 * VP + hf * 8;
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) win_pre[i] = bf16_frag(buf, buf + NJK * 512, i);
+    for (int i = 0; i < kDepth; ++i)
+      win_pre[i] = *(const u32x4 *)(vl + (i % NDB) * 32 * VP + (i / NDB) * 16);
   };
-  auto mphase_bf16 = [&](const uint16_t *kl, const uint16_t *vl, auto item, auto nitc,
-                         auto dmac) {
+  auto mphase_bf16 = [&](const uint16_t *kl, const uint16_t *vl, auto item, auto nitc) {
     constexpr int NPV = 4 * NDB;
     constexpr int NST = NPV + 2 * NKS;
     constexpr int NI = decltype(nitc)::value;
-    constexpr bool DMA = decltype(dmac)::value;
-    static_assert(NST >= kDepth, "the window must fit the phase");
     const uint16_t *vbuf = vl + l32 * VP + hf * 8;
     const uint16_t *kbuf = kl + l32 * KP + hf * 8;
     auto frag = [&](int i) -> u32x4 {
@@ -332,7 +271,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     };
     u32x4 win[kDepth];
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) win[i] = DMA ? win_pre[i] : frag(i);
+    for (int i = 0; i < kDepth; ++i) win[i] = win_pre[i];
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       const u32x4 cur = win[i % kDepth];
@@ -348,34 +287,27 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       for (int j = 0; j < NI; ++j)
         if (i == 1 + j * NST / NI) item(j);
     }
-    // Pin that order for the scheduler: kDepth LDS reads, then MFMA / LDS read pairs, with the
-    // staging items in between.
-    if constexpr (!DMA) {
-#pragma unroll
-      for (int i = 0; i < kDepth; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+    // Pin that order for the scheduler: MFMA / LDS read pairs, with the copy items in between.
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        if (i == 1 + j * NST / NI) {
-          if constexpr (!DMA) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
+        if (i == 1 + j * NST / NI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       if (i + kDepth < NST) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
   // The FP8 M-phase: the same P V steps, then 2 * D / 64 score steps (k-step ks, key block blk),
   // each fed by two 16-byte LDS reads of K8 (bytes 64*ks + 32*hf .. +31 of the lane's key row).
   // The LDS reads form one stream, kDepth reads ahead of the MFMA that consumes them.
-  auto mphase_fp8 = [&](int t, auto item) {
+  auto mphase_fp8 = [&](const uint16_t *kl, const uint16_t *vl, auto item, auto nitc) {
     constexpr int NPV = 4 * NDB;
     constexpr int NSS = 2 * NKS8;      // score MFMAs
     constexpr int NST = NPV + NSS;     // MFMAs
     constexpr int NR = NPV + 2 * NSS;  // LDS reads
-    const uint16_t *vbuf = (((t - 1) & 1) ? sV1 : sV0) + l32 * VP + hf * 8;
-    const uint8_t *kbuf = (const uint8_t *)((t & 1) ? sK1 : sK0) + l32 * KP8 + hf * 32;
+    constexpr int NI = decltype(nitc)::value;
+    const uint16_t *vbuf = vl + l32 * VP + hf * 8;
+    const uint8_t *kbuf = (const uint8_t *)kl + l32 * KP8 + hf * 32;
     auto frag = [&](int r) -> u32x4 {
       if (r < NPV) {
         const int kk = r / NDB, db = r % NDB;
@@ -386,7 +318,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     };
     u32x4 win[kDepth];
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) win[i] = frag(i);
+    for (int i = 0; i < kDepth; ++i) win[i] = win_pre[i];
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const u32x4 cur = win[i % kDepth];
@@ -412,16 +344,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
         if (NPV + st == 1 + j * NST / NI) item(j);
     }
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
     for (int i = 0; i < NPV; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        if (i == 1 + j * NST / NI) {
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
+        if (i == 1 + j * NST / NI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       if (i + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
@@ -430,10 +357,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        if (NPV + st == 1 + j * NST / NI) {
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
+        if (NPV + st == 1 + j * NST / NI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       if (r0 + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       if (r0 + 1 + kDepth < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -451,17 +375,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // Zero P and the V buffer read by the first M-phase (its P V step then adds exactly 0).
+  // P = 0 for the first M-phase (its P V step then adds exactly 0 against a zero V^T tile).
 #pragma unroll
   for (int g = 0; g < 4; ++g) pb[g] = f16x8{};
-  if constexpr (FP8) {
-    for (int i = tid; i < D * VP / 8; i += NT) *(u32x4 *)(sV1 + i * 8) = u32x4{0u, 0u, 0u, 0u};
-    if (T > 0) {
-#pragma unroll
-      for (int j = 0; j < KLDN; ++j) store_item(j, 0, 0, fetch_item(j, kt_of(0), 0));
-    }
-    __syncthreads();
-  }
 
   // V-phase of tile t: score modifications, mask, online softmax, P_t in fp16.
   auto vphase = [&](int kt, float skt) {
@@ -623,53 +539,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     sk_cur = sk_next;
     sk_next = sk_n2;
   };
-  if constexpr (FP8) {
-    // Register staging through two LDS buffers.  Chunks in flight: stg[] holds those of K_{k+1}
-    // and V_k, written in iteration k; with kStageAhead = 2, stg2[] those of K_{k+2} and
-    // V_{k+1}, fetched an iteration earlier still.
-    u32x4 stg[NI], stg2[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      stg[j] = fetch_item(j, kt_next, kt_cur);
-      if constexpr (kStageAhead == 2) stg2[j] = fetch_item(j, kt_n2, kt_next);
-    }
-
-    // Two slots per iteration k.  Slot A: group 0 runs M-phase k, group 1 V-phase k-1.  Slot B:
-    // group 0 runs V-phase k, group 1 M-phase k.  K_k and V_{k-1} are read in both slots.  Each
-    // wave stages its chunks inside its own M-phase, between the MFMAs: it writes the chunks of
-    // K_{k+1} and V_k (fetched one iteration earlier) to the idle buffers, which no step of
-    // iteration k reads, and fetches those of K_{k+2} and V_{k+1}.  Both groups execute the
-    // same 2T + 2 barriers.  In M-phase 0, P = 0 against a zeroed V buffer adds nothing; in
-    // M-phase T the score product reads a stale K buffer and its result is never used.
-    auto stage = [&](int k) {
-      return [&, k](int j) {
-        store_item(j, (k + 1) & 1, k & 1, stg[j]);
-        if constexpr (kStageAhead == 2) {
-          stg[j] = stg2[j];
-          stg2[j] = fetch_item(j, kt_n3, kt_n2);
-        } else {
-          stg[j] = fetch_item(j, kt_n2, kt_next);
-        }
-      };
-    };
-    if (grp == 0) {
-      for (int k = 0; k <= T; ++k) {
-        mphase([&] { mphase_fp8(k, stage(k)); });
-        __syncthreads();
-        if (k < T) vphase(kt_cur, sk_cur);
-        advance(k);
-        __syncthreads();
-      }
-    } else {
-      for (int k = 0; k <= T; ++k) {
-        if (k >= 1) vphase(kt_prev, sk_prev);
-        __syncthreads();
-        mphase([&] { mphase_fp8(k, stage(k)); });
-        advance(k);
-        __syncthreads();
-      }
-    }
-  } else {
+  {
     // Buffer-to-LDS copies through four LDS buffers: buffer t mod 4 holds the pair
     // (K_t, V^T_{t-1}), which is what the M-phase of iteration t reads.  In iteration k every
     // wave issues, between the MFMAs of its own M-phase, its share of the copies of pair k + 3
@@ -695,7 +565,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       if (g < NJK) {
         const int sl = g * 64 + lane, row = sl / SPK, ch = sl % SPK;
         // LDS row `row` holds key pi(row) (pi is an involution)
-        dvo[r] = pi_key(row) * KROW + min(ch, KCH - 1) * 16;
+        dvo[r] = pi_key(row) * KROW + min(ch, KCHR - 1) * 16;
       } else {
         const int sl = (g - NJK) * 64 + lane, row = sl / SPV, ch = sl % SPV;
         dvo[r] = row * a.Npad * 2 + min(ch, VCH - 1) * 16;  // < 2^31: row < D, Npad <= 2^24
@@ -723,7 +593,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     for (int r = 0; r < NDMA; ++r) copy_item(r, sB2, kt_n2, kt_next, false);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (grp == 0) bf16_prefetch(sB0);
+    if (grp == 0) prefetch(sB0);
 
     // Iteration k with B = k mod 4 and phase group G, every buffer named statically.
     auto iteration = [&](int k, auto bc, auto gc) {
@@ -733,17 +603,22 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       uint16_t *nb = B1 == 0 ? sB0 : B1 == 1 ? sB1 : B1 == 2 ? sB2 : sB3;    // pair k + 1
       uint16_t *wb = B3 == 0 ? sB0 : B3 == 1 ? sB1 : B3 == 2 ? sB2 : sB3;    // pair k + 3
       auto item = [&](int r) { copy_item(r, wb, kt_n3, kt_n2, false); };
-      auto mp = [&] { mphase_bf16(rb, rb + NJK * 512, item, IntC<NDMA>{}, IntC<1>{}); };
+      auto mp = [&] {
+        if constexpr (FP8)
+          mphase_fp8(rb, rb + NJK * 512, item, IntC<NDMA>{});
+        else
+          mphase_bf16(rb, rb + NJK * 512, item, IntC<NDMA>{});
+      };
       if constexpr (G == 0) {
         mphase(mp);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NDMA));  // pair k + 1: issued in k - 2
         __builtin_amdgcn_s_barrier();
         if (k < T) vphase(kt_cur, sk_cur);
         advance(k);
-        bf16_prefetch(nb);
+        prefetch(nb);
       } else {
         if (k >= 1) vphase(kt_prev, sk_prev);
-        bf16_prefetch(rb);
+        prefetch(rb);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));  // pair k + 1: issued in k - 2
         __builtin_amdgcn_s_barrier();
         mphase(mp);
