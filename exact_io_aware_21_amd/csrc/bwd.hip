@@ -184,19 +184,14 @@ __device__ __forceinline__ u32x4 tr_frag(const uint16_t *tile, const int off[2],
 }
 
 // ---------------------------------------------------------------------------------------------
-// Block placement of a (position, head) grid, gridDim = (nx, B*H).  Workgroups are dispatched
-// round-robin over the 8 XCDs in linear block order, and a freed compute unit takes the next
-// block.  For causal and document masks the positions of a head carry very different amounts
-// of work: when each XCD's share of the linear order is whole heads, its blocks are ordered by
-// position first and head second, so that every head's longest position (position 0) starts
-// before any shorter one and the heads of one XCD share its L2.  Otherwise the natural order.
-__device__ __forceinline__ void block_place(int kind, int &pos, int &bh) {
-  const int nx = gridDim.x, nblk = gridDim.x * gridDim.y, w = blockIdx.y * nx + blockIdx.x;
-  const int n8 = nblk & ~7, per = n8 >> 3;
-  if ((kind == kMaskCausal || kind == kMaskDocument) && w < n8 && per % nx == 0) {
-    const int hc = per / nx, i = w >> 3;
-    bh = (w & 7) * hc + i % hc;
-    pos = i / hc;
+// Block placement of a (position, head) grid, gridDim = (n_pos, B*H): for causal and document
+// masks longest position first across small groups of heads (see place_block; head_bytes are
+// the two row arrays one head's blocks stream, 4 N d bytes), otherwise the natural order.
+__device__ __forceinline__ void block_place(int kind, int N, int d, int &pos, int &bh) {
+  if (kind == kMaskCausal || kind == kMaskDocument) {
+    const int nx = gridDim.x;
+    place_block(blockIdx.y * nx + blockIdx.x, nx * gridDim.y, nx, true, (size_t)4 * N * d, pos,
+                bh);
   } else {
     bh = blockIdx.y;
     pos = blockIdx.x;
@@ -225,7 +220,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS copy targets
   int kx, bh;
-  block_place(a.kind, kx, bh);  // key blocks: the first ones see the most queries
+  block_place(a.kind, a.N, D, kx, bh);  // key blocks: the first ones see the most queries
   const int b = bh / a.H, h = bh - b * a.H;
   const int N = a.N;
   const int key0 = kx * (NW * KPW);
@@ -430,7 +425,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   // the buffer-to-LDS copies (M0) are scalars
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int qx, bh;
-  block_place(a.kind, qx, bh);
+  block_place(a.kind, a.N, D, qx, bh);
   const int b = bh / a.H, h = bh - b * a.H;
   // q-tiles: the last ones see the most keys
   const int qt = (a.kind == kMaskCausal || a.kind == kMaskDocument) ? a.n_qt - 1 - qx : qx;

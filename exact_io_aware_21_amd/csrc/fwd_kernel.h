@@ -119,28 +119,14 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   for (int w2 = 0; w2 < wave; ++w2) grp += simd_of[w2] == simd_of[wave];
   grp = __builtin_amdgcn_readfirstlane(grp > 1 ? 1 : grp);  // wave-uniform: scalar branches
 
-  // Workgroups are dispatched round-robin over the 8 XCDs, in block order: XCD x receives
-  // blocks x, x + 8, ...  Remap so that each XCD works on a contiguous range of heads (their
-  // q-tiles share K and V in its L2).  Causal and document masks give q-tiles key lists of
-  // very different lengths: when the range is whole heads, their blocks are ordered by q-tile
-  // position first and head second, so that every q-tile of one position across the range's
-  // heads is started before those of the next; with the longest key lists first (below), the
-  // freed compute units then pick up ever shorter work.  Other kinds keep the head-major order,
-  // whose concurrently running q-tiles of one head share most of their keys (a sliding window
-  // ran 5 % slower interleaved).
-  const int nblk = gridDim.x, w = blockIdx.x;
-  const int n8 = nblk & ~7, per = n8 >> 3;
+  // Each XCD works on a contiguous range of heads (their q-tiles share K and V in its L2).
+  // Causal and document masks give q-tiles key lists of very different lengths: their blocks
+  // are placed longest first across small groups of heads (see place_block; a head's K and V^T
+  // take 4 N d bytes).  Other kinds keep one head at a time, whose concurrently running q-tiles
+  // share most of their keys (a sliding window ran 5 % slower interleaved).
   const bool lpt = MOD == 0 && (a.kind == kMaskCausal || a.kind == kMaskDocument);
-  int bh, qx;
-  if (lpt && w < n8 && per % a.n_qt == 0) {
-    const int hc = per / a.n_qt, i = w >> 3;
-    bh = (w & 7) * hc + i % hc;
-    qx = i / hc;
-  } else {
-    const int lb = (w < n8) ? (w & 7) * per + (w >> 3) : w;
-    bh = lb / a.n_qt;
-    qx = lb - bh * a.n_qt;
-  }
+  int qx, bh;
+  place_block(blockIdx.x, gridDim.x, a.n_qt, lpt, (size_t)4 * a.N * D, qx, bh);
   // Masked kinds have longer key lists for later q-tiles: start those first.
   const int qt = (a.kind != kMaskNone || (MOD & kModMask)) ? a.n_qt - 1 - qx : qx;
   const int b = bh / a.H, h = bh - b * a.H;

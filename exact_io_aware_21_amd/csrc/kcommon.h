@@ -116,6 +116,37 @@ __device__ __forceinline__ void copy16_to_lds(const void *base, uint32_t bytes, 
 // outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Placement of block w of a grid of nblk blocks over (position, head) pairs, n_pos positions per
+// head.  Blocks are dispatched round-robin over the 8 XCDs in order (XCD x receives blocks
+// x, x + 8, ...) and a freed compute unit takes the next one.  Each XCD gets a contiguous range
+// of heads, whose data then shares its L2.  With lpt (positions of very different work, longest
+// at position 0), when the range is whole heads it is walked in groups of g heads: inside a
+// group position-major (every head's position p before any head's p + 1), so that long blocks
+// start before short ones while only g heads' data is in flight per XCD; g is the largest
+// divisor of the range's head count whose heads' bytes (head_bytes each) stay within 16 MiB,
+// at least 1.  Otherwise position-major within one head at a time (the natural order).
+__device__ __forceinline__ void place_block(int w, int nblk, int n_pos, bool lpt, size_t head_bytes,
+                                            int &pos, int &bh) {
+  const int n8 = nblk & ~7, per = n8 >> 3;
+  if (w < n8 && per % n_pos == 0) {
+    const int hc = per / n_pos, i = w >> 3;
+    int g = 1;
+    if (lpt)
+      for (int c = hc; c >= 1; --c)
+        if (hc % c == 0 && (size_t)c * head_bytes <= (size_t)16 << 20) {
+          g = c;
+          break;
+        }
+    const int gi = i / (g * n_pos), r = i - gi * (g * n_pos);
+    bh = (w & 7) * hc + gi * g + r % g;
+    pos = r / g;
+  } else {
+    const int lb = (w < n8) ? (w & 7) * per + (w >> 3) : w;
+    bh = lb / n_pos;
+    pos = lb - bh * n_pos;
+  }
+}
+
 // bf16 bits -> fp16 bits; exact for |x| in [2^-14, 65504], saturating beyond (NaN stays NaN).
 __device__ __forceinline__ uint32_t bf16_to_f16_bits(uint32_t b) {
   float f = __uint_as_float(b << 16);
