@@ -95,6 +95,10 @@ CASES = [
     ("b_none_softcap_alibi_d64", 1, 2, 150, 64, "none", 0, True, 2.0, 2.0),
     ("b_doc_softcap_d64", 2, 2, 500, 64, "document", 0, False, 30.0, 2.0),
     ("b_doc_d128", 2, 1, 400, 128, "document", 0, False, 0.0, 1.0),
+    # block placement of both kernels: shares of 2 whole heads walked position-major, and
+    # shares that are not whole heads with a tail past the last multiple of 8 blocks
+    ("b_place_grp2_causal_d64", 2, 8, 512, 64, "causal", 0, False, 0.0, 1.0),
+    ("b_place_tail_causal_d128", 3, 5, 700, 128, "causal", 0, False, 0.0, 1.0),
 ]
 
 

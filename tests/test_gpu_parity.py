@@ -113,6 +113,12 @@ SMALL = [
     ("none_softcap_alibi_d64", 1, 2, 150, 64, "none", 0, True, 2.0, 2.0),
     ("doc_softcap_d64", 2, 2, 900, 64, "document", 0, False, 30.0, 2.0),
     ("doc_d128", 3, 1, 500, 128, "document", 0, False, 0.0, 1.0),
+    # block placement: each XCD's share is 2 whole heads, walked position-major (causal, doc)
+    ("place_grp2_causal_d64", 2, 8, 512, 64, "causal", 0, False, 0.0, 1.0),
+    ("place_grp2_doc_d64", 4, 4, 512, 64, "document", 0, False, 0.0, 1.0),
+    # block placement: shares that are not whole heads (5 blocks of 3-q-tile heads) and a
+    # 5-block tail past the last multiple of 8
+    ("place_tail_causal_d128", 3, 5, 700, 128, "causal", 0, False, 0.0, 1.0),
 ]
 
 
