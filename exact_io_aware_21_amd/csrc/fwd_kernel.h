@@ -231,6 +231,12 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   const uint16_t *vbase = a.vt + (size_t)bh * D * a.Npad;
 
   const float slopeL = ALIBI ? a.slopes[h] * 1.4426950408889634f : 0.f;
+  // Soft-cap without ALiBi keeps u = 1 / (1 + e^{2 s / cap}) per score instead of the capped
+  // score t = cap (1 - 2 u) (base 2: capL - 2 capL u): the probability is then one FMA and one
+  // exponential, exp2(capL - m - 2 capL u), and the tile maximum of t is taken as the minimum
+  // of u.  A masked score is u = +inf.
+  constexpr bool UCAP = SOFTCAP && !ALIBI && !POS && MOD == 0;
+  constexpr float kMasked = UCAP ? INFINITY : -INFINITY;
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 oacc[NDB];
 #pragma unroll
@@ -412,7 +418,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
           float tt;
           if constexpr (SOFTCAP) {
             const float e = __builtin_amdgcn_exp2f(x * a.cap_c1);
-            tt = fmaf(-2.f * a.capL, __builtin_amdgcn_rcpf(1.f + e), a.capL);
+            const float u = __builtin_amdgcn_rcpf(1.f + e);
+            tt = UCAP ? u : fmaf(-2.f * a.capL, u, a.capL);
           } else {
             tt = x * c;
           }
@@ -435,7 +442,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
           for (int r = 0; r < 16; ++r) {
             const int j = kb + 32 * blk + 16 * (r >> 3) + (r & 7);
             if (!q_ok || j >= N || !attn_mask_mod(b, qrow, j, a.mod_params))
-              s[blk][r] = -INFINITY;
+              s[blk][r] = kMasked;
           }
         }
       }
@@ -448,7 +455,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = kb + 32 * blk + 16 * (r >> 3) + (r & 7);
-          if (j < lo || j > hi) s[blk][r] = -INFINITY;
+          if (j < lo || j > hi) s[blk][r] = kMasked;
         }
       }
     }
@@ -469,8 +476,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float x = s[g >> 1][8 * (g & 1) + e];
-          const float p = POS ? __builtin_amdgcn_exp2f(fmaf(x, c, -m_use))
-                              : __builtin_amdgcn_exp2f(x - m_use);
+          const float p = POS    ? __builtin_amdgcn_exp2f(fmaf(x, c, -m_use))
+                          : UCAP ? __builtin_amdgcn_exp2f(fmaf(-2.f * a.capL, x, a.capL - m_use))
+                                 : __builtin_amdgcn_exp2f(x - m_use);
           pv[e] = p;
           acc += p;
         }
@@ -480,6 +488,14 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       return (psum[0] + psum[1]) + (psum[2] + psum[3]);
     };
     auto lane_max = [&]() -> float {
+      if constexpr (UCAP) {
+        float mn = INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mn = fminf(mn, s[blk][r]);
+        return fmaf(-2.f * a.capL, mn, a.capL);  // -inf when every score is masked
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
