@@ -112,6 +112,25 @@ __device__ __forceinline__ float score2(const BwdArgs &a, float x, float slopeL,
   return t;
 }
 
+// The same with the distance j - i given as a float (exact: |j - i| < 2^24), so that callers can
+// form it as a per-tile base plus a compile-time offset.
+template <bool ALIBI, bool SOFTCAP>
+__device__ __forceinline__ float score2f(const BwdArgs &a, float x, float slopeL, float dji,
+                                         float &dcap) {
+  float t;
+  if constexpr (SOFTCAP) {
+    const float e = __builtin_amdgcn_exp2f(x * a.cap_c1);
+    t = fmaf(-2.f * a.capL, __builtin_amdgcn_rcpf(1.f + e), a.capL);
+    const float th = t / a.capL;
+    dcap = 1.f - th * th;
+  } else {
+    t = x * a.c;
+    dcap = 1.f;
+  }
+  if constexpr (ALIBI) t = fmaf(slopeL, dji, t);
+  return t;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Buffer-to-LDS copy of two equally laid-out tiles (byte size `bytes` each, from x and y) into
 // dst: wave instruction j (j = wave + NW r < NJ) fills the 64 16-byte slots j * 64 .. j * 64 + 63
@@ -543,8 +562,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int jj = kt * kBc + 32 * blk + 16 * (r >> 3) + 8 * hf + (r & 7);
-        const float tt = score2<ALIBI, SOFTCAP>(a, s[blk][r], slopeL, qrow, jj, dc[blk][r]);
+        // key - query distance: the tile's base plus this register's offset, exact in float
+        const float dji = (float)(kt * kBc + 8 * hf - qrow) + (float)(32 * blk + 16 * (r >> 3) + (r & 7));
+        const float tt = score2f<ALIBI, SOFTCAP>(a, s[blk][r], slopeL, dji, dc[blk][r]);
         s[blk][r] = __builtin_amdgcn_exp2f(tt - l2);
       }
     // Element mask only when some row of this wave does not allow all 64 keys of the tile.
