@@ -94,26 +94,9 @@ __device__ __forceinline__ void store16(void *out, size_t off, const f32x16 &o) 
 }
 
 // Score of one (query i, key j) pair from its raw dot product x, in base-2 units, and the factor
-// d s / d t of the soft-cap (1 - tanh^2; 1 without it).
-template <bool ALIBI, bool SOFTCAP>
-__device__ __forceinline__ float score2(const BwdArgs &a, float x, float slopeL, int i, int j,
-                                        float &dcap) {
-  float t;
-  if constexpr (SOFTCAP) {
-    const float e = __builtin_amdgcn_exp2f(x * a.cap_c1);
-    t = fmaf(-2.f * a.capL, __builtin_amdgcn_rcpf(1.f + e), a.capL);  // cap tanh(x scale/cap) log2e
-    const float th = t / a.capL;
-    dcap = 1.f - th * th;
-  } else {
-    t = x * a.c;
-    dcap = 1.f;
-  }
-  if constexpr (ALIBI) t = fmaf(slopeL, (float)(j - i), t);
-  return t;
-}
-
-// The same with the distance j - i given as a float (exact: |j - i| < 2^24), so that callers can
-// form it as a per-tile base plus a compile-time offset.
+// d s / d t of the soft-cap (1 - tanh^2; 1 without it).  The ALiBi distance j - i comes as a
+// float (exact: |j - i| < 2^24), which callers form as a per-tile base plus a compile-time
+// offset.
 template <bool ALIBI, bool SOFTCAP>
 __device__ __forceinline__ float score2f(const BwdArgs &a, float x, float slopeL, float dji,
                                          float &dcap) {
@@ -360,8 +343,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int aa = r >> 2, bb = r & 3;
-      const int i = q0 + 16 * (aa >> 1) + 8 * hf + 4 * (aa & 1) + bb;
-      const float t = score2<ALIBI, SOFTCAP>(a, s[r], slopeL, i, j, dc[r]);
+      // key - query distance: the step's base plus this register's offset, exact in float
+      const float dji = (float)(j - q0 - 8 * hf) - (float)(16 * (aa >> 1) + 4 * (aa & 1) + bb);
+      const float t = score2f<ALIBI, SOFTCAP>(a, s[r], slopeL, dji, dc[r]);
       p[r] = __builtin_amdgcn_exp2f(fmaf(-kLog2e, l2v[aa][bb], t));  // L is natural-log
     }
     // Element mask only when some key of this wave does not take all 32 queries of the step.
