@@ -10,7 +10,11 @@ that shares nothing with the backward oracle's formulas:
   * B2  torch autograd through torch's own fp64 scaled_dot_product_attention (masks as boolean
         masks, ALiBi as an additive bias);
   * B3  closed forms: N = 1; keys with one common value row; the key-gradient sum that the
-        softmax Jacobian makes zero; D_i = dO_i . O_i.
+        softmax Jacobian makes zero; D_i = dO_i . O_i;
+  * B4  the error scales of backward_magnitudes, which set the GPU tolerance of the backward
+        pass: they bound the gradients, are attained exactly by the worst-case rounding of the
+        operands (formed by torch autograd with perturbed operands, not by restated formulas),
+        and bound random roundings.
 """
 import numpy as np
 import pytest
@@ -141,3 +145,129 @@ def test_b3_row_dot_identity():
     p /= p.sum(axis=1, keepdims=True)
     direct = (p * (g[0, 0] @ v[0, 0].T)).sum(axis=1)
     assert np.abs(oracle.backward_row_dot(o, g)[0, 0] - direct).max() <= 1e-12
+
+
+# --- B4: the error scales M of backward_magnitudes ------------------------------------------
+# M is defined as the largest change of a gradient element when one operand of every product
+# term is rounded to a relative precision u (P in dV = P^T dO; dS in dQ, dK; D_i = dO_i . O_i
+# formed from an O rounded the same way).  The pins below perturb those operands inside torch
+# autograd (a hook on the gradient that flows into the scores, a factor on P in the forward) and
+# let autograd form the perturbed gradients, so no backward formula is restated here:
+#   * triangle inequality: |gradient| <= M element-wise;
+#   * attainment: with Q, K >= 0 (dQ, dK) or dO >= 0 (dV) every term of a gradient element has
+#     one sign, so the worst-case rounding (relative +u on |dS|, D moved by u sum|dO O| against
+#     the terms, P scaled by 1 + u) moves every element by exactly u M;
+#   * random roundings within u move every element by at most u M.
+# A dropped scale, a dropped soft-cap factor, a |dS| counted twice, a transposed product or a
+# missing D term in M each break the attainment equality.
+U = 2.0 ** -8
+
+
+def _autograd(q, k, v, g, scale, b, h, kw, ds_hook=None, p_factor=None):
+    """Gradients of sum(O * g) for head (b, h) by torch autograd (fp64).  ds_hook(grad, P, O)
+    replaces the gradient reaching the masked scores; p_factor multiplies P where it enters P V.
+    Returns (dQ, dK, dV, P, O) as numpy arrays."""
+    N = q.shape[2]
+    rows = np.arange(N)
+    off = None if kw.get("doc_offsets") is None else kw["doc_offsets"][b]
+    ok = torch.tensor(oracle.allowed(rows, rows, N, kw["mask"], kw.get("window", 0), off))
+    Q, K, V = (torch.tensor(x[b, h], requires_grad=True) for x in (q, k, v))
+    t = scale * (Q @ K.T)
+    cap = kw.get("softcap", 0.0)
+    s = cap * torch.tanh(t / cap) if cap else t
+    if kw.get("slopes") is not None:
+        dist = torch.tensor((rows[:, None] - rows[None, :]).astype(np.float64))
+        s = s - float(kw["slopes"][h]) * dist
+    s = s.masked_fill(~ok, float("-inf"))
+    P = torch.softmax(s, dim=-1)
+    O = P @ V
+    if ds_hook is not None:
+        Pd, Od = P.detach(), O.detach()
+        s.register_hook(lambda grad: ds_hook(grad, Pd, Od))
+    Pv = P if p_factor is None else P * torch.tensor(p_factor)
+    Ov = Pv @ V
+    (Ov * torch.tensor(g[b, h])).sum().backward()
+    return Q.grad.numpy(), K.grad.numpy(), V.grad.numpy(), P.detach().numpy(), O.detach().numpy()
+
+
+B4_VARIANTS = [("none", False, 0.0), ("causal", False, 0.0), ("window", True, 0.0),
+               ("document", False, 0.0), ("causal", False, 2.0), ("window", True, 1.5)]
+
+
+def _b4_inputs(seed, positive_qk=False, positive_do=False):
+    B, H, N, d = 1, 2, 24, 8
+    q, k, v, g = (rnd((B, H, N, d), seed + i) for i in range(4))
+    if positive_qk:
+        q, k = np.abs(q), np.abs(k)
+    if positive_do:
+        g = np.abs(g)
+    return q, k, v, g
+
+
+@pytest.mark.parametrize("mask,alibi,cap", B4_VARIANTS)
+def test_b4_magnitudes_bound_gradients(mask, alibi, cap):
+    """Triangle inequality: every gradient element is at most its M."""
+    q, k, v, g = _b4_inputs(40)
+    kw = variant_kwargs(mask, q.shape[2], q.shape[1], alibi=alibi, softcap=cap, window=5)
+    grads = oracle.attention_backward(q, k, v, g, 0.7, **kw)
+    mags = oracle.backward_magnitudes(q, k, v, g, 0.7, **kw)
+    for gr, m in zip(grads, mags):
+        assert np.all(np.abs(gr) <= m * (1 + 1e-12) + 1e-300)
+
+
+@pytest.mark.parametrize("mask,alibi,cap", B4_VARIANTS)
+def test_b4_worst_case_rounding_attains_m(mask, alibi, cap):
+    """Attainment: the worst-case operand rounding moves dQ, dK (Q, K >= 0) and dV (dO >= 0) by
+    exactly u M, element by element."""
+    scale = 0.7
+    q, k, v, g = _b4_inputs(50, positive_qk=True)
+    H, N = q.shape[1], q.shape[2]
+    kw = variant_kwargs(mask, N, H, alibi=alibi, softcap=cap, window=5)
+    mq, mk, _ = oracle.backward_magnitudes(q, k, v, g, scale, **kw)
+
+    def worst(grad, P, O):
+        # dS rounded up in magnitude by u, and D_i = dO_i . O_i off by u sum_c |dO_ic O_ic| in
+        # the direction that adds P_ij times it to every dS_ij of the row
+        dD = U * (torch.tensor(g[0, h]) * O).abs().sum(dim=1)
+        return grad + U * grad.abs() + P * dD[:, None]
+
+    for h in range(H):
+        dq0, dk0, _, _, _ = _autograd(q, k, v, g, scale, 0, h, kw)
+        dq1, dk1, _, _, _ = _autograd(q, k, v, g, scale, 0, h, kw, ds_hook=worst)
+        np.testing.assert_allclose(dq1 - dq0, U * mq[0, h], rtol=1e-9, atol=1e-15)
+        np.testing.assert_allclose(dk1 - dk0, U * mk[0, h], rtol=1e-9, atol=1e-15)
+
+    q, k, v, g = _b4_inputs(60, positive_do=True)
+    _, _, mv = oracle.backward_magnitudes(q, k, v, g, scale, **kw)
+    for h in range(H):
+        _, _, dv0, _, _ = _autograd(q, k, v, g, scale, 0, h, kw)
+        _, _, dv1, _, _ = _autograd(q, k, v, g, scale, 0, h, kw,
+                                    p_factor=np.full((N, N), 1.0 + U))
+        np.testing.assert_allclose(dv1 - dv0, U * mv[0, h], rtol=1e-9, atol=1e-15)
+
+
+@pytest.mark.parametrize("mask,alibi,cap", B4_VARIANTS[:4])
+def test_b4_random_rounding_within_m(mask, alibi, cap):
+    """Random roundings of the operands within relative u (signs of Q, K, dO arbitrary) move
+    every gradient element by at most u M."""
+    scale = 0.7
+    q, k, v, g = _b4_inputs(70)
+    H, N = q.shape[1], q.shape[2]
+    kw = variant_kwargs(mask, N, H, alibi=alibi, softcap=cap, window=5)
+    mq, mk, mv = oracle.backward_magnitudes(q, k, v, g, scale, **kw)
+    rng = np.random.default_rng(3)
+    for h in range(H):
+        dq0, dk0, dv0, _, _ = _autograd(q, k, v, g, scale, 0, h, kw)
+        for _ in range(3):
+            dl = torch.tensor(rng.uniform(-U, U, (N, N)))
+            eps = torch.tensor(rng.uniform(-U, U, (N, q.shape[3])))
+
+            def rand_round(grad, P, O, dl=dl, eps=eps):
+                dD = (torch.tensor(g[0, h]) * O * eps).sum(dim=1)  # D from O (1 + eps)
+                return grad * (1 + dl) - P * dD[:, None]
+
+            dq1, dk1, _, _, _ = _autograd(q, k, v, g, scale, 0, h, kw, ds_hook=rand_round)
+            _, _, dv1, _, _ = _autograd(q, k, v, g, scale, 0, h, kw,
+                                        p_factor=1 + rng.uniform(-U, U, (N, N)))
+            for d1, d0, m in ((dq1, dq0, mq), (dk1, dk0, mk), (dv1, dv0, mv)):
+                assert np.all(np.abs(d1 - d0) <= U * m[0, h] * (1 + 1e-9) + 1e-15)
