@@ -109,7 +109,13 @@ def attention(q, k, v, scale, mask="none", window=0, softcap=0.0, slopes=None,
     for b, h in heads:
         off = None if doc_offsets is None else np.asarray(doc_offsets)[b]
         ok = allowed(rows, cols, N, mask, window, off)
-        s = scores(q[b, h, rows], k[b, h], scale, h, rows, cols, softcap, slopes)
+        # A key that none of the evaluated rows may attend to gets s = -inf in every row, hence
+        # weight e^{-inf} = 0 in every sum below: only keys some row allows are scored (at
+        # least one, so that a row with no allowed key still goes through the same steps).
+        live = np.flatnonzero(ok.any(axis=0))
+        kc = cols[live] if live.size else cols[:1]
+        ok = ok[:, kc]
+        s = scores(q[b, h, rows], k[b, h, kc], scale, h, rows, kc, softcap, slopes)
         s = np.where(ok, s, -np.inf)
         # pass 1: row maximum
         m = s.max(axis=1)
@@ -119,7 +125,7 @@ def attention(q, k, v, scale, mask="none", window=0, softcap=0.0, slopes=None,
         e = np.exp(s - m_safe[:, None])
         ell = e.sum(axis=1)
         p = e / np.where(empty, 1.0, ell)[:, None]
-        O[b, h] = p @ v[b, h]
+        O[b, h] = p @ v[b, h, kc]
         with np.errstate(divide="ignore"):
             L[b, h] = np.where(empty, -np.inf, m + np.log(np.where(empty, 1.0, ell)))
         O[b, h][empty] = 0.0
@@ -128,23 +134,39 @@ def attention(q, k, v, scale, mask="none", window=0, softcap=0.0, slopes=None,
 
 def attention_blocked(q, k, v, scale, Br, Bc, form="local_max", mask="none", window=0,
                       softcap=0.0, slopes=None, doc_offsets=None):
-    """The tiled forward pass with the online-softmax recurrence, for checking the oracle.
+    """A tiled evaluation of the same softmax, used only to check the oracle (pin P3).
 
-    Steps of page "FlashAttention/es", section "El algoritmo FlashAttention":
-      partition Q into blocks of Br rows and K, V into blocks of Bc rows; for each query block
-      start from O = 0, m = -inf, l = 0; for each key/value block form the score block, its local
-      row maximum m_ij and the local exponentials e^{S - m_ij}; merge with the running statistics
-      by m_new = max(m, m_ij), scaling the old O and l by e^{m - m_new} and the new block's
-      contribution by e^{m_ij - m_new}; at the end divide O by l and form L = m + log l.
-    form="local_max" is that local-maximum form.  form="running_max" exponentiates directly
-    against m_new (e^{S - m_new}), which is the same algebra with one exponential per score.
-    A block row with no allowed key contributes nothing (its local maximum is -inf); the pages
-    say nothing about that case.
+    Page "FlashAttention/es", section "El algoritmo FlashAttention", computes O and L block by
+    block.  The mathematics behind it: for a set J of keys of one query row, the triple
+    (m_J, l_J, o_J) = (max_{j in J} s_j, sum_j e^{s_j - m_J}, sum_j e^{s_j - m_J} v_j) merges with
+    the triple of a disjoint set K into that of J u K by rescaling both to the larger maximum:
+    m = max(m_J, m_K), l = e^{m_J - m} l_J + e^{m_K - m} l_K, o likewise.  The merge is
+    associative, so folding the key blocks in order and dividing o by l at the end gives the
+    two-pass result, with L = m + ln l.
+    form="local_max" forms each block's triple with its own maximum and then merges it;
+    form="running_max" exponentiates the block directly against the merged maximum (one
+    exponential per score).  A block in which a row has no allowed key has m = -inf and
+    contributes nothing.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, N, d = q.shape
+    if form not in ("local_max", "running_max"):
+        raise ValueError(form)
+
+    def rescale(m_from, m_to):
+        # e^{m_from - m_to}, with a set that has seen no allowed key (m = -inf) weighing 0
+        with np.errstate(invalid="ignore"):
+            return np.where(np.isfinite(m_from), np.exp(m_from - np.where(np.isfinite(m_to),
+                                                                          m_to, 0.0)), 0.0)
+
+    def merge(x, y):
+        # (m, l, o) of the union of two disjoint key sets
+        m = np.maximum(x[0], y[0])
+        ax, ay = rescale(x[0], m), rescale(y[0], m)
+        return m, ax * x[1] + ay * y[1], ax[:, None] * x[2] + ay[:, None] * y[2]
+
     O = np.zeros((B, H, N, d))
     L = np.zeros((B, H, N))
     for b in range(B):
@@ -152,35 +174,18 @@ def attention_blocked(q, k, v, scale, Br, Bc, form="local_max", mask="none", win
         for h in range(H):
             for r0 in range(0, N, Br):
                 rows = np.arange(r0, min(r0 + Br, N))
-                o = np.zeros((rows.size, d))
-                m = np.full(rows.size, -np.inf)
-                ell = np.zeros(rows.size)
+                acc = (np.full(rows.size, -np.inf), np.zeros(rows.size), np.zeros((rows.size, d)))
                 for c0 in range(0, N, Bc):
                     cols = np.arange(c0, min(c0 + Bc, N))
-                    s = scores(q[b, h, rows], k[b, h, cols], scale, h, rows, cols, softcap,
-                               slopes)
                     ok = allowed(rows, cols, N, mask, window, off)
-                    s = np.where(ok, s, -np.inf)
+                    s = np.where(ok, scores(q[b, h, rows], k[b, h, cols], scale, h, rows, cols,
+                                            softcap, slopes), -np.inf)
                     m_blk = s.max(axis=1)
-                    m_new = np.maximum(m, m_blk)
-                    seen = np.isfinite(m_new)
-                    a_old = np.where(seen & np.isfinite(m), np.exp(m - np.where(seen, m_new, 0)),
-                                     np.where(seen, 0.0, 1.0))
-                    if form == "local_max":
-                        has = np.isfinite(m_blk)
-                        mb = np.where(has, m_blk, 0.0)
-                        pt = np.where(ok, np.exp(s - mb[:, None]), 0.0)
-                        a_blk = np.where(has, np.exp(mb - np.where(seen, m_new, 0.0)), 0.0)
-                        o = o * a_old[:, None] + (pt @ v[b, h, cols]) * a_blk[:, None]
-                        ell = ell * a_old + pt.sum(axis=1) * a_blk
-                    elif form == "running_max":
-                        mn = np.where(seen, m_new, 0.0)
-                        pt = np.where(ok, np.exp(s - mn[:, None]), 0.0)
-                        o = o * a_old[:, None] + pt @ v[b, h, cols]
-                        ell = ell * a_old + pt.sum(axis=1)
-                    else:
-                        raise ValueError(form)
-                    m = m_new
+                    # the maximum the block's exponentials are taken against
+                    ref = m_blk if form == "local_max" else np.maximum(acc[0], m_blk)
+                    e = np.where(ok, np.exp(s - np.where(np.isfinite(ref), ref, 0.0)[:, None]), 0.0)
+                    acc = merge(acc, (ref, e.sum(axis=1), e @ v[b, h, cols]))
+                m, ell, o = acc
                 empty = ell == 0
                 O[b, h, rows] = np.where(empty[:, None], 0.0, o / np.where(empty, 1, ell)[:, None])
                 with np.errstate(divide="ignore"):
