@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -205,9 +206,14 @@ int check_device() {
     (void)hipGetLastError();
     return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "cannot query device %d", dev);
   }
-  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  // Test hook: ATTN_TEST_ARCH_OVERRIDE, if set when a device is first checked, stands in for the
+  // architecture name the device reports, so that the unsupported-device path can be exercised
+  // on a gfx950 (nothing is launched on that path).
+  const char *ov = std::getenv("ATTN_TEST_ARCH_OVERRIDE");
+  const char *arch = (ov && *ov) ? ov : prop.gcnArchName;
+  const bool ok = std::strncmp(arch, "gfx950", 6) == 0;
   if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
-  if (!ok) return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  if (!ok) return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device %d is %s, not gfx950", dev, arch);
   return ATTN_OK;
 }
 

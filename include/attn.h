@@ -39,6 +39,8 @@
  * All arguments are validated before any HIP call.  attn_strerror(code) names a code;
  * attn_last_error() returns a thread-local message naming the offending argument.
  * A device that is not gfx950 gives ATTN_ERR_UNSUPPORTED_DEVICE: there is no fallback path.
+ * For tests, the environment variable ATTN_TEST_ARCH_OVERRIDE, if set when the library first
+ * checks a device in a process, replaces the architecture name that device reports.
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -116,13 +118,29 @@ typedef struct {
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
              int d, float scale, uint32_t variant, const attn_params *params, void *stream);
 
-/* Bytes of workspace attn_fwd needs for this shape and variant (0 on invalid arguments).
-   It holds a key-transposed copy of V, the block table and, with ATTN_PREC_FP8, the E4M3
-   codes of K ([B][H][N][d] bytes) and their scales (fp32 [B][H][ceil(N/Bc)]). */
+/*
+ * attn_workspace_size -- bytes of device workspace attn_fwd needs for this shape and variant
+ * (0 on invalid arguments; no HIP call).  The caller allocates it once and passes it in
+ * params->workspace, so that no call allocates: page "FlashAttention-3 y torch.compile ...",
+ * section 6, item 2, explains that graph-captured execution forbids memory allocation during
+ * the recorded run and that intermediate buffers must be allocated beforehand.  The workspace
+ * holds a key-transposed fp16 copy of V ([B][H][d][ceil(N/Bc)*Bc]), the block table and, with
+ * ATTN_PREC_FP8, the E4M3 codes of K ([B][H][N][d] bytes) and their scales (fp32
+ * [B][H][ceil(N/Bc)]).  Its contents are scratch: rewritten by every call, never read across
+ * calls.
+ */
 size_t attn_workspace_size(int B, int H, int N, int d, uint32_t variant);
 
-/* Tile shape (Br query rows x Bc keys) the forward kernel uses for (d, variant); the block table
-   is defined on this shape.  Returns ATTN_OK or ATTN_ERR_INVALID_ARG. */
+/*
+ * attn_tile_shape -- the tile shape (*Br query rows x *Bc keys) of the forward kernel for
+ * (d, variant).  Page "FlashAttention/es", section "El algoritmo FlashAttention", cuts Q into
+ * blocks of Br rows and K, V into blocks of Bc rows; page "El FlexAttention de PyTorch con
+ * FlashAttention-4 ...", section "Limitaciones actuales", skips the blocks the mask empties.
+ * The block table (attn_block_table) classifies exactly these tiles, so its contents are only
+ * defined together with this shape.  d as for attn_fwd; Br, Bc are host pointers.
+ * Returns ATTN_OK, or ATTN_ERR_INVALID_ARG (unsupported d, unknown variant bits, NULL output);
+ * no HIP call.
+ */
 int attn_tile_shape(int d, uint32_t variant, int *Br, int *Bc);
 
 /*
@@ -139,8 +157,11 @@ int attn_tile_shape(int d, uint32_t variant, int *Br, int *Bc);
 int attn_block_table(int B, int H, int N, int d, uint32_t variant, const attn_params *params,
                      int8_t *cls, int32_t *kv_cnt, int32_t *kv_list, void *stream);
 
-/* Same table computed on the host by the same closed-form tile predicates the device uses.
-   Here params->doc_offsets and the three outputs are HOST pointers.  No HIP call is made. */
+/* attn_block_table_host -- the same block table (page "El FlexAttention ...", section
+   "Limitaciones actuales": tiles the mask empties are skipped) computed on the host by the same
+   closed-form tile predicates the device uses, for checking without a GPU.  Arguments as
+   attn_block_table, but params->doc_offsets and the three outputs are HOST pointers (caller
+   owned, sized as there).  Returns ATTN_OK or ATTN_ERR_INVALID_ARG; no HIP call is made. */
 int attn_block_table_host(int B, int H, int N, int d, uint32_t variant, const attn_params *params,
                           int8_t *cls, int32_t *kv_cnt, int32_t *kv_list);
 
@@ -228,6 +249,18 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
    [B*H][n_split][Lq rounded up to 1, 2, 4 or 8] x (d + 2). */
 size_t attn_decode_workspace_size(int B, int H, int Lq, int d, int page_size, int max_pages);
 
+/*
+ * attn_strerror -- a static, NUL-terminated English name of a return code ("unknown error code"
+ * for values not listed above); never NULL, never freed by the caller.
+ * attn_last_error -- a thread-local, NUL-terminated message naming the argument or condition
+ * behind the last error this thread received ("" if none); valid until the thread's next call.
+ * Errors are reported and never hidden behind another code path: page "Hugging Face Reduce el
+ * Exceso de Atención ..." warns that an attention dispatcher which silently falls back to an
+ * unfused path for an unsupported head size or dtype is only found with a profiler, and page
+ * "FlashAttention-3 y torch.compile ...", section 6, item 3, asks for a capability check on the
+ * device instead of a crash.  So an unsupported shape is ATTN_ERR_INVALID_ARG and a device that
+ * is not gfx950 is ATTN_ERR_UNSUPPORTED_DEVICE, each with its message, before any launch.
+ */
 const char *attn_strerror(int code);
 const char *attn_last_error(void);
 
