@@ -146,6 +146,41 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_device(dev, **tensors):
+    """Every named tensor (None skipped) lives on the GPU `dev`.  The library receives raw
+    device addresses and cannot tell a host pointer or another GPU's memory from its own, so this
+    is the only guard against a kernel reading the wrong memory."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (it is on {t.device})")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device} while the inputs are on {dev}")
+
+
+def _check_aux(dev, B, H, variant, alibi_slopes, doc_offsets, workspace):
+    """alibi_slopes: contiguous fp32 with at least H values; doc_offsets: contiguous int32
+    [B, max_docs + 1]; workspace: contiguous; all on `dev`."""
+    import torch
+    _on_device(dev, alibi_slopes=alibi_slopes, doc_offsets=doc_offsets, workspace=workspace)
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32
+                                     or not alibi_slopes.is_contiguous()
+                                     or alibi_slopes.numel() < H):
+        raise ValueError(f"alibi_slopes must be a contiguous fp32 tensor of >= {H} values")
+    if doc_offsets is not None and (doc_offsets.dtype != torch.int32
+                                    or not doc_offsets.is_contiguous()
+                                    or doc_offsets.dim() != 2 or doc_offsets.shape[0] != B
+                                    or doc_offsets.shape[1] < 2):
+        raise ValueError(f"doc_offsets must be a contiguous int32 [B={B}, max_docs + 1] tensor")
+    if (variant & 0xF) == ATTN_MASK_DOCUMENT and doc_offsets is None:
+        raise ValueError("the document mask needs doc_offsets")
+    if (variant & ATTN_MOD_ALIBI) and alibi_slopes is None:
+        raise ValueError("ATTN_MOD_ALIBI needs alibi_slopes")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
 def make_params(window=0, softcap=0.0, alibi_slopes=None, doc_offsets=None, o_dtype=ATTN_O_BF16,
                 workspace=None):
     p = attn_params()
@@ -189,6 +224,8 @@ def attn_fwd(q, k, v, o, lse, scale, variant, window=0, softcap=0.0, alibi_slope
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
                             or tuple(lse.shape) != (B, H, N)):
         raise ValueError("lse must be a contiguous fp32 [B,H,N] tensor")
+    _on_device(q.device, q=q, k=k, v=v, o=o, lse=lse)
+    _check_aux(q.device, B, H, variant, alibi_slopes, doc_offsets, workspace)
     if workspace is None:
         workspace = alloc_workspace(B, H, N, d, variant, q.device)
     p = make_params(window, softcap, alibi_slopes, doc_offsets,
@@ -233,6 +270,8 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale, variant, window=0, softca
                              f"(bf16 or fp32)")
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H, N):
         raise ValueError("lse must be a contiguous fp32 [B,H,N] tensor")
+    _on_device(q.device, q=q, k=k, v=v, o=o, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv)
+    _check_aux(q.device, B, H, variant, alibi_slopes, doc_offsets, workspace)
     if workspace is None:
         workspace = alloc_bwd_workspace(B, H, N, d, variant, q.device)
     p = make_params(window, softcap, alibi_slopes, doc_offsets,
@@ -288,6 +327,8 @@ def attn_decode(q, k_cache, v_cache, page_table, seq_lens, o, lse, scale, causal
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
                             or tuple(lse.shape) != (B, H, Lq)):
         raise ValueError("lse must be a contiguous fp32 [B,H,Lq] tensor")
+    _on_device(q.device, q=q, k_cache=k_cache, v_cache=v_cache, page_table=page_table,
+               seq_lens=seq_lens, o=o, lse=lse, workspace=workspace)
     max_pages = page_table.shape[1]
     if workspace is None:
         workspace = alloc_decode_workspace(B, H, Lq, d, page, max_pages, q.device)
@@ -319,6 +360,7 @@ def attn_quantize_fp8(x, codes, scales, rows, stream=None):
     if scales.dtype != torch.float32 or not scales.is_contiguous() or \
             tuple(scales.shape) != (B, H, nb):
         raise ValueError("scales must be a contiguous fp32 [B,H,ceil(N/rows)] tensor")
+    _on_device(x.device, x=x, codes=codes, scales=scales)
     _check(lib().attn_quantize_fp8(_ptr(x), _ptr(codes), _ptr(scales), B, H, N, d, rows,
                                    _stream(stream)))
     return codes, scales
@@ -327,6 +369,17 @@ def attn_quantize_fp8(x, codes, scales, rows, stream=None):
 def attn_block_table(B, H, N, d, variant, cls, kv_cnt, kv_list, window=0, doc_offsets=None,
                      stream=None):
     """Device block table into torch tensors cls (int8), kv_cnt (int32), kv_list (int32)."""
+    import torch
+    Br, Bc = attn_tile_shape(d, variant)
+    n_qt, n_kt = -(-N // Br), -(-N // Bc)
+    Bm = B if (variant & 0xF) == ATTN_MASK_DOCUMENT else 1
+    for name, t, dt, shape in (("cls", cls, torch.int8, (Bm, n_qt, n_kt)),
+                               ("kv_cnt", kv_cnt, torch.int32, (Bm, n_qt)),
+                               ("kv_list", kv_list, torch.int32, (Bm, n_qt, n_kt))):
+        if t.dtype != dt or not t.is_contiguous() or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {shape}")
+    _on_device(cls.device, cls=cls, kv_cnt=kv_cnt, kv_list=kv_list)
+    _check_aux(cls.device, B, H, variant & 0xF, None, doc_offsets, None)
     p = make_params(window=window, doc_offsets=doc_offsets)
     _check(lib().attn_block_table(B, H, N, d, variant, ctypes.byref(p), _ptr(cls), _ptr(kv_cnt),
                                   _ptr(kv_list), _stream(stream)))
@@ -412,6 +465,8 @@ class AttnMod:
         if mod_params is not None and (mod_params.dtype != torch.float32
                                        or not mod_params.is_contiguous()):
             raise ValueError("mod_params must be a contiguous fp32 tensor")
+        _on_device(q.device, q=q, k=k, v=v, o=o, lse=lse, mod_params=mod_params,
+                   workspace=workspace)
         if workspace is None:
             workspace = self.alloc_workspace(B, H, N, q.device)
         p = make_params(o_dtype=ATTN_O_F32 if o.dtype == torch.float32 else ATTN_O_BF16,
