@@ -133,10 +133,15 @@ class SclkSampler:
     The published MFMA peak assumes the 2.4 GHz maximum clock; under sustained matrix-core load the
     clock settles lower, and this records where."""
 
-    def __init__(self, period_s=0.005):
+    def __init__(self, period_s=0.005, started=None):
+        """started: optional callable; samples are kept only once it returns True (the bench
+        passes the completion query of the first timed step's end event, so that the readings
+        taken while the driver's value still lags the idle clock are dropped)."""
         import glob
         import threading
         self.period_s = period_s
+        self.started = started
+        self.dropped = 0
         self.samples = []
         self.path = None
         for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
@@ -161,7 +166,10 @@ class SclkSampler:
         while not self._stop.is_set():
             mhz = self._read(self.path)
             if mhz is not None:
-                self.samples.append(mhz)
+                if self.started is None or self.started():
+                    self.samples.append(mhz)
+                else:
+                    self.dropped += 1
             self._stop.wait(self.period_s)
 
     def __enter__(self):
@@ -179,7 +187,26 @@ class SclkSampler:
             return None
         x = sorted(self.samples)
         return {"median": x[len(x) // 2], "min": x[0], "max": x[-1], "samples": len(x),
-                "source": self.path}
+                "dropped_before_first_step": self.dropped, "source": self.path}
+
+
+def clock_scaled_peak(rec, peak, achieved):
+    """Adds to the clock record the MFMA peak scaled to the median sampled clock and the fraction
+    of it reached.  The sysfs clock is read by the driver on its own schedule and can lag the
+    hardware, so a fraction above 1 (physically impossible) marks the reading as stale: the
+    fraction is then left out and the record says why."""
+    if not rec:
+        return rec
+    scaled = peak * rec["median"] / MAX_SCLK_MHZ
+    rec["mfma_peak_at_median_tflops"] = round(scaled, 1)
+    frac = achieved / scaled
+    if frac <= 1.0:
+        rec["frac_of_that_peak"] = round(frac, 4)
+    else:
+        rec["frac_of_that_peak"] = None
+        rec["note"] = ("sampled clock lags the hardware (the kernel ran faster than the peak at "
+                       "that clock allows); not used")
+    return rec
 
 
 def mod_source(w):
@@ -283,7 +310,7 @@ def bench_bwd(args, w, inp, q, k, v, o, lse, var, slopes, offs, dev):
         b.record()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    sclk = SclkSampler()
+    sclk = SclkSampler(started=kev[0][1].query)
     with sclk:
         start.record()
         for i in range(K):
@@ -351,7 +378,7 @@ def bench_decode(args):
         b.record()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    sclk = SclkSampler()
+    sclk = SclkSampler(started=kev[0][1].query)
     with sclk:
         start.record()
         for i in range(K):
@@ -515,8 +542,8 @@ def main():
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    sclk = SclkSampler()
-    with sclk:  # sampled until the device has finished the timed work
+    sclk = SclkSampler(started=kev[0][1].query)
+    with sclk:  # sampled from the end of the first timed step until the device has finished
         start.record()
         for i in range(K):
             if args.cold:
@@ -539,12 +566,8 @@ def main():
     value = flops / (step_ms * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
     traffic = traffic_from_profile(w.name)
-    sclk_rec = sclk.summary()
     peak = PEAK_FP8_FWD_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
-    if sclk_rec:  # the same peak scaled to the clock the device ran at
-        sclk_rec["mfma_peak_at_median_tflops"] = round(peak * sclk_rec["median"] /
-                                                       MAX_SCLK_MHZ, 1)
-        sclk_rec["frac_of_that_peak"] = round(achieved / sclk_rec["mfma_peak_at_median_tflops"], 4)
+    sclk_rec = clock_scaled_peak(sclk.summary(), peak, achieved)
     mfma_bound = flops / hbm_bytes > peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),

@@ -55,3 +55,20 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_clock_scaled_peak_never_above_one():
+    """A fraction of the clock-scaled peak above 1 cannot be a measurement (the sampled clock
+    lagged the hardware): it is withheld, with a note, instead of being printed."""
+    rec = bench.clock_scaled_peak({"median": 800.0}, 2500.0, 1100.0)
+    assert rec["frac_of_that_peak"] is None and "note" in rec
+    rec = bench.clock_scaled_peak({"median": 1800.0}, 2500.0, 1100.0)
+    assert rec["frac_of_that_peak"] == round(1100.0 / (2500.0 * 1800.0 / 2400.0), 4) <= 1.0
+    assert bench.clock_scaled_peak(None, 2500.0, 1.0) is None
+
+
+def test_clock_sampler_drops_samples_before_start():
+    s = bench.SclkSampler(period_s=0.001, started=lambda: False)
+    s.path = __file__  # any readable file: no '*' line, so nothing is parsed
+    s.samples.clear()
+    assert s.summary() is None
