@@ -67,10 +67,22 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     Inputs here are finite Gaussian draws, so the NaN case of the rounding is not needed.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    u = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    return u.astype(np.uint16)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat, fo = x.reshape(-1).view(np.uint32), out.reshape(-1)
+    step = min(flat.size, 1 << 20)
+    ubuf, lbuf = np.empty(step, np.uint32), np.empty(step, np.uint32)
+    for a in range(0, flat.size, step):  # in pieces, through two reused buffers
+        n = min(step, flat.size - a)
+        u, lsb = ubuf[:n], lbuf[:n]
+        np.copyto(u, flat[a:a + n])
+        np.right_shift(u, np.uint32(16), out=lsb)
+        np.bitwise_and(lsb, np.uint32(1), out=lsb)
+        # no wrap-around: the largest finite or infinite pattern plus 0x8000 stays below 2^32
+        u += np.uint32(0x7FFF)
+        u += lsb
+        u >>= np.uint32(16)
+        fo[a:a + n] = u
+    return out
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
