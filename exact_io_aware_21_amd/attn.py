@@ -9,7 +9,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# ATTN_LIB_PATH selects another build of the same library (the tests load the race-check and
+# AddressSanitizer debug builds this way, each in a process of its own).
+LIB_PATH = os.environ.get("ATTN_LIB_PATH") or \
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 # variant bits and codes, as in include/attn.h
 ATTN_MASK_NONE = 0

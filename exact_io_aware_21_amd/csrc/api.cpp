@@ -32,6 +32,7 @@ int fail(int code, const char *fmt, ...) {
 constexpr uint32_t kKnownBits = 0xFu | ATTN_MOD_ALIBI | ATTN_MOD_SOFTCAP | ATTN_PREC_FP8;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+char g_arch_name[kMaxDevices][64];         // written before g_arch_ok is set to -1
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -197,9 +198,11 @@ int check_device() {
     return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "no HIP device available");
   }
   if (dev < kMaxDevices) {
-    const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    const int c = g_arch_ok[dev].load(std::memory_order_acquire);
     if (c == 1) return ATTN_OK;
-    if (c == -1) return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+    if (c == -1)
+      return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device %d is %s, not gfx950", dev,
+                  g_arch_name[dev]);
   }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
@@ -212,7 +215,10 @@ int check_device() {
   const char *ov = std::getenv("ATTN_TEST_ARCH_OVERRIDE");
   const char *arch = (ov && *ov) ? ov : prop.gcnArchName;
   const bool ok = std::strncmp(arch, "gfx950", 6) == 0;
-  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+  if (dev < kMaxDevices) {
+    if (!ok) std::snprintf(g_arch_name[dev], sizeof g_arch_name[dev], "%s", arch);
+    g_arch_ok[dev].store(ok ? 1 : -1, std::memory_order_release);
+  }
   if (!ok) return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device %d is %s, not gfx950", dev, arch);
   return ATTN_OK;
 }

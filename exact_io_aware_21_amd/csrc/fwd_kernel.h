@@ -57,8 +57,38 @@
 __device__ float attn_score_mod(float s, int b, int h, int i, int j, const float *p);
 __device__ bool attn_mask_mod(int b, int i, int j, const float *p);
 
+// Race-check build (ATTN_RACE_CHECK=1, a debug library only): every LDS tile word starts as a
+// pattern that is NaN as bf16, as fp16 and as each of its two E4M3 bytes, so a read of a slot no
+// copy has filled poisons the output; every wait of the copy ring drains all outstanding memory
+// operations and every barrier in the loop is a full workgroup barrier with a memory fence, so
+// no copy is in flight across a barrier.  Its outputs must equal the pipelined build's bit for
+// bit: a miscounted wait, or a copy landing in a buffer still being read, shows up as a
+// difference (or a NaN) there.
+#ifndef ATTN_RACE_CHECK
+#define ATTN_RACE_CHECK 0
+#endif
+
 namespace attn {
 namespace {
+
+// Waits until at most the copies the immediate allows are outstanding (all of them in the
+// race-check build).
+template <int IMM>
+__device__ __forceinline__ void ring_wait() {
+  if constexpr (ATTN_RACE_CHECK)
+    __builtin_amdgcn_s_waitcnt(0);
+  else
+    __builtin_amdgcn_s_waitcnt(IMM);
+}
+
+// The barriers of the loop: bare (copies stay in flight across them), or full in the
+// race-check build.
+__device__ __forceinline__ void ring_barrier() {
+  if constexpr (ATTN_RACE_CHECK)
+    __syncthreads();
+  else
+    __builtin_amdgcn_s_barrier();
+}
 
 constexpr int kModScore = 1;  // MOD bit: attn_score_mod replaces the scaled score
 constexpr int kModMask = 2;   // MOD bit: attn_mask_mod decides the element mask
@@ -601,6 +631,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       const uint32_t bytes = isk ? (uint32_t)(rows * KROW) : (g < NJ && !vzero) ? vbytes : 0u;
       copy16_to_lds(base, bytes, dvo[r], buf + min(g, NJ) * 512);
     };
+    if constexpr (ATTN_RACE_CHECK) {
+      constexpr int NW = (NJ + 1) * 512 / 2;  // 32-bit words per buffer
+      for (int i = tid; i < NW; i += NT) {
+        ((uint32_t *)sB0)[i] = 0x7FFF7FFFu;
+        ((uint32_t *)sB1)[i] = 0x7FFF7FFFu;
+        ((uint32_t *)sB2)[i] = 0x7FFF7FFFu;
+        ((uint32_t *)sB3)[i] = 0x7FFF7FFFu;
+      }
+      __syncthreads();
+    }
     // Pairs 0 (K_0 and a zero V^T_{-1}: P = 0 in the first M-phase), 1 and 2.
 #pragma unroll
     for (int r = 0; r < NDMA; ++r) copy_item(r, sB0, kt_cur, kt_cur, true);
@@ -628,20 +668,20 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       };
       if constexpr (G == 0) {
         mphase(mp);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NDMA));  // pair k + 1: issued in k - 2
-        __builtin_amdgcn_s_barrier();
+        ring_wait<waitcnt_vm(2 * NDMA)>();  // pair k + 1: issued in k - 2
+        ring_barrier();
         if (k < T) vphase(kt_cur, sk_cur);
         advance(k);
         prefetch(nb);
       } else {
         if (k >= 1) vphase(kt_prev, sk_prev);
         prefetch(rb);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));  // pair k + 1: issued in k - 2
-        __builtin_amdgcn_s_barrier();
+        ring_wait<waitcnt_vm(NDMA)>();  // pair k + 1: issued in k - 2
+        ring_barrier();
         mphase(mp);
         advance(k);
       }
-      __builtin_amdgcn_s_barrier();
+      ring_barrier();
     };
     auto run = [&](auto gc) {
       for (int k = 0;; k += 4) {
