@@ -176,3 +176,13 @@ def test_fp8_deterministic():
     a, la = run_fp8(w, inp, True)
     b, lb = run_fp8(w, inp, True)
     assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, -1.0 / 128 ** 0.5])
+def test_fp8_scale_not_positive(scale):
+    """scale = 0 and scale < 0 select the FP8 instance that scales every score before its
+    maximum is taken."""
+    for mask, d in (("causal", 128), ("none", 64)):
+        w = inputs.Workload(f"f8_scale{scale:+.3f}_{mask}", B=1, H=2, N=333, d=d, mask=mask,
+                            seed=1610, scale=scale)
+        check(w, inputs.make_inputs(w))
