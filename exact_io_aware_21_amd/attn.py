@@ -36,7 +36,9 @@ ATTN_MODF_MASK = 2
 MASK_BITS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
              "window": ATTN_MASK_SLIDING_WINDOW, "document": ATTN_MASK_DOCUMENT}
 
-EXPORTS = ("attn_fwd", "attn_workspace_size", "attn_tile_shape", "attn_block_table",
+ATTN_NOALLOC_SCRATCH_BYTES = 64 << 20  # the static scratch of attn_fwd_noalloc
+
+EXPORTS = ("attn_fwd", "attn_fwd_noalloc", "attn_workspace_size", "attn_tile_shape", "attn_block_table",
            "attn_block_table_host", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
            "attn_decode_workspace_size", "attn_quantize_fp8", "attn_mod_create",
            "attn_mod_destroy", "attn_mod_workspace_size", "attn_fwd_mod", "attn_fwd_mod_cached",
@@ -74,6 +76,8 @@ def lib():
         L.attn_fwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_f,
                                c_u32, P, c_vp]
         L.attn_fwd.restype = c_int
+        L.attn_fwd_noalloc.argtypes = L.attn_fwd.argtypes
+        L.attn_fwd_noalloc.restype = c_int
         L.attn_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_u32]
         L.attn_workspace_size.restype = ctypes.c_size_t
         L.attn_tile_shape.argtypes = [c_int, c_u32, ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
@@ -209,13 +213,9 @@ def alloc_workspace(B, H, N, d, variant, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def attn_fwd(q, k, v, o, lse, scale, variant, window=0, softcap=0.0, alibi_slopes=None,
-             doc_offsets=None, workspace=None, stream=None, timing_events=None):
-    """Calls attn_fwd on torch tensors q, k, v ([B,H,N,d] bf16), o (bf16 or fp32), lse (fp32 or
-    None).  alibi_slopes: fp32 [H]; doc_offsets: int32 [B, max_docs+1]; workspace: uint8 tensor
-    of at least attn_workspace_size bytes (allocated here when None); timing_events: optional
-    pair of torch.cuda.Event(enable_timing=True), each recorded once beforehand (torch creates
-    the underlying event on its first record), recorded again around the main kernel."""
+def _fwd_args(q, k, v, o, lse, variant, window, softcap, alibi_slopes, doc_offsets, workspace,
+              timing_events):
+    """Checks the forward arguments; returns (B, H, N, d, params, keepalive)."""
     import torch
     B, H, N, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -229,8 +229,6 @@ def attn_fwd(q, k, v, o, lse, scale, variant, window=0, softcap=0.0, alibi_slope
         raise ValueError("lse must be a contiguous fp32 [B,H,N] tensor")
     _on_device(q.device, q=q, k=k, v=v, o=o, lse=lse)
     _check_aux(q.device, B, H, variant, alibi_slopes, doc_offsets, workspace)
-    if workspace is None:
-        workspace = alloc_workspace(B, H, N, d, variant, q.device)
     p = make_params(window, softcap, alibi_slopes, doc_offsets,
                     ATTN_O_F32 if o.dtype == torch.float32 else ATTN_O_BF16, workspace)
     ev = None
@@ -239,8 +237,36 @@ def attn_fwd(q, k, v, o, lse, scale, variant, window=0, softcap=0.0, alibi_slope
             raise ValueError("timing events must have been recorded once before use")
         ev = (ctypes.c_void_p * 2)(timing_events[0].cuda_event, timing_events[1].cuda_event)
         p.timing_events = ctypes.cast(ev, ctypes.c_void_p)
+    return B, H, N, d, p, ev
+
+
+def attn_fwd(q, k, v, o, lse, scale, variant, window=0, softcap=0.0, alibi_slopes=None,
+             doc_offsets=None, workspace=None, stream=None, timing_events=None):
+    """Calls attn_fwd on torch tensors q, k, v ([B,H,N,d] bf16), o (bf16 or fp32), lse (fp32 or
+    None).  alibi_slopes: fp32 [H]; doc_offsets: int32 [B, max_docs+1]; workspace: uint8 tensor
+    of at least attn_workspace_size bytes (allocated here when None); timing_events: optional
+    pair of torch.cuda.Event(enable_timing=True), each recorded once beforehand (torch creates
+    the underlying event on its first record), recorded again around the main kernel."""
+    B, H, N, d, p, _ev = _fwd_args(q, k, v, o, lse, variant, window, softcap, alibi_slopes,
+                                   doc_offsets, workspace, timing_events)
+    if workspace is None:
+        workspace = alloc_workspace(B, H, N, d, variant, q.device)
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                           float(scale), variant, ctypes.byref(p), _stream(stream)))
+    return o, lse
+
+
+def attn_fwd_noalloc(q, k, v, o, lse, scale, variant, window=0, softcap=0.0, alibi_slopes=None,
+                     doc_offsets=None, stream=None, timing_events=None):
+    """Calls attn_fwd_noalloc: attn_fwd with the library's static scratch as the workspace, for
+    callers that cannot allocate (no workspace argument; shapes whose workspace would exceed
+    ATTN_NOALLOC_SCRATCH_BYTES are refused).  Calls that can overlap on one GPU race."""
+    B, H, N, d, p, _ev = _fwd_args(q, k, v, o, lse, variant, window, softcap, alibi_slopes,
+                                   doc_offsets, None, timing_events)
+    _check(lib().attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                  float(scale), variant, ctypes.byref(p), _stream(stream)))
     return o, lse
 
 

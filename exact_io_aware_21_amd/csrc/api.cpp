@@ -386,9 +386,13 @@ int attn_block_table(int B, int H, int N, int d, uint32_t variant, const attn_pa
   return ATTN_OK;
 }
 
-int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
-             int d, float scale, uint32_t variant, const attn_params *params, void *stream) {
-  Shape s;
+}  // extern "C"
+
+namespace {
+
+// Validation of attn_fwd's arguments other than the workspace (no HIP call); fills s.
+int fwd_check(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+              int N, int d, float scale, uint32_t variant, const attn_params *params, Shape &s) {
   int rc = check_shape(B, H, N, d, variant, s);
   if (rc) return rc;
   if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
@@ -396,17 +400,15 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
     return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
   if (lse && ((uintptr_t)lse & 3u)) return fail(ATTN_ERR_INVALID_ARG, "lse misaligned");
   if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
-  if ((rc = check_params(s, variant, params, true))) return rc;
-  const WsLayout wl = ws_layout(s);
-  if (!params->workspace || ((uintptr_t)params->workspace & 255u))
-    return fail(ATTN_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
-  if (params->workspace_bytes < wl.total)
-    return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", params->workspace_bytes,
-                wl.total);
-  if ((rc = check_device())) return rc;
+  return check_params(s, variant, params, false);
+}
 
-  const hipStream_t st = (hipStream_t)stream;
-  char *ws = (char *)params->workspace;
+// The launches of one forward pass on validated arguments, with the workspace at ws (at least
+// ws_layout(s).total bytes).  Launches only: allocates nothing.
+int fwd_launch(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+               int N, int d, float scale, uint32_t variant, const attn_params *params,
+               const Shape &s, char *ws, hipStream_t st) {
+  const WsLayout wl = ws_layout(s);
   uint16_t *vt = (uint16_t *)(ws + wl.vt);
   if (attn::launch_vt_pack((const uint16_t *)v, vt, B * H, N, s.Npad, d, st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "V transpose kernel launch failed");
@@ -468,6 +470,78 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
   if (ev && hipEventRecord((hipEvent_t)ev[1], st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "timing event record failed");
   return ATTN_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// The workspace of attn_fwd_noalloc: a file-scope device array (each device holds its own copy
+// from the library's load on it until the process ends).  In host code `scratch` only names the
+// symbol; its device address is resolved once per device with hipGetSymbolAddress, with that
+// device current, and only that address is ever handed to a kernel.
+constexpr size_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+char *g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (resolved on the device's first call).
+int scratch_on_current_device(char **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "no usable current device");
+  }
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(ATTN_ERR_LAUNCH, "resolving the static scratch array on device %d failed", dev);
+    }
+    if ((uintptr_t)p & 255u)
+      return fail(ATTN_ERR_LAUNCH, "the static scratch array is not 256-byte aligned");
+    g_scratch_ptr[dev] = (char *)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
+             int d, float scale, uint32_t variant, const attn_params *params, void *stream) {
+  Shape s;
+  int rc = fwd_check(q, k, v, o, lse, B, H, N, d, scale, variant, params, s);
+  if (rc) return rc;
+  if (!params) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+  const WsLayout wl = ws_layout(s);
+  if (!params->workspace || ((uintptr_t)params->workspace & 255u))
+    return fail(ATTN_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (params->workspace_bytes < wl.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", params->workspace_bytes,
+                wl.total);
+  if ((rc = check_device())) return rc;
+  return fwd_launch(q, k, v, o, lse, B, H, N, d, scale, variant, params, s,
+                    (char *)params->workspace, (hipStream_t)stream);
+}
+
+int attn_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                     int H, int N, int d, float scale, uint32_t variant,
+                     const attn_params *params, void *stream) {
+  Shape s;
+  int rc = fwd_check(q, k, v, o, lse, B, H, N, d, scale, variant, params, s);
+  if (rc) return rc;
+  if (!params) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+  const size_t need = ws_layout(s).total;
+  if (need > kScratchBytes)
+    return fail(ATTN_ERR_WORKSPACE,
+                "this shape needs %zu bytes of workspace; the static scratch holds %zu "
+                "(use attn_fwd with a caller workspace)", need, kScratchBytes);
+  if ((rc = check_device())) return rc;
+  char *ws = nullptr;
+  if ((rc = scratch_on_current_device(&ws))) return rc;
+  return fwd_launch(q, k, v, o, lse, B, H, N, d, scale, variant, params, s, ws,
+                    (hipStream_t)stream);
 }
 
 size_t attn_bwd_workspace_size(int B, int H, int N, int d, uint32_t variant) {

@@ -119,6 +119,25 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
              int d, float scale, uint32_t variant, const attn_params *params, void *stream);
 
 /*
+ * attn_fwd_noalloc -- attn_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same forward pass,
+ * kernels and results, with the workspace taken from a static device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES bytes inside the library instead of params->workspace.
+ *   Arguments, outputs and errors as attn_fwd; params is required, but its workspace and
+ *   workspace_bytes fields are ignored.  A shape whose attn_workspace_size exceeds
+ *   ATTN_NOALLOC_SCRATCH_BYTES is rejected with ATTN_ERR_WORKSPACE before any HIP call.
+ *   The call allocates nothing: each device holds its own copy of the array from the library's
+ *   load on it until the process ends, and its address is resolved once, on the device's first
+ *   call.  Every call on a device uses that device's one array and nothing is carried between
+ *   calls, so calls that can overlap on one device (other streams, other threads) race and must
+ *   be serialised by the caller.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int attn_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                     int H, int N, int d, float scale, uint32_t variant,
+                     const attn_params *params, void *stream);
+
+/*
  * attn_workspace_size -- bytes of device workspace attn_fwd needs for this shape and variant
  * (0 on invalid arguments; no HIP call).  The caller allocates it once and passes it in
  * params->workspace, so that no call allocates: page "FlashAttention-3 y torch.compile ...",

@@ -440,3 +440,22 @@ def test_fwd_mod_cached_binding_needs_a_workspace(alibi_causal_mod):
     x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         alibi_causal_mod.fwd(x, x, x, x.clone(), None, 0.125, cached_table=True)
+
+
+def test_fwd_noalloc_validates_before_any_hip_call():
+    """attn_fwd_noalloc refuses, with no HIP call, a shape whose workspace exceeds the static
+    scratch (ATTN_ERR_WORKSPACE) and the argument errors attn_fwd refuses."""
+    L = attn.lib()
+    p = attn.attn_params()
+    big = (1, 32, 16384, 128)  # V^T alone is 128 MiB
+    assert attn.attn_workspace_size(*big, attn.ATTN_MASK_CAUSAL) > attn.ATTN_NOALLOC_SCRATCH_BYTES
+    rc = L.attn_fwd_noalloc(16, 16, 16, 16, None, *big, 0.1, attn.ATTN_MASK_CAUSAL,
+                            ctypes.byref(p), None)
+    assert rc == attn.ATTN_ERR_WORKSPACE
+    assert b"static scratch" in L.attn_last_error()
+    assert L.attn_fwd_noalloc(16, 16, 16, 16, None, 1, 1, 256, 64, 0.1, 0, None, None) == \
+        attn.ATTN_ERR_INVALID_ARG
+    assert L.attn_fwd_noalloc(16, 16, 16, 16, None, 1, 1, 256, 96, 0.1, 0, ctypes.byref(p),
+                              None) == attn.ATTN_ERR_INVALID_ARG
+    assert L.attn_fwd_noalloc(0, 16, 16, 16, None, 1, 1, 256, 64, 0.1, 0, ctypes.byref(p),
+                              None) == attn.ATTN_ERR_INVALID_ARG
