@@ -46,11 +46,12 @@ struct Shape {
 int check_shape(int B, int H, int N, int d, uint32_t variant, Shape &s) {
   if (B < 1 || H < 1 || N < 1) return fail(ATTN_ERR_INVALID_ARG, "B, H and N must be >= 1");
   if (N > (1 << 24)) return fail(ATTN_ERR_INVALID_ARG, "N must be <= 2^24");
-  if (d != 64 && d != 128) return fail(ATTN_ERR_INVALID_ARG, "d must be 64 or 128");
+  if (d != 64 && d != 128 && d != 256) return fail(ATTN_ERR_INVALID_ARG, "d must be 64, 128 or 256");
   if (variant & ~kKnownBits) return fail(ATTN_ERR_INVALID_ARG, "unknown variant bits");
   s.kind = variant & 0xFu;
   if (s.kind > ATTN_MASK_DOCUMENT) return fail(ATTN_ERR_INVALID_ARG, "unknown mask kind");
   s.fp8 = (variant & ATTN_PREC_FP8) != 0;
+  if (s.fp8 && d == 256) return fail(ATTN_ERR_INVALID_ARG, "ATTN_PREC_FP8 takes d 64 or 128");
   if (s.fp8 && (variant & (ATTN_MOD_ALIBI | ATTN_MOD_SOFTCAP)))
     return fail(ATTN_ERR_INVALID_ARG, "ATTN_PREC_FP8 takes no score modification");
   if (s.fp8 && (long long)B * H > 65535)
@@ -332,7 +333,10 @@ const char *attn_strerror(int code) {
 const char *attn_last_error(void) { return g_err; }
 
 int attn_tile_shape(int d, uint32_t variant, int *Br, int *Bc) {
-  if (d != 64 && d != 128) return fail(ATTN_ERR_INVALID_ARG, "d must be 64 or 128");
+  if (d != 64 && d != 128 && d != 256)
+    return fail(ATTN_ERR_INVALID_ARG, "d must be 64, 128 or 256");
+  if ((variant & ATTN_PREC_FP8) && d == 256)
+    return fail(ATTN_ERR_INVALID_ARG, "ATTN_PREC_FP8 takes d 64 or 128");
   if (variant & ~kKnownBits || (variant & 0xFu) > ATTN_MASK_DOCUMENT)
     return fail(ATTN_ERR_INVALID_ARG, "unknown variant bits");
   if (!Br || !Bc) return fail(ATTN_ERR_INVALID_ARG, "Br/Bc output pointer is NULL");
@@ -546,7 +550,7 @@ int attn_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float
 
 size_t attn_bwd_workspace_size(int B, int H, int N, int d, uint32_t variant) {
   Shape s;
-  if (check_shape(B, H, N, d, variant, s) != ATTN_OK || s.fp8) return 0;
+  if (check_shape(B, H, N, d, variant, s) != ATTN_OK || s.fp8 || d == 256) return 0;
   return bwd_layout(s).total;
 }
 
@@ -557,6 +561,7 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
   int rc = check_shape(B, H, N, d, variant, s);
   if (rc) return rc;
   if (s.fp8) return fail(ATTN_ERR_INVALID_ARG, "ATTN_PREC_FP8 is a forward-only variant");
+  if (d == 256) return fail(ATTN_ERR_INVALID_ARG, "the backward pass takes d 64 or 128");
   if ((long long)B * H > 65535) return fail(ATTN_ERR_INVALID_ARG, "B*H must be <= 65535");
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(ATTN_ERR_INVALID_ARG, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL");
@@ -727,7 +732,8 @@ int mod_create(const char *source, uint32_t flags, int d, attn_mod **out, char *
   if (!source) return fail(ATTN_ERR_INVALID_ARG, "source is NULL");
   if (flags == 0 || (flags & ~(uint32_t)(ATTN_MODF_SCORE | ATTN_MODF_MASK)))
     return fail(ATTN_ERR_INVALID_ARG, "flags must be a non-empty set of ATTN_MODF_SCORE, ATTN_MODF_MASK");
-  if (d != 64 && d != 128) return fail(ATTN_ERR_INVALID_ARG, "d must be 64 or 128");
+  if (d != 64 && d != 128 && d != 256)
+    return fail(ATTN_ERR_INVALID_ARG, "d must be 64, 128 or 256");
   std::string prog = "#include \"fwd_kernel.h\"\n#line 1 \"attn_mod_source\"\n";
   prog += source;
   char tail[1024];
@@ -905,9 +911,10 @@ int fwd_mod(const attn_mod *mc, const void *q, const void *k, const void *v, voi
   if (ev && hipEventRecord((hipEvent_t)ev[0], st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "timing event record failed");
   void *fargs[] = {&a};
+  // d = 256: two workgroups per (q-tile, head), one per half of the columns of O
   if (hipModuleLaunchKernel(m->fwd[dev][params->o_dtype == ATTN_O_F32 ? 1 : 0],
-                            (unsigned)(s.n_qt * B * H), 1, 1, 512, 1, 1, 0, st, fargs,
-                            nullptr) != hipSuccess) {
+                            (unsigned)(s.n_qt * B * H), d > 128 ? 2 : 1, 1, 512, 1, 1, 0, st,
+                            fargs, nullptr) != hipSuccess) {
     (void)hipGetLastError();
     return fail(ATTN_ERR_LAUNCH, "forward kernel launch failed");
   }

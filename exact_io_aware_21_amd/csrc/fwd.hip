@@ -98,12 +98,17 @@ hipError_t launch_out(bool out_f32, const FwdArgs &a, dim3 grid, hipStream_t s) 
 
 template <int D>
 hipError_t launch_d(const FwdInstance &in, const FwdArgs &a, dim3 grid, hipStream_t s) {
-  if (in.fp8) {
+  if constexpr (D > 128) {
+    // two workgroups per (q-tile, head): one for each half of the columns of O
+    grid.y = 2;
+    if (in.fp8) return hipErrorInvalidValue;
+  } else if (in.fp8) {
     if (in.alibi || in.softcap) return hipErrorInvalidValue;
     if (in.pos_scale) return launch_out<D, false, false, true, true>(in.out_f32, a, grid, s);
     return launch_out<D, false, false, false, true>(in.out_f32, a, grid, s);
   }
   if (in.alibi && in.softcap) return launch_out<D, true, true, false>(in.out_f32, a, grid, s);
+  // (d = 256 reaches this point only without FP8)
   if (in.alibi) return launch_out<D, true, false, false>(in.out_f32, a, grid, s);
   if (in.softcap) return launch_out<D, false, true, false>(in.out_f32, a, grid, s);
   if (in.pos_scale) return launch_out<D, false, false, true>(in.out_f32, a, grid, s);
@@ -115,7 +120,9 @@ hipError_t launch_d(const FwdInstance &in, const FwdArgs &a, dim3 grid, hipStrea
 hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Npad, int d,
                           hipStream_t stream) {
   dim3 grid(Npad / 64, BH);
-  if (d == 128)
+  if (d == 256)
+    vt_pack_kernel<256><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
+  else if (d == 128)
     vt_pack_kernel<128><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
   else
     vt_pack_kernel<64><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
@@ -130,6 +137,7 @@ hipError_t launch_block_table(MaskDesc m, const int32_t *offs_all, int Bm, int n
 
 hipError_t launch_fwd(const FwdInstance &in, const FwdArgs &a, hipStream_t stream) {
   const dim3 grid((unsigned)a.n_qt * (unsigned)(a.B * a.H));
+  if (in.d == 256) return launch_d<256>(in, a, grid, stream);
   if (in.d == 128) return launch_d<128>(in, a, grid, stream);
   return launch_d<64>(in, a, grid, stream);
 }

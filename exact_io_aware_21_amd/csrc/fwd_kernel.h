@@ -111,10 +111,16 @@ constexpr int kModMask = 2;   // MOD bit: attn_mask_mod decides the element mask
 template <int D, bool ALIBI, bool SOFTCAP, bool POS, bool OUTF32, bool FP8, int MOD>
 __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   constexpr int NT = 512;                // threads per workgroup
+  // Head dimension 256: the scores need all of d, but 256 columns of O do not fit the register
+  // file beside Q^T at two waves per SIMD, so each workgroup forms the scores over all of d and
+  // accumulates one half of O, DV = 128 columns (blockIdx.y picks the half); the tiles then take
+  // three LDS buffers instead of four.
+  constexpr int DV = D > 128 ? 128 : D;  // columns of O (rows of V^T) of this workgroup
+  constexpr int NB = D > 128 ? 3 : 4;    // LDS buffers of the copy ring
   constexpr int KCH = D / 8;             // 16-byte chunks per K row
   constexpr int VCH = kBc / 8;           // 16-byte chunks per V^T row
   constexpr int NKS = D / 16;            // k-steps of the score product
-  constexpr int NDB = D / 32;            // 32-column blocks of O
+  constexpr int NDB = DV / 32;           // 32-column blocks of O
   constexpr int KP = pitch(D);           // LDS pitch of a K row (keys x D)
   constexpr int VP = pitch(kBc);         // LDS pitch of a V^T row (D x keys)
   constexpr int KP8 = D + 16;            // LDS pitch of an FP8 K row, bytes
@@ -129,13 +135,22 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   // where a read needs one).  The spare row takes the copy instructions a wave issues beyond
   // the tiles' share, which read nothing and write zeros.  FP8 K rows are KP8 bytes.
   constexpr int SPK = FP8 ? KP8 / 16 : KP / 8, SPV = VP / 8;  // 16-byte slots per LDS row
-  constexpr int NJK = kBc * SPK / 64, NJV = D * SPV / 64;  // copy instructions per tile
+  constexpr int NJK = kBc * SPK / 64, NJV = DV * SPV / 64;  // copy instructions per tile
   constexpr int NJ = NJK + NJV;
-  static_assert(kBc * SPK % 64 == 0 && D * SPV % 64 == 0, "tiles must fill whole copy rows");
+  static_assert(kBc * SPK % 64 == 0 && DV * SPV % 64 == 0, "tiles must fill whole copy rows");
+  static_assert(!FP8 || D <= 128, "FP8 instances are built for d <= 128");
   __shared__ __attribute__((aligned(16))) uint16_t sB0[(NJ + 1) * 512];
   __shared__ __attribute__((aligned(16))) uint16_t sB1[(NJ + 1) * 512];
   __shared__ __attribute__((aligned(16))) uint16_t sB2[(NJ + 1) * 512];
-  __shared__ __attribute__((aligned(16))) uint16_t sB3[(NJ + 1) * 512];
+  __shared__ __attribute__((aligned(16))) uint16_t sB3[NB > 3 ? (NJ + 1) * 512 : 8];
+  auto buf = [&](auto bc) -> uint16_t * {
+    constexpr int Bi = decltype(bc)::value;
+    if constexpr (Bi == 0) return sB0;
+    if constexpr (Bi == 1) return sB1;
+    if constexpr (Bi == 2) return sB2;
+    if constexpr (Bi == 3) return sB3;
+    return nullptr;
+  };
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   // Phase group: of the two waves the dispatcher placed on a SIMD, the lower-numbered one is
@@ -156,7 +171,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   // share most of their keys (a sliding window ran 5 % slower interleaved).
   const bool lpt = MOD == 0 && (a.kind == kMaskCausal || a.kind == kMaskDocument);
   int qx, bh;
-  place_block(blockIdx.x, gridDim.x, a.n_qt, lpt, (size_t)4 * a.N * D, qx, bh);
+  place_block(blockIdx.x, gridDim.x, a.n_qt, lpt, (size_t)2 * a.N * (D + DV), qx, bh);
+  const int vcol0 = D > 128 ? (int)blockIdx.y * DV : 0;  // first column of O of this workgroup
   // Masked kinds have longer key lists for later q-tiles: start those first.
   const int qt = (a.kind != kMaskNone || (MOD & kModMask)) ? a.n_qt - 1 - qx : qx;
   const int b = bh / a.H, h = bh - b * a.H;
@@ -258,7 +274,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   constexpr int KCHR = KROW / 16;        // 16-byte chunks per K row
   const char *kbytes = FP8 ? (const char *)(a.k8 + (size_t)bh * N * D)
                            : (const char *)(a.k + (size_t)bh * N * D);
-  const uint16_t *vbase = a.vt + (size_t)bh * D * a.Npad;
+  const uint16_t *vbase = a.vt + ((size_t)bh * D + vcol0) * a.Npad;
 
   const float slopeL = ALIBI ? a.slopes[h] * 1.4426950408889634f : 0.f;
   // Soft-cap without ALiBi keeps u = 1 / (1 + e^{2 s / cap}) per score instead of the capped
@@ -587,16 +603,17 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     sk_next = sk_n2;
   };
   {
-    // Buffer-to-LDS copies through four LDS buffers: buffer t mod 4 holds the pair
-    // (K_t, V^T_{t-1}), which is what the M-phase of iteration t reads.  In iteration k every
-    // wave issues, between the MFMAs of its own M-phase, its share of the copies of pair k + 3
-    // (K_{k+3}, V^T_{k+2}) into the buffer last read in iteration k - 1.  Before the barrier in
-    // the middle of iteration k each wave waits for its copies of pair k + 1 (issued in
-    // iteration k - 2; vmcnt counts the copies in issue order), so after that barrier pair
-    // k + 1 is whole and the wave whose next M-phase reads it issues that phase's first
-    // fragment reads at the end of its V-phase, across the next barrier.  The copies are in
-    // flight for more than an iteration and nothing else waits for them: the barriers inside
-    // the loop are bare s_barrier instructions (a workgroup fence would wait for every copy).
+    // Buffer-to-LDS copies through NB LDS buffers (four; three for d = 256): buffer t mod NB
+    // holds the pair (K_t, V^T_{t-1}), which is what the M-phase of iteration t reads.  In
+    // iteration k every wave issues, between the MFMAs of its own M-phase, its share of the
+    // copies of pair k + NB - 1 (K_{k+NB-1}, V^T_{k+NB-2}) into the buffer last read in
+    // iteration k - 1.  Before the barrier in the middle of iteration k each wave waits for its
+    // copies of pair k + 1 (issued in iteration k + 2 - NB; vmcnt counts the copies in issue
+    // order), so after that barrier pair k + 1 is whole and the wave whose next M-phase reads
+    // it issues that phase's first fragment reads at the end of its V-phase, across the next
+    // barrier.  With four buffers the copies are in flight for more than an iteration; with
+    // three, for about one.  Nothing else waits for them: the barriers inside the loop are bare
+    // s_barrier instructions (a workgroup fence would wait for every copy).
     //
     // A tile row is SPK (K) or SPV (V^T) 16-byte slots, the last one padding; copy instruction
     // g of a pair fills slots 64 g .. 64 g + 63 of its buffer (K tile first).  Wave w issues
@@ -623,7 +640,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     auto copy_item = [&](int r, uint16_t *buf, int ktk, int ktv, bool vzero) {
       const int g = wv + 8 * r;
       const int rows = min(kBc, N - ktk * kBc);
-      const size_t left = ((size_t)D * a.Npad - (size_t)ktv * kBc) * 2;
+      const size_t left = ((size_t)(D - vcol0) * a.Npad - (size_t)ktv * kBc) * 2;
       const uint32_t vbytes = (uint32_t)(left < 0xFFFFFFFFull ? left : 0xFFFFFFFFull);
       const bool isk = g < NJK;
       const char *base = isk ? kbytes + (size_t)ktk * kBc * KROW
@@ -637,38 +654,46 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
         ((uint32_t *)sB0)[i] = 0x7FFF7FFFu;
         ((uint32_t *)sB1)[i] = 0x7FFF7FFFu;
         ((uint32_t *)sB2)[i] = 0x7FFF7FFFu;
-        ((uint32_t *)sB3)[i] = 0x7FFF7FFFu;
+        if constexpr (NB > 3) ((uint32_t *)sB3)[i] = 0x7FFF7FFFu;
       }
       __syncthreads();
     }
-    // Pairs 0 (K_0 and a zero V^T_{-1}: P = 0 in the first M-phase), 1 and 2.
+    // Pairs 0 (K_0 and a zero V^T_{-1}: P = 0 in the first M-phase) .. NB - 2.
 #pragma unroll
     for (int r = 0; r < NDMA; ++r) copy_item(r, sB0, kt_cur, kt_cur, true);
 #pragma unroll
     for (int r = 0; r < NDMA; ++r) copy_item(r, sB1, kt_next, kt_cur, false);
+    if constexpr (NB > 3) {
 #pragma unroll
-    for (int r = 0; r < NDMA; ++r) copy_item(r, sB2, kt_n2, kt_next, false);
+      for (int r = 0; r < NDMA; ++r) copy_item(r, sB2, kt_n2, kt_next, false);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (grp == 0) prefetch(sB0);
 
-    // Iteration k with B = k mod 4 and phase group G, every buffer named statically.
+    // Iteration k with B = k mod NB and phase group G, every buffer named statically.
     auto iteration = [&](int k, auto bc, auto gc) {
       constexpr int B = decltype(bc)::value, G = decltype(gc)::value;
-      constexpr int B1 = (B + 1) % 4, B3 = (B + 3) % 4;
-      uint16_t *rb = B == 0 ? sB0 : B == 1 ? sB1 : B == 2 ? sB2 : sB3;       // pair k
-      uint16_t *nb = B1 == 0 ? sB0 : B1 == 1 ? sB1 : B1 == 2 ? sB2 : sB3;    // pair k + 1
-      uint16_t *wb = B3 == 0 ? sB0 : B3 == 1 ? sB1 : B3 == 2 ? sB2 : sB3;    // pair k + 3
-      auto item = [&](int r) { copy_item(r, wb, kt_n3, kt_n2, false); };
+      uint16_t *rb = buf(IntC<B>{});                 // pair k
+      uint16_t *nb = buf(IntC<(B + 1) % NB>{});      // pair k + 1
+      uint16_t *wb = buf(IntC<(B + NB - 1) % NB>{});  // pair k + NB - 1
+      auto item = [&](int r) {
+        if constexpr (NB == 4)
+          copy_item(r, wb, kt_n3, kt_n2, false);
+        else
+          copy_item(r, wb, kt_n2, kt_next, false);
+      };
       auto mp = [&] {
         if constexpr (FP8)
           mphase_fp8(rb, rb + NJK * 512, item, IntC<NDMA>{});
         else
           mphase_bf16(rb, rb + NJK * 512, item, IntC<NDMA>{});
       };
+      // Pair k + 1 was issued in iteration k + 2 - NB; the copies of the younger iterations
+      // (and, in group 0, of this one) may stay in flight.
       if constexpr (G == 0) {
         mphase(mp);
-        ring_wait<waitcnt_vm(2 * NDMA)>();  // pair k + 1: issued in k - 2
+        ring_wait<waitcnt_vm((NB - 2) * NDMA)>();
         ring_barrier();
         if (k < T) vphase(kt_cur, sk_cur);
         advance(k);
@@ -676,7 +701,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       } else {
         if (k >= 1) vphase(kt_prev, sk_prev);
         prefetch(rb);
-        ring_wait<waitcnt_vm(NDMA)>();  // pair k + 1: issued in k - 2
+        ring_wait<waitcnt_vm((NB - 3) * NDMA)>();
         ring_barrier();
         mphase(mp);
         advance(k);
@@ -684,15 +709,17 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       ring_barrier();
     };
     auto run = [&](auto gc) {
-      for (int k = 0;; k += 4) {
+      for (int k = 0;; k += NB) {
         iteration(k, IntC<0>{}, gc);
         if (k >= T) break;
         iteration(k + 1, IntC<1>{}, gc);
         if (k + 1 >= T) break;
-        iteration(k + 2, IntC<2>{}, gc);
+        iteration(k + 2, IntC<2 % NB>{}, gc);
         if (k + 2 >= T) break;
-        iteration(k + 3, IntC<3>{}, gc);
-        if (k + 3 >= T) break;
+        if constexpr (NB > 3) {
+          iteration(k + 3, IntC<3 % NB>{}, gc);
+          if (k + 3 >= T) break;
+        }
       }
     };
     if (grp == 0)
@@ -705,7 +732,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_ok) {
-    const size_t obase = ((size_t)bh * N + qrow) * D + 16 * hf;
+    const size_t obase = ((size_t)bh * N + qrow) * D + vcol0 + 16 * hf;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const f32x16 o = oacc[db] * inv;
@@ -722,7 +749,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
         *(bf16x8 *)(op + 8) = __builtin_convertvector(o1, bf16x8);
       }
     }
-    if (a.lse && hf == 0)
+    if (a.lse && hf == 0 && vcol0 == 0)
       a.lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }

@@ -459,3 +459,35 @@ def test_fwd_noalloc_validates_before_any_hip_call():
                               None) == attn.ATTN_ERR_INVALID_ARG
     assert L.attn_fwd_noalloc(0, 16, 16, 16, None, 1, 1, 256, 64, 0.1, 0, ctypes.byref(p),
                               None) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_head_dim_256_contract():
+    """d = 256 is accepted by the forward pass, its tables and runtime-compiled modifications on
+    the same 256 x 64 tiles; the backward pass and the FP8 variant refuse it."""
+    assert attn.attn_tile_shape(256, attn.ATTN_MASK_CAUSAL) == (256, 64)
+    with pytest.raises(attn.AttnError):
+        attn.attn_tile_shape(256, attn.ATTN_PREC_FP8)
+    al = lambda x: (x + 255) // 256 * 256
+    assert attn.attn_workspace_size(1, 2, 300, 256, 0) == al(2 * 256 * 320 * 2)
+    assert attn.attn_workspace_size(1, 2, 300, 256, attn.ATTN_PREC_FP8) == 0
+    assert attn.attn_bwd_workspace_size(1, 2, 300, 256, 0) == 0
+    L = attn.lib()
+    p = attn.attn_params()
+    p.workspace, p.workspace_bytes = 4096, 1 << 30
+    z = [16] * 9
+    assert L.attn_bwd(*z, 1, 1, 64, 256, 0.1, 0, ctypes.byref(p), None) == \
+        attn.ATTN_ERR_INVALID_ARG
+    assert L.attn_fwd(16, 16, 16, 16, None, 1, 1, 64, 256, 0.1, attn.ATTN_PREC_FP8,
+                      ctypes.byref(p), None) == attn.ATTN_ERR_INVALID_ARG
+    # the host block table is defined on the same tiles for d = 256
+    ref = oracle.tile_table(1000, 256, 64, "causal")
+    got = attn.attn_block_table_host(1, 1, 1000, 256, attn.ATTN_MASK_CAUSAL)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g, r)
+
+
+def test_mod_compiles_for_head_dim_256():
+    m = attn.AttnMod("__device__ bool attn_mask_mod(int b, int i, int j, const float *p)"
+                     " { return j <= i; }", attn.ATTN_MODF_MASK, 256)
+    assert m.workspace_size(1, 2, 300) > 0
+    m.close()
