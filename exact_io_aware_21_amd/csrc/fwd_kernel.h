@@ -182,7 +182,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   const bool q_ok = qrow < N;
   const MaskDesc md{a.kind, N, a.window, a.offs ? a.offs + (size_t)b * (a.max_docs + 1) : nullptr,
                     a.max_docs};
-  int lo = 1, hi = 0;  // empty interval for rows beyond N
+  int lo = N + kBc, hi = N + kBc;  // rows beyond N: a single key past every tile (all masked)
   if (q_ok) {
     lo = row_lo(md, qrow);
     hi = row_hi(md, qrow);
@@ -280,7 +280,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   // Soft-cap without ALiBi keeps u = 1 / (1 + e^{2 s / cap}) per score instead of the capped
   // score t = cap (1 - 2 u) (base 2: capL - 2 capL u): the probability is then one FMA and one
   // exponential, exp2(capL - m - 2 capL u), and the tile maximum of t is taken as the minimum
-  // of u.  A masked score is u = +inf.
+  // of u.  A masked score is u = +inf.  (An odd polynomial for tanh on the FMA pipe, taking
+  // two transcendentals per score off, ran 10 % slower: these kernels are bound by vector
+  // issue, not by the transcendental unit.)
   constexpr bool UCAP = SOFTCAP && !ALIBI && !POS && MOD == 0;
   constexpr float kMasked = UCAP ? INFINITY : -INFINITY;
   float m_run = -INFINITY, l_run = 0.f;
@@ -494,14 +496,18 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       }
     } else if (__builtin_amdgcn_ballot_w64(!(lo <= kt * kBc && hi >= kt * kBc + kBc - 1))) {
       // Element mask only when some row of this wave does not allow all 64 keys of the tile
-      // (hi <= N - 1 always, so a fully allowed row also has the tile in range).
+      // (hi <= N - 1 always, so a fully allowed row also has the tile in range).  Key j = kb + o
+      // is allowed iff lo <= j <= hi, i.e. iff (unsigned)(o - (lo - kb)) <= (unsigned)(hi - lo):
+      // one subtraction, one compare and one select per score.
       keep_branch();
+      const int a0 = lo - kb;
+      const uint32_t span = (uint32_t)(hi - lo);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = kb + 32 * blk + 16 * (r >> 3) + (r & 7);
-          if (j < lo || j > hi) s[blk][r] = kMasked;
+          const int o = 32 * blk + 16 * (r >> 3) + (r & 7);
+          if ((uint32_t)(o - a0) > span) s[blk][r] = kMasked;
         }
       }
     }
