@@ -414,9 +414,6 @@ int fwd_launch(const void *q, const void *k, const void *v, void *o, float *lse,
                const Shape &s, char *ws, hipStream_t st) {
   const WsLayout wl = ws_layout(s);
   uint16_t *vt = (uint16_t *)(ws + wl.vt);
-  if (attn::launch_vt_pack((const uint16_t *)v, vt, B * H, N, s.Npad, d, st) != hipSuccess)
-    return fail(ATTN_ERR_LAUNCH, "V transpose kernel launch failed");
-
   attn::FwdArgs a{};
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k;
@@ -454,11 +451,12 @@ int fwd_launch(const void *q, const void *k, const void *v, void *o, float *lse,
     a.cls = (const int8_t *)(ws + wl.cls);
     a.cnt = (const int32_t *)(ws + wl.cnt);
     a.list = (const int32_t *)(ws + wl.list);
-    if (attn::launch_block_table(mask_desc(s, params), a.offs, s.Bm, s.n_qt, s.n_kt,
-                                 (int8_t *)(ws + wl.cls), (int32_t *)(ws + wl.cnt),
-                                 (int32_t *)(ws + wl.list), st) != hipSuccess)
-      return fail(ATTN_ERR_LAUNCH, "block table kernel launch failed");
   }
+  // V^T pack and block table: one launch
+  if (attn::launch_prep((const uint16_t *)v, vt, B * H, N, s.Npad, d, mask_desc(s, params), a.offs,
+                        s.Bm, s.n_qt, s.n_kt, (int8_t *)a.cls, (int32_t *)a.cnt,
+                        (int32_t *)a.list, st) != hipSuccess)
+    return fail(ATTN_ERR_LAUNCH, "V transpose / block table kernel launch failed");
   attn::FwdInstance in{};
   in.d = d;
   in.alibi = (variant & ATTN_MOD_ALIBI) != 0;

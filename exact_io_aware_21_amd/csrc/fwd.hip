@@ -10,11 +10,12 @@ namespace {
 // V [BH][N][D] bf16 -> V^T [BH][D][Npad] fp16: keys contiguous, zero beyond N, d rows permuted
 // by sigma_d.
 template <int D>
-__global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t *__restrict__ v,
-                                                      uint16_t *__restrict__ vt, int N, int Npad) {
+__device__ __forceinline__ void vt_pack_body(const uint16_t *__restrict__ v,
+                                             uint16_t *__restrict__ vt, int N, int Npad, int kt,
+                                             int bh) {
   constexpr int RS = D + 2;  // padded LDS row, in elements
   __shared__ uint16_t t[64 * RS];
-  const int kt = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const uint16_t *src = v + (size_t)bh * N * D;
   for (int c = tid; c < 64 * D / 8; c += 256) {
     const int key = c / (D / 8), ch = c % (D / 8);
@@ -44,14 +45,19 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t *__restrict
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t *__restrict__ v,
+                                                      uint16_t *__restrict__ vt, int N, int Npad) {
+  vt_pack_body<D>(v, vt, N, Npad, blockIdx.x, blockIdx.y);
+}
+
 // ---------------------------------------------------------------------------------------------
 // One workgroup per table row (bm, qt): 256 tiles are classified at a time and the non-empty
 // ones compacted in ascending kt with a wave ballot plus a 4-entry LDS prefix.
-__global__ __launch_bounds__(256) void block_table_kernel(MaskDesc m, const int32_t *offs_all,
-                                                          int n_qt, int n_kt, int8_t *cls,
-                                                          int32_t *cnt, int32_t *list) {
+__device__ __forceinline__ void block_table_body(const MaskDesc &m, const int32_t *offs_all,
+                                                 int n_qt, int n_kt, int8_t *cls, int32_t *cnt,
+                                                 int32_t *list, int row) {
   __shared__ int wave_tot[4];
-  const int row = blockIdx.x;
   const int bm = row / n_qt, qt = row - bm * n_qt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   MaskDesc mm = m;
@@ -79,6 +85,30 @@ __global__ __launch_bounds__(256) void block_table_kernel(MaskDesc m, const int3
   }
   for (int kt = base + tid; kt < n_kt; kt += 256) lrow[kt] = 0;
   if (tid == 0) cnt[row] = base;
+}
+
+__global__ __launch_bounds__(256) void block_table_kernel(MaskDesc m, const int32_t *offs_all,
+                                                          int n_qt, int n_kt, int8_t *cls,
+                                                          int32_t *cnt, int32_t *list) {
+  block_table_body(m, offs_all, n_qt, n_kt, cls, cnt, list, blockIdx.x);
+}
+
+// The two preparation steps of a forward call in one launch: workgroups [0, n_rows) build the
+// block table (one row each, when the kind has one), the rest pack V^T (one 64-key tile of one
+// head each).  Saves a launch and its gap, which is a few percent of the short workloads' step.
+template <int D>
+__global__ __launch_bounds__(256) void prep_kernel(const uint16_t *__restrict__ v,
+                                                   uint16_t *__restrict__ vt, int N, int Npad,
+                                                   MaskDesc m, const int32_t *offs_all, int n_rows,
+                                                   int n_qt, int n_kt, int8_t *cls, int32_t *cnt,
+                                                   int32_t *list) {
+  const int w = blockIdx.x;
+  if (w < n_rows) {
+    block_table_body(m, offs_all, n_qt, n_kt, cls, cnt, list, w);
+  } else {
+    const int p = w - n_rows, tiles = Npad / 64;
+    vt_pack_body<D>(v, vt, N, Npad, p % tiles, p / tiles);
+  }
 }
 
 template <int D, bool ALIBI, bool SOFTCAP, bool POS, bool OUTF32, bool FP8>
@@ -126,6 +156,23 @@ hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Np
     vt_pack_kernel<128><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
   else
     vt_pack_kernel<64><<<grid, 256, 0, stream>>>(v, vt, N, Npad);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const uint16_t *v, uint16_t *vt, int BH, int N, int Npad, int d,
+                       const MaskDesc &m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,
+                       int8_t *cls, int32_t *cnt, int32_t *list, hipStream_t stream) {
+  const int n_rows = cls ? Bm * n_qt : 0;
+  const dim3 grid((unsigned)(n_rows + (Npad / 64) * BH));
+  if (d == 256)
+    prep_kernel<256><<<grid, 256, 0, stream>>>(v, vt, N, Npad, m, offs_all, n_rows, n_qt, n_kt,
+                                               cls, cnt, list);
+  else if (d == 128)
+    prep_kernel<128><<<grid, 256, 0, stream>>>(v, vt, N, Npad, m, offs_all, n_rows, n_qt, n_kt,
+                                               cls, cnt, list);
+  else
+    prep_kernel<64><<<grid, 256, 0, stream>>>(v, vt, N, Npad, m, offs_all, n_rows, n_qt, n_kt,
+                                              cls, cnt, list);
   return hipGetLastError();
 }
 

@@ -117,7 +117,6 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   // three LDS buffers instead of four.
   constexpr int DV = D > 128 ? 128 : D;  // columns of O (rows of V^T) of this workgroup
   constexpr int NB = D > 128 ? 3 : 4;    // LDS buffers of the copy ring
-  constexpr int KCH = D / 8;             // 16-byte chunks per K row
   constexpr int VCH = kBc / 8;           // 16-byte chunks per V^T row
   constexpr int NKS = D / 16;            // k-steps of the score product
   constexpr int NDB = DV / 32;           // 32-column blocks of O

@@ -99,5 +99,9 @@ hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Np
 hipError_t launch_block_table(MaskDesc m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,
                               int8_t *cls, int32_t *cnt, int32_t *list, hipStream_t stream);
 hipError_t launch_fwd(const FwdInstance &inst, const FwdArgs &a, hipStream_t stream);
+// The V^T pack and, when cls is not null, the block table (Bm * n_qt rows), in one launch.
+hipError_t launch_prep(const uint16_t *v, uint16_t *vt, int BH, int N, int Npad, int d,
+                       const MaskDesc &m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,
+                       int8_t *cls, int32_t *cnt, int32_t *list, hipStream_t stream);
 
 }  // namespace attn
