@@ -263,7 +263,15 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   } else {
     T = a.n_kt;
   }
+  // ALiBi instances walk the key tiles from the last one back to the first.  The bias
+  // -slope (i - j) grows towards larger keys, by slope * 64 per tile, so in ascending order the
+  // running maximum of a steep head moves on nearly every tile (each move rescales O); the
+  // first tile of the descending walk holds the largest biases, and the maximum then rarely
+  // moves.  The order of the tiles does not change the sums (the online softmax is a merge of
+  // per-tile partial results), only their rounding order.
+  constexpr bool REV = ALIBI && MOD == 0;
   auto kt_of = [&](int t) -> int {
+    if constexpr (REV) t = T - 1 - t;
     if (!lst) return t;
     if constexpr ((MOD & kModMask) != 0) return min(max(lst[t], 0), a.n_kt - 1);
     return lst[t];
@@ -512,12 +520,13 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     }
     // Probabilities against the running maximum m (base 2), which must keep every P <= 2^8
     // (the range and precision of the fp16 P V operands): the lazy rescale with threshold 8.
-    // Unmodified scores (POS instances without a modification) skip the tile maximum in the
-    // common case: a lane's sum of its 32 probabilities bounds each of them, so while every sum
-    // is <= 2^8 the running m stands.  Otherwise, or for a row with no maximum yet that sees a
-    // finite score, the tile maximum is taken, m moves and the output is rescaled, and the
-    // probabilities are formed again.  Score modifications (ALiBi, soft-cap, user functions)
-    // move the maximum often, so those instances take the tile maximum first, every tile.
+    // Unmodified scores (POS instances without a modification) and ALiBi scores walked in
+    // descending key order skip the tile maximum in the common case: a lane's sum of its 32
+    // probabilities bounds each of them, so while every sum is <= 2^8 the running m stands.
+    // Otherwise, or for a row with no maximum yet that sees a finite score, the tile maximum is
+    // taken, m moves and the output is rescaled, and the probabilities are formed again.  The
+    // soft-cap and user modifications move the maximum often, so those instances take the tile
+    // maximum first, every tile.
     auto probs = [&](float m_use) -> float {
       float psum[4];
 #pragma unroll
@@ -561,7 +570,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
       m_run = m_new;
     };
-    if constexpr (!(POS && MOD == 0)) {
+    // Without a modification (and for ALiBi, walked in descending key order) the maximum moves
+    // rarely, and the probabilities are formed against the running maximum first (see below).
+    if constexpr (!((POS || (ALIBI && !SOFTCAP)) && MOD == 0)) {
       const float mx = pair_max(lane_max());
       const float m_tile = POS ? mx * c : mx;
       if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kTau)) {
