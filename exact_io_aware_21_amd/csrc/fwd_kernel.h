@@ -442,11 +442,17 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   for (int g = 0; g < 4; ++g) pb[g] = f16x8{};
 
   // V-phase of tile t: score modifications, mask, online softmax, P_t in fp16.
+  // ALiBi without soft-cap forms its scores relative to the running maximum m (folded into the
+  // per-tile bias base), so its probabilities need no subtraction: exp2(s) directly.
+  constexpr bool REL = ALIBI && !SOFTCAP && MOD == 0;
   auto vphase = [&](int kt, float skt) {
     // Base-2 score scale of this tile; FP8: times s_k of the key tile (skt, loaded ahead).
     const float c = FP8 ? cq * skt : cq;
     // Register r of block blk is key kt*Bc + 32*blk + 16*(r/8) + 8*hf + r%8.
     const int kb = kt * kBc + 8 * hf;
+    // The reference the scores of this tile are taken against (REL): m, or 0 before the row
+    // has seen a finite score.
+    const float m_ref = REL ? (m_run == -INFINITY ? 0.f : m_run) : 0.f;
     if constexpr (MOD != 0) {
       // Natural-units scores, modified by the user's function; these instances run with
       // POS = true and c = log2(e), so the conversion to base 2 rides on the exponent's FMA.
@@ -464,7 +470,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
         }
       }
     } else if constexpr (!POS) {
-      const float abase = ALIBI ? slopeL * (float)(kb - qrow) : 0.f;
+      const float abase = ALIBI ? slopeL * (float)(kb - qrow) - m_ref : 0.f;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
@@ -582,7 +588,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       l_run += probs(m_run == -INFINITY ? 0.f : m_run);
       return;
     }
-    float lsum = probs(m_run == -INFINITY ? 0.f : m_run);
+    float lsum = probs(REL ? 0.f : m_run == -INFINITY ? 0.f : m_run);
     bool need = !(lsum <= kPmax);
     if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
       keep_branch();
@@ -592,8 +598,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       keep_branch();
       // Tile row maximum: in-lane over 32 keys, then with the lane that shares the query.
       const float mx = pair_max(lane_max());
-      rescale_to(fmaxf(m_run, POS ? mx * c : mx));
-      lsum = probs(m_run == -INFINITY ? 0.f : m_run);
+      rescale_to(fmaxf(m_run, REL ? m_ref + mx : POS ? mx * c : mx));
+      lsum = probs(m_run == -INFINITY ? 0.f : REL ? m_run - m_ref : m_run);
     }
     l_run += lsum;
   };
