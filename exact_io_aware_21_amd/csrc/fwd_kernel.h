@@ -689,8 +689,13 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
 #pragma unroll
       for (int r = 0; r < NDMA; ++r) copy_item(r, sB2, kt_n2, kt_next, false);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // Only pair 0 has to be whole before the loop (both groups' first M-phase and group 0's
+    // first fragment reads use it); the loop's own waits cover pairs 1 and 2.  When every
+    // workgroup starts at once, waiting for all three pairs would put the whole burst of
+    // first loads in front of the first MFMA.  The copies are the only vector-memory
+    // operations in flight here (the Q loads have been waited for).
+    ring_wait<waitcnt_vm((NB - 2) * NDMA)>();
+    ring_barrier();
     if (grp == 0) prefetch(sB0);
 
     // Iteration k with B = k mod NB and phase group G, every buffer named statically.
