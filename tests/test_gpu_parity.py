@@ -342,3 +342,31 @@ def test_binding_rejects_mixed_devices():
         attn.attn_fwd(q, q, q, o, None, 0.125, attn.ATTN_MASK_DOCUMENT,
                       doc_offsets=torch.tensor([[0, 64], [0, 64]], dtype=torch.int64,
                                                device=DEV))
+
+
+def test_v_beyond_fp16_range_saturates():
+    """Values of V beyond fp16's range (|v| > 65504, representable in bf16) enter P V saturated to
+    +-65504, as include/attn.h states: O equals the attention of the clipped V (relative to the
+    magnitudes involved), and differs from the unclipped one where such a value carries weight."""
+    w = inputs.Workload("v_sat", B=1, H=2, N=300, d=64, mask="causal", seed=1300)
+    inp = inputs.make_inputs(w)
+    v = inputs.bf16_bits_to_f32(inp["v"]).copy()
+    v[0, 0, 5, 3] = 1.0e5
+    v[0, 1, 40, 7] = -3.0e5
+    v[0, 1, 41, 9] = 65504.0  # the largest fp16 value itself is exact
+    vbits = inputs.f32_to_bf16_bits(v)
+    o32, l32 = run_gpu(inp, w, out_f32=True, v_override=vbits)
+    vb = oracle.decode_bf16(vbits)
+    q, k = oracle.decode_bf16(inp["q"]), oracle.decode_bf16(inp["k"])
+    O_clip, L_ref = oracle.attention(q, k, np.clip(vb, -65504.0, 65504.0), float(inp["scale"]),
+                                     mask="causal")
+    O_raw, _ = oracle.attention(q, k, vb, float(inp["scale"]), mask="causal")
+    got = o32.cpu().numpy()
+    # P enters the product as fp16 (relative 2^-11 per weight): in the columns that hold the
+    # large values the error scale is 2^-11 * 65504 = 32; every other column keeps 1e-2
+    assert np.abs(got - O_clip).max() <= 2.0 ** -11 * 65504.0 * 1.05
+    other = np.ones(got.shape, dtype=bool)
+    other[0, 0, :, 3] = other[0, 1, :, 7] = other[0, 1, :, 9] = False
+    assert np.abs(got - O_clip)[other].max() <= TOL_O
+    assert np.abs(l32.cpu().numpy() - L_ref).max() <= TOL_L
+    assert np.abs(got - O_raw).max() > 1.0e3  # the saturation is visible where |v| > 65504
