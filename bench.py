@@ -133,10 +133,17 @@ class SclkSampler:
     The published MFMA peak assumes the 2.4 GHz maximum clock; under sustained matrix-core load the
     clock settles lower, and this records where."""
 
-    def __init__(self, period_s=0.005, started=None):
+    # Steps shorter than this are not sampled: on short workloads, whose loop is bound by
+    # launch overhead, the sysfs reads (each a query of the power-management firmware by the
+    # driver) slowed the timed loop several-fold (plain_n256_d64: 97 us per step with sampling,
+    # 18 us without), so the sample would change what it measures.
+    MIN_STEP_MS = 0.2
+
+    def __init__(self, period_s=0.005, started=None, step_ms=None):
         """started: optional callable; samples are kept only once it returns True (the bench
         passes the completion query of the first timed step's end event, so that the readings
-        taken while the driver's value still lags the idle clock are dropped)."""
+        taken while the driver's value still lags the idle clock are dropped).  step_ms: the
+        step time seen in the warm-up; below MIN_STEP_MS nothing is sampled."""
         import glob
         import threading
         self.period_s = period_s
@@ -144,7 +151,9 @@ class SclkSampler:
         self.dropped = 0
         self.samples = []
         self.path = None
-        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        self.skipped = step_ms is not None and step_ms < self.MIN_STEP_MS
+        for path in ([] if self.skipped else
+                     sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))):
             if self._read(path) is not None:
                 self.path = path
                 break
@@ -183,6 +192,9 @@ class SclkSampler:
             self._thread.join()
 
     def summary(self):
+        if self.skipped:
+            return {"skipped": f"steps under {self.MIN_STEP_MS} ms: sysfs clock reads slow the "
+                               "launch loop of such short steps"}
         if not self.samples:
             return None
         x = sorted(self.samples)
@@ -195,7 +207,7 @@ def clock_scaled_peak(rec, peak, achieved):
     of it reached.  The sysfs clock is read by the driver on its own schedule and can lag the
     hardware, so a fraction above 1 (physically impossible) marks the reading as stale: the
     fraction is then left out and the record says why."""
-    if not rec:
+    if not rec or "skipped" in rec:
         return rec
     scaled = peak * rec["median"] / MAX_SCLK_MHZ
     rec["mfma_peak_at_median_tflops"] = round(scaled, 1)
@@ -209,22 +221,30 @@ def clock_scaled_peak(rec, peak, achieved):
     return rec
 
 
+KEV_EVERY = 16    # kernel event pairs on every 16th step of a short workload (see the loop)
+GRAPH_CALLS = 20  # calls captured per graph in --graph mode (a replay's own launch cost is shared)
+
+
 def bench_graph(args, w, inp, call):
-    """--graph: one call captured in a HIP graph (the calls allocate nothing and issue no
-    memset, so they can be captured), then K replays timed with a HIP event pair on the
-    replaying stream.  The per-call time is the device's; the kernel-only event pair is not
-    recorded inside the graph, so the roofline is taken on the whole call."""
+    """--graph: GRAPH_CALLS calls captured in one HIP graph (the calls allocate nothing and
+    issue no memset, so they can be captured), replayed until at least K calls have run, timed
+    with a HIP event pair on the replaying stream.  The per-call time is the device's; the
+    kernel-only event pair is not recorded inside the graph, so the roofline is taken on the
+    whole call."""
     import torch
+    G = max(1, min(args.steps, GRAPH_CALLS))
+    reps = -(-args.steps // G)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        call()
-    for _ in range(max(1, args.warmup)):
+        for _ in range(G):
+            call()
+    for _ in range(max(1, -(-args.warmup // G))):
         g.replay()
     torch.cuda.synchronize()
-    K = args.steps
+    K = reps * G
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(K):
+    for _ in range(reps):
         g.replay()
     end.record()
     torch.cuda.synchronize()
@@ -247,7 +267,7 @@ def bench_graph(args, w, inp, call):
            "data": "synthetic (seeded N(0, sigma^2) Q/K/V rounded to bf16)",
            "config": {"workload": ("graph_fp8_" if args.fp8 else "graph_") + w.name, "B": w.B,
                       "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
-                      "timing": "HIP graph of one call, K replays; device time per call"},
+                      "timing": f"HIP graph of {G} calls, replayed {reps} times; device time per call"},
            "roofline": roof}
     print(json.dumps(out), flush=True)
 
@@ -570,36 +590,50 @@ def main():
                     timing_events=timing_events, cached_table=args.mod_cached and bool(built))
             built.append(True)
     else:
-        def call(timing_events=None):
-            attn.attn_fwd(q, k, v, o, lse, inp["scale"], var, timing_events=timing_events, **kw)
+        # checked and marshalled once: each step is one C call (a serving loop's calling
+        # pattern); under --graph the calls go to the capturing stream, else to this one
+        call = attn.FwdPlan(q, k, v, o, lse, inp["scale"], var,
+                            stream=None if args.graph else torch.cuda.current_stream(), **kw)
 
+    t0 = time.perf_counter()
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t0) * 1e3 / args.warmup if args.warmup else None
 
     if args.graph:
         bench_graph(args, w, inp, call)
         return
 
     K = args.steps
+    # Kernel event pairs on every step, or on every KEV_EVERY-th step when a step takes under
+    # SclkSampler.MIN_STEP_MS: two event records cost about as much as such a step's kernel
+    # (plain_n256_d64: 13.3 us per step with a pair on every step, the kernel itself ~6 us).
+    ev_every = KEV_EVERY if warm_ms is not None and warm_ms < SclkSampler.MIN_STEP_MS else 1
+    kev_steps = list(range(0, K, ev_every))
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+           for _ in kev_steps]
     cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K if args.cold else 0)]
     for a, b in kev + cev:  # torch creates the underlying hipEvent on the first record
         a.record()
         b.record()
+    # the kernel event pairs, marshalled before the timed loop where the call takes them so
+    tev = [call.events(e) for e in kev] if isinstance(call, attn.FwdPlan) else kev
+    step_ev = [None] * K
+    for j, i in enumerate(kev_steps):
+        step_ev[i] = tev[j]
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    sclk = SclkSampler(started=kev[0][1].query)
+    sclk = SclkSampler(started=kev[0][1].query, step_ms=warm_ms)
     with sclk:  # sampled from the end of the first timed step until the device has finished
         start.record()
         for i in range(K):
             if args.cold:
                 flush.fill_(i & 255)
                 cev[i][0].record()
-            call(kev[i])
+            call(step_ev[i])
             if args.cold:
                 cev[i][1].record()
         end.record()
@@ -609,7 +643,7 @@ def main():
     else:
         step_ms = start.elapsed_time(end) / K
     kern = sorted(a.elapsed_time(b) for a, b in kev)
-    kern_ms = sum(kern) / K
+    kern_ms = sum(kern) / len(kern)
 
     flops = 4.0 * w.d * allowed_pairs(w, inp["doc_offsets"])
     hbm_bytes = w.B * w.H * w.N * (4 * w.d * 2 + 4)  # Q, K, V read; O (bf16) and L written
@@ -644,8 +678,10 @@ def main():
                    "window": w.window, "alibi": w.alibi, "softcap": w.softcap,
                    "unmasked_gflop": round(flops / 1e9, 3),
                    "fwd_kernel_ms": round(kern_ms, 4),
-                   "fwd_kernel_ms_median": round(kern[K // 2], 4),
+                   "fwd_kernel_ms_median": round(kern[len(kern) // 2], 4),
                    "fwd_kernel_ms_min": round(kern[0], 4),
+                   "kernel_events": "every step" if ev_every == 1 else
+                                    f"every {ev_every}th step ({len(kern)} of {K})",
                    "cache": "cold: 512 MiB written before each call" if args.cold else "warm",
                    "compulsory_hbm_bytes": hbm_bytes,
                    "sclk_mhz": sclk_rec,

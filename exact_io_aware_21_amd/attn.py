@@ -270,6 +270,54 @@ def attn_fwd_noalloc(q, k, v, o, lse, scale, variant, window=0, softcap=0.0, ali
     return o, lse
 
 
+class FwdPlan:
+    """attn_fwd (or, with noalloc=True, attn_fwd_noalloc) on fixed buffers, for loops that run
+    the forward pass many times on the same tensors: the arguments are checked and marshalled
+    once, here, and each call is then one C call (which still validates its arguments).  The
+    tensors must stay alive and keep their storage while the plan is used; their contents may
+    change between calls.  stream=None means the current stream at each call (so a call made
+    under graph capture goes to the capturing stream)."""
+
+    def __init__(self, q, k, v, o, lse, scale, variant, window=0, softcap=0.0, alibi_slopes=None,
+                 doc_offsets=None, workspace=None, stream=None, noalloc=False):
+        if noalloc and workspace is not None:
+            raise ValueError("attn_fwd_noalloc takes no workspace")
+        B, H, N, d, p, _ = _fwd_args(q, k, v, o, lse, variant, window, softcap, alibi_slopes,
+                                     doc_offsets, workspace, None)
+        if not noalloc and workspace is None:
+            workspace = alloc_workspace(B, H, N, d, variant, q.device)
+            p.workspace = workspace.data_ptr()
+            p.workspace_bytes = workspace.numel() * workspace.element_size()
+        self._keep = (q, k, v, o, lse, alibi_slopes, doc_offsets, workspace)
+        self._p = p
+        self._ev = None
+        self._fn = lib().attn_fwd_noalloc if noalloc else lib().attn_fwd
+        self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                      variant, ctypes.byref(p))
+        self._stream = None if stream is None else _stream(stream)
+
+    @staticmethod
+    def events(timing_events):
+        """A pair of torch.cuda.Event(enable_timing=True), each recorded once beforehand,
+        marshalled for __call__ (prepare them before a timed loop)."""
+        if not (timing_events[0].cuda_event and timing_events[1].cuda_event):
+            raise ValueError("timing events must have been recorded once before use")
+        return (ctypes.c_void_p * 2)(timing_events[0].cuda_event, timing_events[1].cuda_event)
+
+    def __call__(self, timing_events=None):
+        """One forward pass; timing_events: None, a pair of events as for attn_fwd, or the
+        result of events() for that pair."""
+        p = self._p
+        if timing_events is None:
+            p.timing_events = None
+        else:
+            if not isinstance(timing_events, ctypes.Array):
+                timing_events = self.events(timing_events)
+            self._ev = timing_events
+            p.timing_events = ctypes.addressof(timing_events)
+        _check(self._fn(*self._args, self._stream if self._stream is not None else _stream(None)))
+
+
 def attn_bwd_workspace_size(B: int, H: int, N: int, d: int, variant: int) -> int:
     return int(lib().attn_bwd_workspace_size(B, H, N, d, variant))
 

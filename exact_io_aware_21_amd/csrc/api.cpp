@@ -407,16 +407,52 @@ int fwd_check(const void *q, const void *k, const void *v, void *o, float *lse, 
   return check_params(s, variant, params, false);
 }
 
+// Which kernel takes a forward pass: the tiled kernel (V^T pack and block table, then key tiles
+// walked per 256-row query tile), or for short sequences the single-launch kernel, which holds
+// all N <= 256 keys of a head in LDS (K and V^T: up to 137 KB per workgroup at N = 256,
+// d = 128) and re-reads them per 64 query rows.  Measured against the tiled kernel on one
+// MI355X (device time per call from graph replays), the short kernel is as fast or faster for
+// d = 64 and for N <= 128 at every grid measured (B H up to 2048), and for d = 128 with
+// 128 < N <= 256 while the grid has at most 256 workgroups (its 137 KB of LDS allow one
+// workgroup per CU); beyond that the tiled kernel's throughput wins.  ATTN_FWD_PATH=tiled|short overrides the choice (for tests and
+// measurements); "short" on a shape the short kernel does not take is an error.
+int fwd_short_path(const Shape &s, bool &use_short) {
+  const bool fits = !s.fp8 && s.d <= 128 && s.N <= attn::kShortMaxN;
+  const char *env = std::getenv("ATTN_FWD_PATH");
+  if (env && *env) {
+    if (!std::strcmp(env, "tiled")) {
+      use_short = false;
+      return ATTN_OK;
+    }
+    if (!std::strcmp(env, "short")) {
+      if (!fits)
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "ATTN_FWD_PATH=short takes N <= %d, d 64 or 128 and bf16 operands",
+                    attn::kShortMaxN);
+      use_short = true;
+      return ATTN_OK;
+    }
+    return fail(ATTN_ERR_INVALID_ARG, "ATTN_FWD_PATH must be 'tiled' or 'short', not '%s'", env);
+  }
+  const long long wgs = (long long)s.B * s.H * ((s.N + 63) / 64);
+  use_short = fits && (s.d == 64 || s.N <= 128 || wgs <= 256);
+  return ATTN_OK;
+}
+
 // The launches of one forward pass on validated arguments, with the workspace at ws (at least
 // ws_layout(s).total bytes).  Launches only: allocates nothing.
 int fwd_launch(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                int N, int d, float scale, uint32_t variant, const attn_params *params,
                const Shape &s, char *ws, hipStream_t st) {
+  bool use_short = false;
+  int rc = fwd_short_path(s, use_short);
+  if (rc) return rc;
   const WsLayout wl = ws_layout(s);
   uint16_t *vt = (uint16_t *)(ws + wl.vt);
   attn::FwdArgs a{};
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v;
   a.vt = vt;
   a.o = o;
   a.lse = lse;
@@ -433,6 +469,27 @@ int fwd_launch(const void *q, const void *k, const void *v, void *o, float *lse,
     a.capL = params->softcap * log2e;
   }
   a.slopes = (variant & ATTN_MOD_ALIBI) ? params->alibi_slopes : nullptr;
+  a.kind = (int)s.kind;
+  a.window = s.kind == ATTN_MASK_SLIDING_WINDOW ? params->window : 0;
+  a.max_docs = s.kind == ATTN_MASK_DOCUMENT ? params->max_docs : 0;
+  a.offs = s.kind == ATTN_MASK_DOCUMENT ? params->doc_offsets : nullptr;
+  attn::FwdInstance in{};
+  in.d = d;
+  in.alibi = (variant & ATTN_MOD_ALIBI) != 0;
+  in.softcap = (variant & ATTN_MOD_SOFTCAP) != 0;
+  in.pos_scale = !in.alibi && !in.softcap && scale > 0.f;
+  in.out_f32 = params->o_dtype == ATTN_O_F32;
+  in.fp8 = s.fp8;
+  void *const *ev = params->timing_events;
+  if (use_short) {
+    if (ev && hipEventRecord((hipEvent_t)ev[0], st) != hipSuccess)
+      return fail(ATTN_ERR_LAUNCH, "timing event record failed");
+    if (attn::launch_fwd_short(in, a, st) != hipSuccess)
+      return fail(ATTN_ERR_LAUNCH, "short-sequence forward kernel launch failed");
+    if (ev && hipEventRecord((hipEvent_t)ev[1], st) != hipSuccess)
+      return fail(ATTN_ERR_LAUNCH, "timing event record failed");
+    return ATTN_OK;
+  }
   if (s.fp8) {
     // K to E4M3 codes with one scale per 64-key tile; Q is quantized inside the forward kernel.
     uint8_t *k8 = (uint8_t *)(ws + wl.k8);
@@ -443,10 +500,6 @@ int fwd_launch(const void *q, const void *k, const void *v, void *o, float *lse,
     a.k8 = k8;
     a.sk = sk;
   }
-  a.kind = (int)s.kind;
-  a.window = s.kind == ATTN_MASK_SLIDING_WINDOW ? params->window : 0;
-  a.max_docs = s.kind == ATTN_MASK_DOCUMENT ? params->max_docs : 0;
-  a.offs = s.kind == ATTN_MASK_DOCUMENT ? params->doc_offsets : nullptr;
   if (s.kind != ATTN_MASK_NONE) {
     a.cls = (const int8_t *)(ws + wl.cls);
     a.cnt = (const int32_t *)(ws + wl.cnt);
@@ -457,14 +510,6 @@ int fwd_launch(const void *q, const void *k, const void *v, void *o, float *lse,
                         s.Bm, s.n_qt, s.n_kt, (int8_t *)a.cls, (int32_t *)a.cnt,
                         (int32_t *)a.list, st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "V transpose / block table kernel launch failed");
-  attn::FwdInstance in{};
-  in.d = d;
-  in.alibi = (variant & ATTN_MOD_ALIBI) != 0;
-  in.softcap = (variant & ATTN_MOD_SOFTCAP) != 0;
-  in.pos_scale = !in.alibi && !in.softcap && scale > 0.f;
-  in.out_f32 = params->o_dtype == ATTN_O_F32;
-  in.fp8 = s.fp8;
-  void *const *ev = params->timing_events;
   if (ev && hipEventRecord((hipEvent_t)ev[0], st) != hipSuccess)
     return fail(ATTN_ERR_LAUNCH, "timing event record failed");
   if (attn::launch_fwd(in, a, st) != hipSuccess)

@@ -11,6 +11,7 @@ struct FwdArgs {
   const uint16_t *q;   // bf16 [BH][N][D]
   const uint16_t *k;   // bf16 [BH][N][D]
   const uint16_t *vt;  // bf16 [BH][D][Npad], key-contiguous, d rows permuted (see fwd.hip)
+  const uint16_t *v;   // bf16 [BH][N][D]: read directly by the short-sequence kernel
   void *o;             // bf16 or fp32 [BH][N][D]
   float *lse;          // fp32 [BH][N] or null
   int B, H, N, Npad, n_qt, n_kt;
@@ -99,6 +100,10 @@ hipError_t launch_vt_pack(const uint16_t *v, uint16_t *vt, int BH, int N, int Np
 hipError_t launch_block_table(MaskDesc m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,
                               int8_t *cls, int32_t *cnt, int32_t *list, hipStream_t stream);
 hipError_t launch_fwd(const FwdInstance &inst, const FwdArgs &a, hipStream_t stream);
+// Short sequences (short.hip): N <= kShortMaxN, d 64 or 128, bf16 operands; one launch, reads
+// V directly (no V^T pack, no block table).
+constexpr int kShortMaxN = 256;
+hipError_t launch_fwd_short(const FwdInstance &inst, const FwdArgs &a, hipStream_t stream);
 // The V^T pack and, when cls is not null, the block table (Bm * n_qt rows), in one launch.
 hipError_t launch_prep(const uint16_t *v, uint16_t *vt, int BH, int N, int Npad, int d,
                        const MaskDesc &m, const int32_t *offs_all, int Bm, int n_qt, int n_kt,

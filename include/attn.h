@@ -99,7 +99,7 @@ typedef struct {
  *   o       : device, [B][H][N][d], bf16 or fp32 per params->o_dtype, 16-byte aligned.
  *   lse     : device, fp32 [B][H][N], the natural-log L; NULL skips it.
  *   B, H, N : >= 1, N <= 2^24, B*H*ceil(N/Br) < 2^31.
- *   d       : 64 or 128.
+ *   d       : 64, 128 or 256 (ATTN_PREC_FP8: 64 or 128).
  *   scale   : finite (1/sqrt(d) for the standard scaling).
  *   variant : one mask kind, optionally OR-ed with ATTN_MOD_ALIBI and/or ATTN_MOD_SOFTCAP, or
  *             with ATTN_PREC_FP8 (no score modification; B*H <= 65535).
@@ -114,6 +114,14 @@ typedef struct {
  * rows = Br (inside the forward kernel) and K with rows = Bc (into the workspace), and
  * S = scale * (s_q Q8)(s_k K8)^T is formed from the E4M3 codes with fp32 accumulation; V and
  * the P V product are as above.  Inputs must be finite.
+ * Kernels: sequences of N <= 256 keys (d 64 or 128, bf16 operands) run, while the grid is
+ * small, on a single-launch kernel that holds all keys of a head on chip and takes the exact
+ * row maximum (the workspace is then unused); other shapes run the tiled kernel (V^T pack and
+ * block table into the workspace, then the online softmax over key tiles).  Both are within
+ * the precision above; they are not bit-identical to each other.  The environment variable
+ * ATTN_FWD_PATH = "tiled" or "short", read at each call, forces one of them (for tests and
+ * measurements); "short" on a shape that kernel does not take, or any other non-empty value,
+ * gives ATTN_ERR_INVALID_ARG.
  */
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
              int d, float scale, uint32_t variant, const attn_params *params, void *stream);

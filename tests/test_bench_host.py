@@ -72,3 +72,15 @@ def test_clock_sampler_drops_samples_before_start():
     s.path = __file__  # any readable file: no '*' line, so nothing is parsed
     s.samples.clear()
     assert s.summary() is None
+
+
+def test_clock_sampler_skips_short_steps():
+    s = bench.SclkSampler(step_ms=0.05)
+    assert s.path is None
+    with s:
+        pass
+    rec = s.summary()
+    assert "skipped" in rec
+    assert bench.clock_scaled_peak(rec, 2500.0, 1.0) == rec
+    assert not bench.SclkSampler(step_ms=5.0).skipped
+    assert not bench.SclkSampler().skipped

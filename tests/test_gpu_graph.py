@@ -3,7 +3,8 @@ section 6, item 2: graph-captured execution forbids allocation during the record
 (with a workspace allocated beforehand) and attn_fwd_noalloc allocate nothing and issue no
 memset, so a HIP graph of a call can be replayed.  Each graph is replayed several times, with
 new inputs copied in by eager work and a synchronisation between replays, and every replay is
-checked bit for bit against an eager call on the same inputs."""
+checked bit for bit against an eager call on the same inputs.  FwdPlan's calls are captured
+the same way (the plan takes the capturing stream as the current one)."""
 import numpy as np
 import pytest
 import torch
@@ -25,12 +26,16 @@ CASES = [
                     alibi=True, seed=2201),
     inputs.Workload("graph_doc_softcap", B=2, H=2, N=900, d=64, mask="document", softcap=30.0,
                     sigma=2.0, seed=2202, doc_len_range=(50, 400)),
+    # a short sequence: the single-launch kernel
+    inputs.Workload("graph_short_causal_alibi", B=1, H=2, N=200, d=128, mask="causal",
+                    alibi=True, seed=2203),
 ]
 
 
-@pytest.mark.parametrize("noalloc", [False, True], ids=["attn_fwd", "attn_fwd_noalloc"])
+@pytest.mark.parametrize("how", ["attn_fwd", "attn_fwd_noalloc", "plan"])
 @pytest.mark.parametrize("w", CASES, ids=[c.name for c in CASES])
-def test_graph_replays_match_eager(w, noalloc):
+def test_graph_replays_match_eager(w, how):
+    noalloc = how == "attn_fwd_noalloc"
     var = attn.variant_bits(w.mask, w.alibi, w.softcap > 0)
     sets = [inputs.make_inputs(inputs.Workload(w.name, B=w.B, H=w.H, N=w.N, d=w.d,
                                                sigma=w.sigma, mask=w.mask, window=w.window,
@@ -48,8 +53,13 @@ def test_graph_replays_match_eager(w, noalloc):
     ws = None if noalloc else attn.alloc_workspace(w.B, w.H, w.N, w.d, var)
     scale = first["scale"]
 
+    plan = attn.FwdPlan(q, k, v, o, lse, scale, var, workspace=ws, **kw) if how == "plan" \
+        else None
+
     def call(out, l):
-        if noalloc:
+        if plan is not None and out is o:
+            plan()
+        elif noalloc:
             attn.attn_fwd_noalloc(q, k, v, out, l, scale, var, **kw)
         else:
             attn.attn_fwd(q, k, v, out, l, scale, var, workspace=ws, **kw)
@@ -57,7 +67,7 @@ def test_graph_replays_match_eager(w, noalloc):
     call(o, lse)  # first call outside the capture (resolves the static scratch on the device)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    print(f"[gpu] capture {w.name} noalloc={noalloc}", flush=True)
+    print(f"[gpu] capture {w.name} {how}", flush=True)
     with torch.cuda.graph(g):
         call(o, lse)
     o_ref = torch.empty_like(o)

@@ -122,6 +122,19 @@ SMALL = [
 ]
 
 
+def paths_for(N, d):
+    """Forward kernels that take a shape: sequences of at most 256 keys (d 64 or 128) run on
+    the single-launch short kernel by default and are also checked on the tiled kernel."""
+    return ["short", "tiled"] if N <= 256 and d <= 128 else ["auto"]
+
+
+def set_path(monkeypatch, path):
+    if path == "auto":
+        monkeypatch.delenv("ATTN_FWD_PATH", raising=False)
+    else:
+        monkeypatch.setenv("ATTN_FWD_PATH", path)
+
+
 def small_inputs(name, B, H, N, d, mask, window, alibi, softcap, sigma, seed):
     w = inputs.Workload(name, B=B, H=H, N=N, d=d, sigma=sigma, mask=mask, window=window,
                         alibi=alibi, softcap=softcap, seed=seed)
@@ -131,16 +144,22 @@ def small_inputs(name, B, H, N, d, mask, window, alibi, softcap, sigma, seed):
     return w, inputs.make_inputs(w)
 
 
-@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_small_shapes(case):
+SMALL_PATHS = [(c, p) for c in SMALL for p in paths_for(c[3], c[4])]
+
+
+@pytest.mark.parametrize("case,path", SMALL_PATHS, ids=[f"{c[0]}-{p}" for c, p in SMALL_PATHS])
+def test_small_shapes(case, path, monkeypatch):
+    set_path(monkeypatch, path)
     w, inp = small_inputs(*case, seed=1000 + SMALL.index(case))
     o32, l32 = run_gpu(inp, w, out_f32=True)
     o16, l16 = run_gpu(inp, w, out_f32=False)
     check(w, inp, o32, l32, o16, l16)
 
 
-def test_document_length_one_docs():
+@pytest.mark.parametrize("path", ["short", "tiled"])
+def test_document_length_one_docs(path, monkeypatch):
     # every token its own document: each row attends to itself only, O = v, L = s_ii
+    set_path(monkeypatch, path)
     B, H, N, d = 1, 2, 130, 64
     w = inputs.Workload("doc_len1", B=B, H=H, N=N, d=d, mask="document", seed=77)
     inp = inputs.make_inputs(w)
@@ -269,8 +288,9 @@ def test_deterministic_and_no_allocation():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
-def test_constant_v():
-    w = inputs.Workload("constv", B=1, H=2, N=1000, d=128, mask="causal", seed=9, sigma=2.0)
+@pytest.mark.parametrize("N", [1000, 200])
+def test_constant_v(N):
+    w = inputs.Workload("constv", B=1, H=2, N=N, d=128, mask="causal", seed=9, sigma=2.0)
     inp = inputs.make_inputs(w)
     c = inputs.f32_to_bf16_bits(np.random.default_rng(1).standard_normal((1, 2, 1, 128))
                                 .astype(np.float32))
@@ -309,11 +329,17 @@ SCALE_CASES = [
     ("scaleneg_causal_d128", 2, 2, 600, 128, "causal", 0, 1.0, -1.0 / 128 ** 0.5),
     ("scaleneg_window_d128", 1, 2, 500, 128, "window", 100, 1.0, -0.09),
     ("scaleneg_doc_d64", 2, 1, 400, 64, "document", 0, 1.0, -0.3),
+    ("scaleneg_causal_d128_n200", 1, 2, 200, 128, "causal", 0, 1.0, -0.2),
+    ("scale0_doc_d64_n250", 2, 1, 250, 64, "document", 0, 1.0, 0.0),
 ]
 
 
-@pytest.mark.parametrize("case", SCALE_CASES, ids=[c[0] for c in SCALE_CASES])
-def test_scale_not_positive(case):
+SCALE_PATHS = [(c, p) for c in SCALE_CASES for p in paths_for(c[3], c[4])]
+
+
+@pytest.mark.parametrize("case,path", SCALE_PATHS, ids=[f"{c[0]}-{p}" for c, p in SCALE_PATHS])
+def test_scale_not_positive(case, path, monkeypatch):
+    set_path(monkeypatch, path)
     name, B, H, N, d, mask, window, sigma, scale = case
     extra = {"doc_len_range": (1, 130)} if mask == "document" else {}
     w = inputs.Workload(name, B=B, H=H, N=N, d=d, sigma=sigma, mask=mask, window=window,
@@ -344,11 +370,12 @@ def test_binding_rejects_mixed_devices():
                                                device=DEV))
 
 
-def test_v_beyond_fp16_range_saturates():
+@pytest.mark.parametrize("N", [300, 200])
+def test_v_beyond_fp16_range_saturates(N):
     """Values of V beyond fp16's range (|v| > 65504, representable in bf16) enter P V saturated to
     +-65504, as include/attn.h states: O equals the attention of the clipped V (relative to the
     magnitudes involved), and differs from the unclipped one where such a value carries weight."""
-    w = inputs.Workload("v_sat", B=1, H=2, N=300, d=64, mask="causal", seed=1300)
+    w = inputs.Workload("v_sat", B=1, H=2, N=N, d=64, mask="causal", seed=1300)
     inp = inputs.make_inputs(w)
     v = inputs.bf16_bits_to_f32(inp["v"]).copy()
     v[0, 0, 5, 3] = 1.0e5
@@ -370,3 +397,78 @@ def test_v_beyond_fp16_range_saturates():
     assert np.abs(got - O_clip)[other].max() <= TOL_O
     assert np.abs(l32.cpu().numpy() - L_ref).max() <= TOL_L
     assert np.abs(got - O_raw).max() > 1.0e3  # the saturation is visible where |v| > 65504
+
+
+# --- the short-sequence kernel beyond its default grid, and the path override -------------------
+SHORT_BIG = [
+    # (name, B, H, N, d, mask, window, alibi, softcap, sigma): grids of over 1000 workgroups of
+    # 64 rows, each run on both kernels
+    ("short_big_causal_alibi_softcap_d128", 4, 80, 256, 128, "causal", 0, True, 20.0, 2.0),
+    ("short_big_doc_d64", 8, 48, 233, 64, "document", 0, False, 0.0, 1.0),
+    ("short_big_window_d64", 2, 160, 250, 64, "window", 37, True, 0.0, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", SHORT_BIG, ids=[c[0] for c in SHORT_BIG])
+@pytest.mark.parametrize("path", ["short", "tiled"])
+def test_short_kernel_large_grid(case, path, monkeypatch):
+    set_path(monkeypatch, path)
+    w, inp = small_inputs(*case, seed=1400 + SHORT_BIG.index(case))
+    o32, l32 = run_gpu(inp, w, out_f32=True)
+    o16, l16 = run_gpu(inp, w, out_f32=False)
+    rng = np.random.default_rng(5)
+    heads = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 12),
+                                                     rng.integers(0, w.H, 12))}
+                   | {(0, 0), (w.B - 1, w.H - 1)})
+    check(w, inp, o32, l32, o16, l16, heads=heads)
+
+
+def test_path_override_errors(monkeypatch):
+    q = torch.zeros(1, 1, 300, 64, dtype=torch.bfloat16, device=DEV)
+    o = torch.zeros_like(q)
+    monkeypatch.setenv("ATTN_FWD_PATH", "short")
+    with pytest.raises(attn.AttnError, match="ATTN_FWD_PATH=short") as e:
+        attn.attn_fwd(q, q, q, o, None, 0.125, 0)
+    assert e.value.code == attn.ATTN_ERR_INVALID_ARG
+    q2 = torch.zeros(1, 1, 100, 256, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(attn.AttnError, match="ATTN_FWD_PATH=short"):
+        attn.attn_fwd(q2, q2, q2, torch.zeros_like(q2), None, 0.125, 0)
+    q3 = torch.zeros(1, 1, 100, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(attn.AttnError, match="ATTN_FWD_PATH=short"):
+        attn.attn_fwd(q3, q3, q3, torch.zeros_like(q3), None, 0.125,
+                      attn.variant_bits(fp8=True))
+    monkeypatch.setenv("ATTN_FWD_PATH", "fast")
+    with pytest.raises(attn.AttnError, match="must be 'tiled' or 'short'"):
+        attn.attn_fwd(q, q, q, o, None, 0.125, 0)
+
+
+# --- FwdPlan: the forward pass on fixed buffers, marshalled once ---------------------------------
+@pytest.mark.parametrize("noalloc", [False, True], ids=["attn_fwd", "attn_fwd_noalloc"])
+@pytest.mark.parametrize("N", [200, 700])
+def test_fwd_plan_matches_attn_fwd(N, noalloc):
+    """A plan's calls equal attn_fwd's bit for bit, also after the input contents change."""
+    w = inputs.Workload("plan", B=2, H=3, N=N, d=64, mask="window", window=90, alibi=True,
+                        seed=1500)
+    inp = inputs.make_inputs(w)
+    var = attn.variant_bits(w.mask, w.alibi, False)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    sl = torch.from_numpy(inp["slopes"]).to(DEV)
+    o = torch.full((w.B, w.H, N, w.d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((w.B, w.H, N), float("nan"), device=DEV)
+    o_ref, l_ref = torch.empty_like(o), torch.empty_like(lse)
+    plan = attn.FwdPlan(q, k, v, o, lse, inp["scale"], var, window=w.window, alibi_slopes=sl,
+                        noalloc=noalloc)
+    print(f"[gpu] FwdPlan N={N} noalloc={noalloc}", flush=True)
+    for r in range(2):
+        if r:
+            q.copy_(dev_bf16(inputs.make_inputs(inputs.Workload(
+                "plan2", B=2, H=3, N=N, d=64, seed=1501))["q"]))
+        plan()
+        attn.attn_fwd(q, k, v, o_ref, l_ref, inp["scale"], var, window=w.window,
+                      alibi_slopes=sl)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), r
+        assert torch.equal(lse, l_ref), r
+    with pytest.raises(ValueError, match="no workspace"):
+        attn.FwdPlan(q, k, v, o, lse, 0.1, var, window=w.window, alibi_slopes=sl, noalloc=True,
+                     workspace=attn.alloc_workspace(w.B, w.H, N, w.d, var))
