@@ -1,13 +1,18 @@
 // Roofline calibration microbenchmarks for gfx950 (a standalone executable, not part of
-// libattn.so).  Each kernel runs a fixed, bounded amount of work per wave over the whole chip;
-// rates are derived from hipEvent timings.  Results feed the roofline figures used to judge the
-// attention forward kernel: dense bf16 MFMA rate, v_exp_f32 and v_fma_f32 issue rates, whether
-// transcendental and MFMA work overlap on one SIMD, LDS read bandwidth and HBM copy bandwidth.
+// libattn.so).  Each kernel runs a fixed, bounded amount of work per wave.  The issue-rate
+// kernels time themselves in core cycles (s_memtime inside the kernel, the median over the
+// workgroups) at a stated number of waves per SIMD: one 4-wave workgroup per CU places one wave
+// on each SIMD, so a grid of k workgroups per CU runs k waves per SIMD.  The bandwidth kernels
+// are timed with hipEvents.  Results feed the roofline figures used to judge the attention
+// forward kernel: the MFMA rate and the core clock under it, the cost of transcendental and FMA
+// instructions alone and mixed, the forward kernel's per-score probability work, how matrix-core
+// and vector waves share a SIMD, LDS read bandwidth and HBM bandwidth.
 //
-//   make micro && ./micro
+//   make micro && ./micro_bench
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <utility>
 #include <vector>
 
 #include <cstdio>
@@ -16,6 +21,7 @@
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned long long u64;
 
 #define CHECK(x)                                                               \
   do {                                                                         \
@@ -26,16 +32,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
     }                                                                          \
   } while (0)
 
-constexpr int kIters = 4096;
+constexpr int kIters = 2048;
+constexpr int kHwRegSimdId = (4) | (4 << 6) | ((2 - 1) << 11);  // HW_ID bits 4..5: SIMD id
 
-// 4 independent accumulator chains of v_mfma_f32_32x32x16_bf16 per wave.
-__global__ __launch_bounds__(256) void mfma_rate(float *out, float seed) {
+// 4 independent accumulator chains of v_mfma_f32_32x32x16_bf16 per wave; core cycles (s_memtime)
+// and 100 MHz wall-clock ticks (s_memrealtime) over the loop.
+__global__ __launch_bounds__(256) void mfma_cycles(u64 *clk, float seed) {
   bf16x8 a, b;
   for (int i = 0; i < 8; ++i) {
     a[i] = (__bf16)(seed * (threadIdx.x + i));
     b[i] = (__bf16)(seed * (i + 1));
   }
   f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  const u64 t0 = __builtin_amdgcn_s_memtime();
+  const u64 r0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < kIters; ++it) {
     c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
     c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
@@ -44,82 +54,138 @@ __global__ __launch_bounds__(256) void mfma_rate(float *out, float seed) {
   }
   float s = 0.f;
   for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
-  if (s == 1234.5f) out[threadIdx.x] = s;
-}
-
-// The same MFMA stream, 4x longer, with the shader clock measured inside the kernel: thread 0 of
-// each workgroup records the elapsed s_memtime cycles (core clock) and s_memrealtime ticks
-// (constant wall clock) around its loop.
-__global__ __launch_bounds__(256) void mfma_clock(unsigned long long *clk, float seed) {
-  bf16x8 a, b;
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(seed * (threadIdx.x + i));
-    b[i] = (__bf16)(seed * (i + 1));
-  }
-  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
-  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
-  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
-  for (int it = 0; it < 4 * kIters; ++it) {
-    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
-    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
-    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
-    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
-  }
-  float s = 0.f;
-  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
-  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
-  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  const u64 t1 = __builtin_amdgcn_s_memtime();
+  const u64 r1 = __builtin_amdgcn_s_memrealtime();
   if (threadIdx.x == 0) {
     clk[2 * blockIdx.x] = t1 - t0;
     clk[2 * blockIdx.x + 1] = (r1 - r0) + (s == 1234.5f);
   }
 }
 
-// 8 independent chains of v_exp_f32 per lane.
-__global__ __launch_bounds__(256) void exp_rate(float *out, float seed) {
-  float x[8];
+// One loop iteration of vector instructions, written as a single asm block so that the compiler
+// keeps the order: 8 independent registers x for transcendentals, 16 independent y for FMAs.
+//   KIND 0: 8 v_exp_f32      KIND 1: 8 v_rcp_f32      KIND 2: 16 v_fma_f32
+//   KIND 3: 8 x (v_exp_f32, v_fma_f32, v_fma_f32), interleaved
+#define VOPS                                                                                    \
+  "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),         \
+      "+v"(x[7]), "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]),     \
+      "+v"(y[6]), "+v"(y[7]), "+v"(y[8]), "+v"(y[9]), "+v"(y[10]), "+v"(y[11]), "+v"(y[12]),  \
+      "+v"(y[13]), "+v"(y[14]), "+v"(y[15])
+#define T8(op)                                                                                  \
+  op " %0, %0\n" op " %1, %1\n" op " %2, %2\n" op " %3, %3\n" op " %4, %4\n" op " %5, %5\n" op \
+     " %6, %6\n" op " %7, %7\n"
+#define F(r) "v_fma_f32 %" #r ", %" #r ", %24, %25\n"
+#define F16 F(8) F(9) F(10) F(11) F(12) F(13) F(14) F(15) F(16) F(17) F(18) F(19) F(20) F(21) F(22) F(23)
+#define EFF(e, f0, f1) "v_exp_f32 %" #e ", %" #e "\n" F(f0) F(f1)
+#define EFF8                                                                                    \
+  EFF(0, 8, 9) EFF(1, 10, 11) EFF(2, 12, 13) EFF(3, 14, 15) EFF(4, 16, 17) EFF(5, 18, 19)       \
+  EFF(6, 20, 21) EFF(7, 22, 23)
+
+template <int KIND>
+__device__ __forceinline__ void valu_iter(float (&x)[8], float (&y)[16], float fa, float fb) {
+  if constexpr (KIND == 0) asm volatile(T8("v_exp_f32") : VOPS : "v"(fa), "v"(fb));
+  if constexpr (KIND == 1) asm volatile(T8("v_rcp_f32") : VOPS : "v"(fa), "v"(fb));
+  if constexpr (KIND == 2) asm volatile(F16 : VOPS : "v"(fa), "v"(fb));
+  if constexpr (KIND == 3) asm volatile(EFF8 : VOPS : "v"(fa), "v"(fb));
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void valu_cycles(float *out, u64 *cyc, float seed) {
+  float x[8], y[16];
   for (int i = 0; i < 8; ++i) x[i] = seed * (threadIdx.x + i) * 1e-3f;
-  for (int it = 0; it < kIters; ++it) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(x[i]) - 1.0f;
-  }
+  for (int i = 0; i < 16; ++i) y[i] = seed * (threadIdx.x + 2 * i);
+  const u64 t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < kIters; ++it) valu_iter<KIND>(x, y, 0.999f, 0.001f);
+  const u64 t1 = __builtin_amdgcn_s_memtime();
   float s = 0.f;
   for (int i = 0; i < 8; ++i) s += x[i];
+  for (int i = 0; i < 16; ++i) s += y[i];
   if (s == 1234.5f) out[threadIdx.x] = s;
+  if (threadIdx.x == 0) cyc[blockIdx.x] = (t1 - t0) / kIters;
 }
 
-// 8 independent chains of v_fma_f32 per lane.
-__global__ __launch_bounds__(256) void fma_rate(float *out, float seed) {
-  float x[8];
-  for (int i = 0; i < 8; ++i) x[i] = seed * (threadIdx.x + i);
-  for (int it = 0; it < kIters; ++it) {
+// Dependent v_fma_f32 chain in one wave (latency): 64 dependent FMAs per iteration.
+__global__ __launch_bounds__(64) void fma_latency(float *out, u64 *cyc, float seed) {
+  float x = seed * threadIdx.x;
+  const u64 t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < kIters / 16; ++it) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = fmaf(x[i], 0.999f, 0.001f);
+    for (int i = 0; i < 64; ++i) x = fmaf(x, 0.999f, 0.001f);
   }
-  float s = 0.f;
-  for (int i = 0; i < 8; ++i) s += x[i];
-  if (s == 1234.5f) out[threadIdx.x] = s;
+  const u64 t1 = __builtin_amdgcn_s_memtime();
+  if (x == 1234.5f) out[threadIdx.x] = x;
+  if (threadIdx.x == 0) cyc[blockIdx.x] = (t1 - t0) / (kIters / 16 * 64);
 }
 
-// Even waves run the MFMA loop, odd waves the exp loop: two waves share each SIMD.
-__global__ __launch_bounds__(512) void mixed_rate(float *out, float seed) {
-  const int wave = threadIdx.x >> 6;
-  float s = 0.f;
-  if (wave & 1) {
-    float x[8];
-    for (int i = 0; i < 8; ++i) x[i] = seed * (threadIdx.x + i) * 1e-3f;
-    for (int it = 0; it < kIters; ++it) {
+// The per-score vector work of the forward kernel's softmax phase: 32 independent scores per
+// lane per iteration (one lane's share of a 64-key tile), each turned into a probability that is
+// summed and packed to fp16 as the P V operand.  SOFTCAP: u = 1 / (1 + 2^(c x)), a running
+// minimum of u (the tile maximum of the capped score) and p = 2^(A - B u): three
+// transcendentals per score.  Otherwise a running maximum and p = 2^(x - A): one.  The scores
+// are made opaque each iteration so that nothing is hoisted out of the loop.
+template <bool SOFTCAP>
+__global__ __launch_bounds__(256) void prob_chain(float *out, u64 *cyc, float seed) {
+  typedef __fp16 h2 __attribute__((ext_vector_type(2)));
+  constexpr int kRounds = 512;
+  float s[32];
+  for (int j = 0; j < 32; ++j) s[j] = seed * (threadIdx.x + j);
+  const float c = 0.0961f, A = 43.2f, B = 86.5f;
+  float l = 0.f, mx = 0.f;
+  const u64 t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < kRounds; ++it) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(x[i]) - 1.0f;
+    for (int j = 0; j < 32; ++j) asm volatile("" : "+v"(s[j]));
+    float t = SOFTCAP ? __builtin_inff() : -__builtin_inff(), sum = 0.f;
+    float p[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (SOFTCAP) {
+        const float u = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(s[j] * c));
+        t = fminf(t, u);
+        p[j] = __builtin_amdgcn_exp2f(fmaf(u, -B, A));
+      } else {
+        t = fmaxf(t, s[j]);
+        p[j] = __builtin_amdgcn_exp2f(s[j] - A);
+      }
+      sum += p[j];
     }
-    for (int i = 0; i < 8; ++i) s += x[i];
-  } else {
+#pragma unroll
+    for (int j = 0; j < 32; j += 2) {
+      const h2 pk = __builtin_amdgcn_cvt_pkrtz(p[j], p[j + 1]);
+      asm volatile("" ::"v"(pk));
+    }
+    l += sum;
+    mx += t;
+  }
+  const u64 t1 = __builtin_amdgcn_s_memtime();
+  if (l + mx == 1234.5f) out[threadIdx.x] = l;
+  if (threadIdx.x == 0) cyc[blockIdx.x] = (t1 - t0) / kRounds;
+}
+
+// Two waves per SIMD (one 8-wave workgroup per CU) with different roles: on each SIMD the wave
+// with the lower wave number (SIMD id from HW_ID) runs the MFMA loop of mfma_cycles, the other
+// one a vector loop (KIND of valu_cycles: 0 exp, 2 fma) for twice as many iterations.  ROLES
+// selects which of the two run (1: matrix only, 2: vector only, 3: both).  cyc gets each wave's
+// core cycles, with bit 63 set for the matrix role.
+template <int KIND, int ROLES>
+__global__ __launch_bounds__(512) void pair_cycles(float *out, u64 *cyc, float seed) {
+  __shared__ int simd_of[8];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) simd_of[wave] = __builtin_amdgcn_s_getreg(kHwRegSimdId) & 3;
+  __syncthreads();
+  int rank = 0;
+  for (int w = 0; w < wave; ++w) rank += simd_of[w] == simd_of[wave];
+  const bool mat = __builtin_amdgcn_readfirstlane(rank) == 0;
+  u64 dt = 0;
+  float s = 0.f;
+  if (mat && (ROLES & 1)) {
     bf16x8 a, b;
     for (int i = 0; i < 8; ++i) {
       a[i] = (__bf16)(seed * (threadIdx.x + i));
       b[i] = (__bf16)(seed * (i + 1));
     }
     f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    const u64 t0 = __builtin_amdgcn_s_memtime();
     for (int it = 0; it < kIters; ++it) {
       c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
       c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
@@ -127,8 +193,19 @@ __global__ __launch_bounds__(512) void mixed_rate(float *out, float seed) {
       c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
     }
     for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+    dt = __builtin_amdgcn_s_memtime() - t0;
+  } else if (!mat && (ROLES & 2)) {
+    float x[8], y[16];
+    for (int i = 0; i < 8; ++i) x[i] = seed * (threadIdx.x + i) * 1e-3f;
+    for (int i = 0; i < 16; ++i) y[i] = seed * (threadIdx.x + 2 * i);
+    const u64 t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < 2 * kIters; ++it) valu_iter<KIND>(x, y, 0.999f, 0.001f);
+    for (int i = 0; i < 8; ++i) s += x[i];
+    for (int i = 0; i < 16; ++i) s += y[i];
+    dt = __builtin_amdgcn_s_memtime() - t0;
   }
   if (s == 1234.5f) out[threadIdx.x] = s;
+  if (lane == 0) cyc[blockIdx.x * 8 + wave] = dt | ((u64)mat << 63);
 }
 
 // ds_read_b128 from a 32 KB LDS array: each lane reads a 16-byte chunk of its own row (pitch
@@ -140,7 +217,7 @@ __global__ __launch_bounds__(256) void lds_rate(float *out, float seed) {
   const int lane = threadIdx.x & 63;
   const float *base = &lds[(lane & 31) * 68 + (lane >> 5) * 4];
   f32x4 acc = {};
-  for (int it = 0; it < kIters; ++it) {
+  for (int it = 0; it < 2 * kIters; ++it) {
     asm volatile("" ::: "memory");  // the reads are loop-invariant: force them every iteration
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -149,66 +226,6 @@ __global__ __launch_bounds__(256) void lds_rate(float *out, float seed) {
     }
   }
   if (acc[0] + acc[1] + acc[2] + acc[3] == 1234.5f) out[threadIdx.x] = acc[0];
-}
-
-// Dependent v_fma_f32 chain in one wave (latency): 64 dependent FMAs per iteration.
-__global__ __launch_bounds__(64) void fma_latency(float *out, float seed) {
-  float x = seed * threadIdx.x;
-  for (int it = 0; it < kIters / 16; ++it) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) x = fmaf(x, 0.999f, 0.001f);
-  }
-  if (x == 1234.5f) out[threadIdx.x] = x;
-}
-
-// Interleaved independent exp and fma chains in one wave: do the transcendental and FMA work
-// overlap?
-__global__ __launch_bounds__(256) void expfma_rate(float *out, float seed) {
-  float x[8], y[8];
-  for (int i = 0; i < 8; ++i) {
-    x[i] = seed * (threadIdx.x + i) * 1e-3f;
-    y[i] = seed * (threadIdx.x + 2 * i);
-  }
-  for (int it = 0; it < kIters; ++it) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x[i] = __builtin_amdgcn_exp2f(x[i]);
-      y[i] = fmaf(y[i], 0.999f, 0.001f);
-    }
-  }
-  float s = 0.f;
-  for (int i = 0; i < 8; ++i) s += x[i] + y[i];
-  if (s == 1234.5f) out[threadIdx.x] = s;
-}
-
-// Even waves MFMA, odd waves FMA.
-__global__ __launch_bounds__(512) void mixed_fma(float *out, float seed) {
-  const int wave = threadIdx.x >> 6;
-  float s = 0.f;
-  if (wave & 1) {
-    float x[8];
-    for (int i = 0; i < 8; ++i) x[i] = seed * (threadIdx.x + i);
-    for (int it = 0; it < kIters; ++it) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = fmaf(x[i], 0.999f, 0.001f);
-    }
-    for (int i = 0; i < 8; ++i) s += x[i];
-  } else {
-    bf16x8 a, b;
-    for (int i = 0; i < 8; ++i) {
-      a[i] = (__bf16)(seed * (threadIdx.x + i));
-      b[i] = (__bf16)(seed * (i + 1));
-    }
-    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
-    for (int it = 0; it < kIters; ++it) {
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
-      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
-      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
-    }
-    for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
-  }
-  if (s == 1234.5f) out[threadIdx.x] = s;
 }
 
 // Read-only stream: 8 independent 16-byte loads in flight per lane, XOR-folded.
@@ -259,6 +276,30 @@ float time_ms(F launch, int reps) {
   return ms / reps;
 }
 
+// Runs launch twice (the first warms up) and returns the n values it left in cyc.
+template <typename F>
+std::vector<u64> cycles(F launch, const u64 *cyc, int n) {
+  for (int r = 0; r < 2; ++r) {
+    launch();
+    CHECK(hipDeviceSynchronize());
+  }
+  std::vector<u64> h(n);
+  CHECK(hipMemcpy(h.data(), cyc, n * sizeof(u64), hipMemcpyDeviceToHost));
+  return h;
+}
+
+double median(std::vector<double> v) {
+  if (v.empty()) return 0.0;
+  std::sort(v.begin(), v.end());
+  return v[v.size() / 2];
+}
+
+template <typename F>
+double median_cycles(F launch, const u64 *cyc, int n) {
+  const std::vector<u64> h = cycles(launch, cyc, n);
+  return median(std::vector<double>(h.begin(), h.end()));
+}
+
 int main() {
   hipDeviceProp_t p;
   CHECK(hipGetDeviceProperties(&p, 0));
@@ -266,80 +307,84 @@ int main() {
   printf("device %s, %d CUs, clock %.0f MHz\n", p.gcnArchName, cus, p.clockRate / 1e3);
   float *out;
   CHECK(hipMalloc(&out, 4096 * sizeof(float)));
+  u64 *cyc;  // 8 entries per workgroup, for up to 4 workgroups per CU
+  CHECK(hipMalloc(&cyc, 8 * 4 * cus * sizeof(u64)));
   const float seed = 1e-3f;
 
-  // One workgroup of 4 waves per CU -> 1 wave per SIMD; 2 per CU -> 2 waves per SIMD.
-  for (int wg_per_cu = 1; wg_per_cu <= 2; ++wg_per_cu) {
-    const int grid = cus * wg_per_cu * 8;
-    float ms = time_ms([&] { mfma_rate<<<grid, 256>>>(out, seed); }, 5);
-    const double flops = (double)grid * 4 * kIters * 4 * 32768.0;
-    printf("mfma bf16 32x32x16, %d wave/SIMD: %.1f TFLOP/s (%.2f cycles/MFMA/SIMD at 2.4 GHz)\n",
-           wg_per_cu, flops / ms / 1e9, ms * 1e-3 * 2.4e9 / ((double)grid * 4 * kIters * 4 / (cus * 4)));
-    ms = time_ms([&] { exp_rate<<<grid, 256>>>(out, seed); }, 5);
-    double ops = (double)grid * 256 * kIters * 8;
-    printf("v_exp_f32, %d wave/SIMD: %.1f Gop/s = %.2f lane-ops/clk/CU at 2.4 GHz\n", wg_per_cu,
-           ops / ms / 1e6, ops / (ms * 1e-3) / 2.4e9 / cus);
-    ms = time_ms([&] { fma_rate<<<grid, 256>>>(out, seed); }, 5);
-    printf("v_fma_f32, %d wave/SIMD: %.1f Gop/s = %.2f lane-ops/clk/CU at 2.4 GHz\n", wg_per_cu,
-           ops / ms / 1e6, ops / (ms * 1e-3) / 2.4e9 / cus);
-  }
-  // The core clock under sustained MFMA load (one wave per SIMD), from inside the kernel.
+  // The MFMA issue rate and the core clock under it, one and two waves per SIMD.
   {
     int wall_khz = 0;
     CHECK(hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, 0));
-    const int grid = cus;
-    unsigned long long *clk;
-    CHECK(hipMalloc(&clk, 2 * grid * sizeof(unsigned long long)));
-    const float ms = time_ms([&] { mfma_clock<<<grid, 256>>>(clk, seed); }, 3);
-    std::vector<unsigned long long> h(2 * grid);
-    CHECK(hipMemcpy(h.data(), clk, h.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost));
-    std::vector<double> mhz, cyc;
-    for (int g = 0; g < grid; ++g) {
-      mhz.push_back((double)h[2 * g] / (double)h[2 * g + 1] * wall_khz / 1e3);
-      cyc.push_back((double)h[2 * g] / (4.0 * kIters * 4));
+    for (int wps = 1; wps <= 2; ++wps) {
+      const int grid = cus * wps;
+      const float ms = time_ms([&] { mfma_cycles<<<grid, 256>>>(cyc, seed); }, 3);
+      std::vector<u64> h(2 * grid);
+      CHECK(hipMemcpy(h.data(), cyc, h.size() * sizeof(u64), hipMemcpyDeviceToHost));
+      std::vector<double> mhz, per;
+      for (int g = 0; g < grid; ++g) {
+        mhz.push_back((double)h[2 * g] / (double)h[2 * g + 1] * wall_khz / 1e3);
+        per.push_back((double)h[2 * g] / (4.0 * kIters) / wps);
+      }
+      const double flops = (double)grid * 4 * 4 * kIters * 32768.0;
+      std::sort(mhz.begin(), mhz.end());
+      printf("mfma bf16 32x32x16, %d wave/SIMD: %.2f core cycles per MFMA per SIMD; core clock "
+             "median %.0f MHz (min %.0f, max %.0f; s_memtime against s_memrealtime at %d kHz); "
+             "%.1f TFLOP/s\n",
+             wps, median(per), mhz[grid / 2], mhz[0], mhz[grid - 1], wall_khz, flops / ms / 1e9);
     }
-    std::sort(mhz.begin(), mhz.end());
-    std::sort(cyc.begin(), cyc.end());
-    const double flops = (double)grid * 4 * 4 * kIters * 4 * 32768.0;
-    printf("core clock under MFMA load (s_memtime / s_memrealtime at %d kHz): median %.0f MHz "
-           "(min %.0f, max %.0f); %.2f core cycles per 32x32x16 MFMA; %.1f TFLOP/s\n",
-           wall_khz, mhz[grid / 2], mhz[0], mhz[grid - 1], cyc[grid / 2], flops / ms / 1e9);
-    CHECK(hipFree(clk));
   }
-  // Throughput-bound VALU: 4 waves per SIMD (four 256-thread workgroups per CU).
-  {
-    const int grid = cus * 4;
-    float ms = time_ms([&] { fma_rate<<<grid * 4, 256>>>(out, seed); }, 5);
-    double ops = (double)grid * 1024 * kIters * 8;
-    printf("v_fma_f32, 4 wave/SIMD: %.2f lane-ops/clk/CU (%.2f cycles per wave64 instruction per SIMD)\n",
-           ops / (ms * 1e-3) / 2.4e9 / cus, 64.0 * 4 / (ops / (ms * 1e-3) / 2.4e9 / cus));
-    ms = time_ms([&] { exp_rate<<<grid * 4, 256>>>(out, seed); }, 5);
-    printf("v_exp_f32 (+1 sub each), 4 wave/SIMD: %.2f exp lane-ops/clk/CU\n", ops / (ms * 1e-3) / 2.4e9 / cus);
-    ms = time_ms([&] { expfma_rate<<<grid * 4, 256>>>(out, seed); }, 5);
-    printf("exp + fma interleaved, 4 wave/SIMD: %.2f (exp+fma) lane-ops/clk/CU\n", 2 * ops / (ms * 1e-3) / 2.4e9 / cus);
-    ms = time_ms([&] { fma_latency<<<cus * 4, 64>>>(out, seed); }, 3);
-    printf("dependent v_fma_f32 chain, 1 wave: %.2f cycles per FMA\n", ms * 1e-3 * 2.4e9 / ((double)(kIters / 16) * 64));
+  // Vector instruction cost per SIMD, one, two and four waves per SIMD.
+  for (int wps = 1; wps <= 4; wps *= 2) {
+    const int grid = cus * wps;
+    const double e = median_cycles([&] { valu_cycles<0><<<grid, 256>>>(out, cyc, seed); }, cyc, grid);
+    const double r = median_cycles([&] { valu_cycles<1><<<grid, 256>>>(out, cyc, seed); }, cyc, grid);
+    const double f = median_cycles([&] { valu_cycles<2><<<grid, 256>>>(out, cyc, seed); }, cyc, grid);
+    const double m = median_cycles([&] { valu_cycles<3><<<grid, 256>>>(out, cyc, seed); }, cyc, grid);
+    printf("%d wave/SIMD, core cycles per wave64 instruction per SIMD: v_exp_f32 %.2f, v_rcp_f32 "
+           "%.2f, v_fma_f32 %.2f; 1 exp + 2 fma interleaved %.2f per group (%.2f apart)\n",
+           wps, e / 8 / wps, r / 8 / wps, f / 16 / wps, m / 8 / wps, (e + f) / 8 / wps);
   }
   {
-    const int grid = cus * 8;
-    const float ms_mf = time_ms([&] { mixed_fma<<<grid, 512>>>(out, seed); }, 5);
-    const float ms_f = time_ms([&] { fma_rate<<<grid, 256>>>(out, seed); }, 5);
-    const float ms_mm = time_ms([&] { mfma_rate<<<grid, 256>>>(out, seed); }, 5);
-    printf("overlap: mfma wave + fma wave per SIMD %.3f ms vs mfma alone %.3f ms, fma alone %.3f ms\n",
-           ms_mf, ms_mm, ms_f);
+    const double l = median_cycles([&] { fma_latency<<<cus * 4, 64>>>(out, cyc, seed); }, cyc, cus * 4);
+    printf("dependent v_fma_f32 chain, 1 wave: %.2f core cycles per FMA\n", l);
   }
+  // Softmax-phase vector work per score.
+  for (int wps = 1; wps <= 4; wps *= 2) {
+    const int grid = cus * wps;
+    const double sc = median_cycles([&] { prob_chain<true><<<grid, 256>>>(out, cyc, seed); }, cyc, grid);
+    const double pl = median_cycles([&] { prob_chain<false><<<grid, 256>>>(out, cyc, seed); }, cyc, grid);
+    printf("probability per score, %d wave/SIMD: soft-cap %.1f, plain %.1f core cycles per SIMD\n",
+           wps, sc / 32 / wps, pl / 32 / wps);
+  }
+  // One matrix-core wave and one vector wave per SIMD: each role's core cycles, together and
+  // with the other role idle.
   {
-    const int grid = cus * 8;
-    const float ms_mix = time_ms([&] { mixed_rate<<<grid, 512>>>(out, seed); }, 5);
-    const float ms_m = time_ms([&] { mfma_rate<<<grid, 256>>>(out, seed); }, 5);
-    const float ms_e = time_ms([&] { exp_rate<<<grid, 256>>>(out, seed); }, 5);
-    printf("overlap: mfma wave + exp wave per SIMD %.3f ms vs mfma alone %.3f ms, exp alone %.3f "
-           "ms (sum %.3f)\n", ms_mix, ms_m, ms_e, ms_m + ms_e);
+    const int grid = cus, n = 8 * grid;
+    auto roles = [&](auto launch) {
+      const std::vector<u64> h = cycles(launch, cyc, n);
+      std::vector<double> mt, vt;
+      for (u64 x : h) {
+        const double c = (double)(x & ~(1ull << 63));
+        if (c == 0) continue;  // an idle role
+        ((x >> 63) ? mt : vt).push_back(c);
+      }
+      return std::make_pair(median(mt), median(vt));
+    };
+    const std::pair<double, double> eb = roles([&] { pair_cycles<0, 3><<<grid, 512>>>(out, cyc, seed); });
+    const std::pair<double, double> em = roles([&] { pair_cycles<0, 1><<<grid, 512>>>(out, cyc, seed); });
+    const std::pair<double, double> ev = roles([&] { pair_cycles<0, 2><<<grid, 512>>>(out, cyc, seed); });
+    printf("one mfma wave + one exp wave per SIMD, core cycles: together mfma %.0f, exp %.0f; "
+           "alone mfma %.0f, exp %.0f\n", eb.first, eb.second, em.first, ev.second);
+    const std::pair<double, double> fb = roles([&] { pair_cycles<2, 3><<<grid, 512>>>(out, cyc, seed); });
+    const std::pair<double, double> fm = roles([&] { pair_cycles<2, 1><<<grid, 512>>>(out, cyc, seed); });
+    const std::pair<double, double> fv = roles([&] { pair_cycles<2, 2><<<grid, 512>>>(out, cyc, seed); });
+    printf("one mfma wave + one fma wave per SIMD, core cycles: together mfma %.0f, fma %.0f; "
+           "alone mfma %.0f, fma %.0f\n", fb.first, fb.second, fm.first, fv.second);
   }
   {
     const int grid = cus * 2 * 8;
     const float ms = time_ms([&] { lds_rate<<<grid, 256>>>(out, seed); }, 5);
-    const double bytes = (double)grid * 256 * kIters * 8 * 16;
+    const double bytes = (double)grid * 256 * 2 * kIters * 8 * 16;
     printf("LDS ds_read_b128: %.1f TB/s = %.1f B/clk/CU at 2.4 GHz\n", bytes / ms / 1e9,
            bytes / (ms * 1e-3) / 2.4e9 / cus);
   }
@@ -371,6 +416,7 @@ int main() {
     CHECK(hipFree(a));
     CHECK(hipFree(b));
   }
+  CHECK(hipFree(cyc));
   CHECK(hipFree(out));
   return 0;
 }
