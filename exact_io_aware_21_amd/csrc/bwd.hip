@@ -206,7 +206,11 @@ __device__ __forceinline__ void block_place(int kind, int N, int d, int &pos, in
 // Each query step's Q and dO rows (32 pi-permuted rows of pitch RP each) and its L and D are
 // copied straight into LDS (buffer-to-LDS loads) one step ahead, double-buffered; the
 // transposed operands Q^T and dO^T of the dK and dV products are read from the same row tiles
-// with ds_read_b64_tr_b16.
+// with ds_read_b64_tr_b16.  For d = 128 every wave stages the step's tiles into LDS buffers of
+// its own (four copies of each tile, 148 KB): the waves then never wait for one another.  They
+// run one per SIMD, and a workgroup barrier at the end of every step (shared buffers) made each
+// step wait for the slowest of the four.  For d = 64 the workgroup shares one copy (21 KB) and
+// two workgroups fit a CU (two waves per SIMD), whose interleaving hides that wait.
 template <int D, bool ALIBI, bool SOFTCAP, bool OUTF32>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NT = 256, NW = 4, QS = 32, KPW = 32;
@@ -214,10 +218,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int RP = pitch(D);                    // LDS pitch of a Q / dO row
   constexpr int RSLOT = QS * (RP / 8);            // 16-byte slots of a row tile
   constexpr int NJR = (RSLOT + 63) / 64;          // wave instructions per row tile
-  constexpr int NRR = (NJR + NW - 1) / NW;        // per wave (at most)
   constexpr int TILE = NJR * 64 * 8;              // elements per row tile (with the spill-over)
   constexpr int STAGE = 2 * TILE + 2 * 64 * 2;    // Q, dO, then L and D (64 floats each)
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  constexpr bool PRIV = D > 64;                   // stages of its own for every wave
+  constexpr int NRR = PRIV ? NJR : (NJR + NW - 1) / NW;  // copy instructions per wave and tile
+  __shared__ __attribute__((aligned(16))) uint16_t lds[(PRIV ? NW : 1) * 2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS copy targets
@@ -261,22 +266,26 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dkt[i] = dvt[i] = f32x16{};
 
-  // Zero both stages once, so that no LDS byte is ever read unwritten.
-  for (int i = tid; i < 2 * STAGE / 8; i += NT) *(u32x4 *)&lds[i * 8] = u32x4{0u, 0u, 0u, 0u};
+  // Zero every stage once, so that no LDS byte is ever read unwritten.
+  for (int i = tid; i < (int)(sizeof(lds) / 16); i += NT) *(u32x4 *)&lds[i * 8] = u32x4{0u, 0u, 0u, 0u};
+  uint16_t *const stages = PRIV ? &lds[wave * 2 * STAGE] : lds;  // the two stages this wave reads
+  const int cw = PRIV ? 0 : wave;  // copy instruction r of a tile: r * (PRIV ? 1 : NW) + cw
   int voff[NRR];
 #pragma unroll
-  for (int r = 0; r < NRR; ++r) voff[r] = tile_slot_offset<D, RP, QS>(64 * (r * NW + wave) + lane);
+  for (int r = 0; r < NRR; ++r)
+    voff[r] = tile_slot_offset<D, RP, QS>(64 * (r * (PRIV ? 1 : NW) + cw) + lane);
   auto fill = [&](int qs, int stage) {
     const int q0 = qs * QS;
     const int rows_left = N - q0;  // >= 1
-    uint16_t *dst = &lds[stage * STAGE];
-    copy_tiles_to_lds<NRR, NJR, NW>(a.q + hbase + (size_t)q0 * D, a.dout + hbase + (size_t)q0 * D,
-                                    rows_left * D * 2, dst, wave, voff);
+    uint16_t *dst = &stages[stage * STAGE];
+    copy_tiles_to_lds<NRR, NJR, PRIV ? 1 : NW>(a.q + hbase + (size_t)q0 * D,
+                                               a.dout + hbase + (size_t)q0 * D, rows_left * D * 2,
+                                               dst, cw, voff);
     // L and D of the 32 queries: one 4-byte-per-lane copy each (lanes 32..63 land in the unused
     // upper half of the 64-float slot).
-    if (wave == 0)
-      copy_rows4_to_lds(a.lse + (size_t)bh * N + q0, a.dvec + (size_t)bh * N + q0,
-                        rows_left * 4, &dst[2 * TILE], lane * 4);
+    if (PRIV || wave == 0)
+      copy_rows4_to_lds(a.lse + (size_t)bh * N + q0, a.dvec + (size_t)bh * N + q0, rows_left * 4,
+                        &dst[2 * TILE], lane * 4);
   };
   int tro[2];
   tr_base<RP>(lane, tro);
@@ -285,11 +294,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   __syncthreads();
   if (qs_begin < qs_end) fill(qs_begin, 0);
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  if constexpr (!PRIV) __syncthreads();
 
   for (int qs = qs_begin; qs < qs_end; ++qs) {
     const int q0 = qs * QS, stage = (qs - qs_begin) & 1;
-    const uint16_t *sQ = &lds[stage * STAGE];
+    const uint16_t *sQ = &stages[stage * STAGE];
     const uint16_t *sDO = sQ + TILE;
     const float *sL = (const float *)(sQ + 2 * TILE);
     const float *sDv = sL + 64;
@@ -381,10 +390,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       else
         dvt[d0] = mfma32(__builtin_bit_cast(bf16x8, fb[i]), pb[kk], dvt[d0]);
     }
-    // This wave's copies of step qs + 1 have landed; after the barrier every wave's have, and
-    // every wave is done reading this stage (the next step's copies overwrite it).
+    // This wave's copies of step qs + 1 have landed, and its reads of this stage (which the
+    // copies of step qs + 2 overwrite) have returned; with shared stages, after the barrier
+    // every wave's have.
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if constexpr (!PRIV) __syncthreads();
   }
 
   if (j_ok) {
