@@ -305,8 +305,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     // The step's 32 MFMAs each take one A fragment (16 bytes a lane) from LDS.  The transposed
     // ones of dV^T += dO^T P and dK^T += Q^T dS (16-query half kk, d block d0; dK when odd) are
     // all read first, before the copies of the next step are issued: a transposing read issued
-    // after those copies would be made to wait for them.  The score products S = Q K^T and
-    // dP = dO V^T (k-step i/2, dP when i is odd) read theirs kDepth MFMAs ahead.
+    // after those copies would be made to wait for them.  The score products S = Q K^T (k-step
+    // i, i < NKS) and dP = dO V^T (k-step i - NKS) read theirs kDepth MFMAs ahead.
+    // One wave runs per SIMD, so the step is ordered for the wave to overlap its own vector
+    // work with its own MFMAs: all of S first, then the dP products while the probabilities
+    // (which need only S) are formed; then the dV products (which need only P) while dS is
+    // formed, then the dK products.  sched_group_barrier pins that interleave.
     constexpr int kDepth = 4;
     constexpr int NA = 2 * NKS, NB = 4 * NDB;
     u32x4 fb[NB];
@@ -318,11 +322,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const uint16_t *qa = &sQ[l32 * RP + hf * 8];
     const uint16_t *da = &sDO[l32 * RP + hf * 8];
     auto frag = [&](int i) -> u32x4 {
-      return *(const u32x4 *)(((i & 1) ? da : qa) + (i >> 1) * 16);
+      return *(const u32x4 *)(i < NKS ? qa + i * 16 : da + (i - NKS) * 16);
     };
     u32x4 win[kDepth];
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) win[i] = frag(i);
+    f32x4 l2v[4], dv4[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      const int base = 16 * (aa >> 1) + 8 * hf + 4 * (aa & 1);
+      l2v[aa] = *(const f32x4 *)&sL[base];
+      dv4[aa] = *(const f32x4 *)&sDv[base];
+    }
     if (qs + 1 < qs_end) fill(qs + 1, stage ^ 1);  // in flight during this step's compute
     // S and dP: accumulator register r (row 8(r/4) + 4 hf + r%4 of the pi-permuted tile) is
     // query q0 + 16(r/8) + 8 hf + r%8, column = key j.
@@ -331,22 +342,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     for (int i = 0; i < NA; ++i) {
       const u32x4 cur = win[i % kDepth];
       if (i + kDepth < NA) win[i % kDepth] = frag(i + kDepth);
-      if (i & 1)
-        dp = mfma32(__builtin_bit_cast(bf16x8, cur), vf[i >> 1], dp);
+      if (i < NKS)
+        s = mfma32(__builtin_bit_cast(bf16x8, cur), kf[i], s);
       else
-        s = mfma32(__builtin_bit_cast(bf16x8, cur), kf[i >> 1], s);
-    }
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + kDepth < NA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    f32x4 l2v[4], dv4[4];
-#pragma unroll
-    for (int aa = 0; aa < 4; ++aa) {
-      const int base = 16 * (aa >> 1) + 8 * hf + 4 * (aa & 1);
-      l2v[aa] = *(const f32x4 *)&sL[base];
-      dv4[aa] = *(const f32x4 *)&sDv[base];
+        dp = mfma32(__builtin_bit_cast(bf16x8, cur), vf[i - NKS], dp);
     }
     float p[16], ds[16], dc[16];
 #pragma unroll
@@ -356,6 +355,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const float dji = (float)(j - q0 - 8 * hf) - (float)(16 * (aa >> 1) + 4 * (aa & 1) + bb);
       const float t = score2f<ALIBI, SOFTCAP>(a, s[r], slopeL, dji, dc[r]);
       p[r] = __builtin_amdgcn_exp2f(fmaf(-kLog2e, l2v[aa][bb], t));  // L is natural-log
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i + kDepth < NA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      if (i >= NKS) __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // vector ALU
     }
     // Element mask only when some key of this wave does not take all 32 queries of the step.
     if (__builtin_amdgcn_ballot_w64(!(qlo <= q0 && qhi >= q0 + QS - 1))) {
@@ -367,29 +372,42 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         if (i < qlo || i > qhi) p[r] = 0.f;
       }
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ds[r] = p[r] * (dp[r] - dv4[r >> 2][r & 3]) * dc[r];
     bf16x8 pb[2], db[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      f32x8 x, y;
+      f32x8 x;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = p[8 * kk + e];
-        y[e] = ds[8 * kk + e];
-      }
+      for (int e = 0; e < 8; ++e) x[e] = p[8 * kk + e];
       pb[kk] = __builtin_convertvector(x, bf16x8);
+    }
+    // dV^T += dO^T P over the 32 queries (two 16-row halves), while dS is formed.
+#pragma unroll
+    for (int i = 0; i < NB; i += 2) {
+      const int kk = i / (2 * NDB), d0 = (i >> 1) % NDB;
+      dvt[d0] = mfma32(__builtin_bit_cast(bf16x8, fb[i]), pb[kk], dvt[d0]);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = p[r] * (dp[r] - dv4[r >> 2][r & 3]) * dc[r];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      f32x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = ds[8 * kk + e];
       db[kk] = __builtin_convertvector(y, bf16x8);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries (two 16-row halves).
+    // dK^T += Q^T dS.
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
+    for (int i = 1; i < NB; i += 2) {
       const int kk = i / (2 * NDB), d0 = (i >> 1) % NDB;
-      if (i & 1)
-        dkt[d0] = mfma32(__builtin_bit_cast(bf16x8, fb[i]), db[kk], dkt[d0]);
-      else
-        dvt[d0] = mfma32(__builtin_bit_cast(bf16x8, fb[i]), pb[kk], dvt[d0]);
+      dkt[d0] = mfma32(__builtin_bit_cast(bf16x8, fb[i]), db[kk], dkt[d0]);
     }
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // the P conversions
+#pragma unroll
+    for (int i = 0; i < NB / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NB / 2, 0);
     // This wave's copies of step qs + 1 have landed, and its reads of this stage (which the
     // copies of step qs + 2 overwrite) have returned; with shared stages, after the barrier
     // every wave's have.
