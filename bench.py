@@ -296,6 +296,8 @@ def mod_source(w):
     if mask:
         src += "__device__ bool attn_mask_mod(int b, int i, int j, const float *p) { " + mask + " }\n"
         flags |= 2
+    if w.softcap:
+        flags |= 4  # ATTN_MODF_MAX_FIRST: a soft-cap moves row maxima often
     if not flags:
         raise SystemExit("--mod: the workload has no score modification or mask")
     params = inputs.alibi_slopes(w.H) if w.alibi else np.zeros(1, dtype=np.float32)

@@ -32,6 +32,7 @@ ATTN_ERR_WORKSPACE = -4
 ATTN_ERR_COMPILE = -5
 ATTN_MODF_SCORE = 1
 ATTN_MODF_MASK = 2
+ATTN_MODF_MAX_FIRST = 4
 
 MASK_BITS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
              "window": ATTN_MASK_SLIDING_WINDOW, "document": ATTN_MASK_DOCUMENT}

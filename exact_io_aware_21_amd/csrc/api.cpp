@@ -773,8 +773,11 @@ int mod_create(const char *source, uint32_t flags, int d, attn_mod **out, char *
   if (!out) return fail(ATTN_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   if (!source) return fail(ATTN_ERR_INVALID_ARG, "source is NULL");
-  if (flags == 0 || (flags & ~(uint32_t)(ATTN_MODF_SCORE | ATTN_MODF_MASK)))
-    return fail(ATTN_ERR_INVALID_ARG, "flags must be a non-empty set of ATTN_MODF_SCORE, ATTN_MODF_MASK");
+  if (!(flags & (ATTN_MODF_SCORE | ATTN_MODF_MASK)) ||
+      (flags & ~(uint32_t)(ATTN_MODF_SCORE | ATTN_MODF_MASK | ATTN_MODF_MAX_FIRST)))
+    return fail(ATTN_ERR_INVALID_ARG,
+                "flags must hold ATTN_MODF_SCORE and/or ATTN_MODF_MASK (optionally with "
+                "ATTN_MODF_MAX_FIRST) and nothing else");
   if (d != 64 && d != 128 && d != 256)
     return fail(ATTN_ERR_INVALID_ARG, "d must be 64, 128 or 256");
   std::string prog = "#include \"fwd_kernel.h\"\n#line 1 \"attn_mod_source\"\n";

@@ -90,8 +90,9 @@ __device__ __forceinline__ void ring_barrier() {
     __builtin_amdgcn_s_barrier();
 }
 
-constexpr int kModScore = 1;  // MOD bit: attn_score_mod replaces the scaled score
-constexpr int kModMask = 2;   // MOD bit: attn_mask_mod decides the element mask
+constexpr int kModScore = 1;     // MOD bit: attn_score_mod replaces the scaled score
+constexpr int kModMask = 2;      // MOD bit: attn_mask_mod decides the element mask
+constexpr int kModMaxFirst = 4;  // MOD bit: the score modification moves row maxima often
 
 // The forward kernel body.  One workgroup = 8 wave64s over Br = 256 query rows (32 rows per wave).
 // Waves w and w + 4 run on the same SIMD; they form two groups (w < 4 and w >= 4) that work one
@@ -267,9 +268,12 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
   // -slope (i - j) grows towards larger keys, by slope * 64 per tile, so in ascending order the
   // running maximum of a steep head moves on nearly every tile (each move rescales O); the
   // first tile of the descending walk holds the largest biases, and the maximum then rarely
-  // moves.  The order of the tiles does not change the sums (the online softmax is a merge of
-  // per-tile partial results), only their rounding order.
-  constexpr bool REV = ALIBI && MOD == 0;
+  // moves.  Instances with a user score modification walk the same way (unless created with
+  // the max-first flag): the position biases such functions usually add (ALiBi,
+  // relative-position terms) favour the nearest keys too.  The order of the tiles does not
+  // change the sums (the online softmax is a merge of per-tile partial results), only their
+  // rounding order.
+  constexpr bool REV = (ALIBI && MOD == 0) || ((MOD & kModScore) != 0 && (MOD & kModMaxFirst) == 0);
   auto kt_of = [&](int t) -> int {
     if constexpr (REV) t = T - 1 - t;
     if (!lst) return t;
@@ -530,9 +534,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
     // descending key order skip the tile maximum in the common case: a lane's sum of its 32
     // probabilities bounds each of them, so while every sum is <= 2^8 the running m stands.
     // Otherwise, or for a row with no maximum yet that sees a finite score, the tile maximum is
-    // taken, m moves and the output is rescaled, and the probabilities are formed again.  The
-    // soft-cap and user modifications move the maximum often, so those instances take the tile
-    // maximum first, every tile.
+    // taken, m moves and the output is rescaled, and the probabilities are formed again.  User
+    // modifications (natural-units scores, POS) take the same path, walked in descending key
+    // order when they modify scores.  The built-in soft-cap moves the maximum often, so those
+    // instances take the tile maximum first, every tile, and so do modifications created with
+    // the max-first flag.
     auto probs = [&](float m_use) -> float {
       float psum[4];
 #pragma unroll
@@ -576,9 +582,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
       m_run = m_new;
     };
-    // Without a modification (and for ALiBi, walked in descending key order) the maximum moves
-    // rarely, and the probabilities are formed against the running maximum first (see below).
-    if constexpr (!((POS || (ALIBI && !SOFTCAP)) && MOD == 0)) {
+    // Without the built-in soft-cap the maximum moves rarely (ALiBi and score modifications
+    // walked in descending key order), and the probabilities are formed against the running
+    // maximum first (see below).
+    if constexpr (!(POS || (ALIBI && !SOFTCAP)) || (MOD & kModMaxFirst) != 0) {
       const float mx = pair_max(lane_max());
       const float m_tile = POS ? mx * c : mx;
       if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kTau)) {
@@ -588,13 +595,12 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
       l_run += probs(m_run == -INFINITY ? 0.f : m_run);
       return;
     }
-    float lsum = probs(REL ? 0.f : m_run == -INFINITY ? 0.f : m_run);
-    bool need = !(lsum <= kPmax);
-    if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
-      keep_branch();
-      need = need || (m_run == -INFINITY && lane_max() > -INFINITY);
-    }
-    if (__builtin_amdgcn_ballot_w64(need)) {
+    // A wave with a row that has no maximum yet (the first tiles of its rows) takes the tile
+    // maximum first: probabilities formed against no maximum would only be formed again.
+    const bool fresh = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+    float lsum = 0.f;
+    if (!fresh) lsum = probs(REL ? 0.f : m_run);
+    if (fresh || __builtin_amdgcn_ballot_w64(!(lsum <= kPmax))) {
       keep_branch();
       // Tile row maximum: in-lane over 32 keys, then with the lane that shares the query.
       const float mx = pair_max(lane_max());

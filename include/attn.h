@@ -306,11 +306,21 @@ const char *attn_last_error(void);
  * The source defines the ones named by `flags` and may hold other device code.
  */
 typedef struct attn_mod_s attn_mod;
-enum { ATTN_MODF_SCORE = 1, ATTN_MODF_MASK = 2 };
+enum { ATTN_MODF_SCORE = 1, ATTN_MODF_MASK = 2, ATTN_MODF_MAX_FIRST = 4 };
+/*
+ * ATTN_MODF_MAX_FIRST is a performance hint, not a change of the result: by default a kernel
+ * with a score modification walks each query tile's key tiles from the last to the first and
+ * forms the probabilities against the running row maximum, taking a tile's maximum only when
+ * a probability sum shows that the maximum moved (cheap when the modification adds a bias that
+ * favours near keys, as ALiBi does).  With the flag it walks them in ascending order and takes
+ * every tile's maximum first, which is cheaper when the modification moves the maximum often
+ * (a soft-cap, say).  Both orders give the same attention up to the rounding order.
+ */
 
 /*
- * attn_mod_create -- compiles `source` (NUL-terminated) for head dimension d (64 or 128) and
- * the functions named by flags (ATTN_MODF_SCORE and/or ATTN_MODF_MASK) into a gfx950 code
+ * attn_mod_create -- compiles `source` (NUL-terminated) for head dimension d (64, 128 or 256)
+ * and the functions named by flags (ATTN_MODF_SCORE and/or ATTN_MODF_MASK, optionally with
+ * ATTN_MODF_MAX_FIRST) into a gfx950 code
  * object held by *out (host memory; each device loads it on first use).  Needs no GPU.
  * log (optional, log_size bytes) receives the compiler's messages, NUL-terminated.
  * Returns ATTN_OK, ATTN_ERR_INVALID_ARG or ATTN_ERR_COMPILE (*out = NULL).

@@ -371,10 +371,15 @@ def test_mod_compiles_without_gpu_and_sizes_its_workspace(alibi_causal_mod):
     score_only = attn.AttnMod(MOD_SRC.split("__device__ bool")[0], attn.ATTN_MODF_SCORE, 64)
     assert score_only.workspace_size(B, H, N) == al(B * H * 64 * n_kt * 64 * 2)
     score_only.close()
+    # the max-first hint compiles the same functions, with the same workspace
+    hinted = attn.AttnMod(MOD_SRC, attn.ATTN_MODF_SCORE | attn.ATTN_MODF_MASK |
+                          attn.ATTN_MODF_MAX_FIRST, 128)
+    assert hinted.workspace_size(B, H, N) == m.workspace_size(B, H, N)
+    hinted.close()
 
 
 @pytest.mark.parametrize("src,flags,d", [
-    (MOD_SRC, 0, 128), (MOD_SRC, 4, 128), (MOD_SRC, 3, 96), (None, 3, 128)])
+    (MOD_SRC, 0, 128), (MOD_SRC, 4, 128), (MOD_SRC, 8 | 3, 128), (MOD_SRC, 3, 96), (None, 3, 128)])
 def test_mod_create_rejects_invalid_arguments(src, flags, d):
     h = ctypes.c_void_p()
     rc = attn.lib().attn_mod_create(None if src is None else src.encode(), flags, d,

@@ -22,6 +22,7 @@ BR, BC = 256, 64
 
 SCORE = attn.ATTN_MODF_SCORE
 MASK = attn.ATTN_MODF_MASK
+MAX_FIRST = attn.ATTN_MODF_MAX_FIRST  # ascending key walk, tile maximum first (a hint only)
 
 # name: (flags, HIP source, numpy score_mod, numpy mask_mod, params(H) -> np.float32 array)
 MODS = {
@@ -40,6 +41,21 @@ MODS = {
         lambda s, b, h, i, j, p: p[h] * np.tanh(s / p[h]),
         None,
         lambda H: np.array([2.0 + 3.0 * h for h in range(H)], dtype=np.float32)),
+    "softcap_per_head_max_first": (
+        SCORE | MAX_FIRST,
+        """__device__ float attn_score_mod(float s, int b, int h, int i, int j, const float *p) {
+             return p[h] * tanhf(s / p[h]); }""",
+        lambda s, b, h, i, j, p: p[h] * np.tanh(s / p[h]),
+        None,
+        lambda H: np.array([2.0 + 3.0 * h for h in range(H)], dtype=np.float32)),
+    "alibi_causal_max_first": (
+        SCORE | MASK | MAX_FIRST,
+        """__device__ float attn_score_mod(float s, int b, int h, int i, int j, const float *p) {
+             return s - p[h] * (float)(i - j); }
+           __device__ bool attn_mask_mod(int b, int i, int j, const float *p) { return j <= i; }""",
+        lambda s, b, h, i, j, p: s - p[h] * (i - j),
+        lambda b, i, j, p: j <= i,
+        lambda H: inputs.alibi_slopes(H)),
     "prefix_lm": (
         MASK,
         """__device__ bool attn_mask_mod(int b, int i, int j, const float *p) {
@@ -175,6 +191,8 @@ CASES = [
     ("alibi_causal", 1, 4, 1000, 128, 1.0),
     ("alibi_causal", 2, 2, 333, 64, 1.0),
     ("softcap_per_head", 1, 3, 700, 128, 3.0),
+    ("softcap_per_head_max_first", 1, 3, 700, 128, 3.0),
+    ("alibi_causal_max_first", 1, 4, 1000, 128, 1.0),
     ("prefix_lm", 2, 2, 900, 128, 1.0),
     ("prefix_lm", 1, 2, 1, 64, 1.0),
     ("relbias_window", 1, 2, 1300, 128, 1.0),
