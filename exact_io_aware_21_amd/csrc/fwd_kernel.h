@@ -19,26 +19,28 @@
 //    score registers of a lane hold keys {16*(r/8) + 8*(lane/32) + r%8}, i.e. two runs of 8
 //    consecutive keys, which is exactly the B-operand layout of the P V product: P^T feeds
 //    O^T = V^T P^T straight from registers, with no LDS round trip.
-//  * V^T (d rows, keys contiguous) is the A operand of that product.  A small pack kernel
-//    writes V^T into the workspace once per call, with the d rows of each 32-block permuted so
-//    that each lane's 16 accumulator registers hold 16 consecutive output columns.
+//  * V^T (d rows, keys contiguous) is the A operand of that product.  The call's preparation
+//    launch (prep_kernel, which also builds the block table) writes V^T into the workspace,
+//    with the d rows of each 32-block permuted so that each lane's 16 accumulator registers
+//    hold 16 consecutive output columns.
 //  * The P V product runs on fp16 operands (v_mfma_f32_32x32x16_f16, the same rate as bf16):
 //    bf16 V converts to fp16 exactly inside the pack kernel, and P <= 2^8 (see below) keeps
 //    11 significant bits instead of bf16's 8.  With bf16 P the rounding of a dominant
 //    probability alone moves O by up to 2^-9 |v|, which exceeds 1e-2 for |v| near 8.
 //    Q K^T stays on bf16 operands, which are the exact input values.
-//  * K and V^T tiles are double-buffered in LDS.  Each wave stages its share of the next tiles
-//    between the MFMAs of its own matrix-core phase, fetched one iteration ahead with buffer
-//    loads into registers and stored to the idle buffers: spread out, not a burst of every
-//    wave's loads and stores at a barrier.  Each LDS row is padded by 16 bytes, so the 8 (or 16)
-//    lanes of one ds_read_b128 phase, which read the same column of 8 (16) consecutive rows, hit
-//    distinct banks, while every operand address stays lane base + compile-time offset.
+//  * K and V^T tiles go through a ring of four LDS buffers (three for d = 256), filled by
+//    buffer-to-LDS copies (buffer_load ... lds: no staging registers, no ds_write) that each
+//    wave issues, for the tile pair three (d = 256: two) iterations ahead, between the MFMAs
+//    of its own matrix-core phase: spread out, not a burst of every wave's loads at a barrier.
+//    Each LDS row is padded by 16 bytes, so the 8 (or 16) lanes of one ds_read_b128 phase,
+//    which read the same column of 8 (16) consecutive rows, hit distinct banks, while every
+//    operand address stays lane base + compile-time offset.
 //  * Scores are kept in base-2 units (scale * log2 e folded in), so each probability costs one
 //    v_exp_f32; L is converted back to natural log in the epilogue.
 //  * The running maximum is only moved when a tile's scores exceed it by more than 8 (base 2):
 //    the output and l are then rescaled, otherwise probabilities are formed against the older
-//    maximum and stay below 2^8.  Both are exact rewritings of the same sums.  Without score
-//    modifications the test is made on the probabilities' sum, so the common tile skips its
+//    maximum and stay below 2^8.  Both are exact rewritings of the same sums.  Except under the
+//    built-in soft-cap the test is made on the probabilities' sum, so the common tile skips its
 //    row maximum altogether.
 //  * Fully masked tiles never reach the kernel: it walks the per-q-tile list of non-empty tiles
 //    from the block table, and evaluates the element mask only on partial tiles.
