@@ -21,7 +21,8 @@
 //    lane % 32 is a key; in bwd_dq_kernel S^T = K Q^T, so lane % 32 is a query.
 //  * The rows of the LDS tiles are stored with index bits 2 and 3 swapped (pi_key), which makes
 //    the 16 accumulator registers of a lane two runs of 8 consecutive rows: P and dS then feed the
-//    next product as its B operand straight from registers.
+//    next product as its B operand straight from registers.  Within each block of 16, the tile
+//    rows are placed in LDS by lds_row, which keeps the transposing reads free of bank conflicts.
 //  * The other operand of those products (Q^T, dO^T for dK, dV; K^T for dQ) is read from the
 //    same row tiles with the transposing LDS read ds_read_b64_tr_b16, with its columns in the
 //    sigma_d order, so each lane's accumulator registers are 16 consecutive output columns and
@@ -149,14 +150,27 @@ __device__ __forceinline__ void copy_rows4_to_lds(const float *x, const float *y
   __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void *)&dst[128], 4, voff, 0, 0, 0);
 }
 
+// Where tile row rho sits in LDS: bits 0-1 and bits 2-3 of the row index swapped (an involution
+// that keeps every aligned block of 16 rows in place).  A transposing read of 32 lanes covers
+// the same 64-byte column span of four rows whose indices differ in bits 0-1; with a pitch of
+// 272 bytes (d = 128) or 144 bytes (d = 64), rows 4 apart start 16 banks apart modulo the 64
+// banks, so stored 4 apart the four spans take all 64 banks once (stored adjacent they overlapped
+// 4-fold at d = 128, 2-fold at d = 64).  The 16 rows a ds_read_b128 phase reads stay the 16 rows
+// of one block, which start at 16 distinct 4-bank groups, as before.
+__device__ __forceinline__ int lds_row(int rho) {
+  return (rho & ~15) | ((rho & 3) << 2) | ((rho >> 2) & 3);
+}
+
 // Per-lane byte offset of 16-byte slot `slot` of a tile of pi-permuted rows (pitch P elements,
-// P / 8 slots a row) of a row-major [rows][D] bf16 source: LDS row rho holds source row
-// pi_key(rho); a pad slot repeats the row's last chunk; slots past the tile read row 0.
+// P / 8 slots a row) of a row-major [rows][D] bf16 source: tile row rho, stored at LDS row
+// lds_row(rho), holds source row pi_key(rho); a pad slot repeats the row's last chunk; slots
+// past the tile read row 0.
 template <int D, int P, int ROWS>
 __device__ __forceinline__ int tile_slot_offset(int slot) {
   constexpr int SPR = P / 8;
+  static_assert(ROWS % 16 == 0, "lds_row permutes whole blocks of 16 rows");
   if (slot >= ROWS * SPR) return 0;
-  const int row = slot / SPR, ch = slot % SPR;
+  const int row = lds_row(slot / SPR), ch = slot % SPR;
   return (pi_key(row) * D + (ch < D / 8 ? ch : D / 8 - 1) * 8) * 2;
 }
 
@@ -170,13 +184,14 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 // permutation).  ds_read_b64_tr_b16 hands lane 16 g + 4 q + e, for m = 0..3, element e of the
 // 8 bytes addressed by lane 16 g + q + 4 m, so the addressing lane s = 16 g + q + 4 m points at
 // row 16 kg + 8 (g / 2) + m (+ 4 for t = 4..7) and column 32 d0 + 16 (q & 1) + 8 (g & 1) +
-// 4 (q >> 1).  tr_base() is the lane's part; kg and d0 add the immediate 16 kg P + 32 d0.
+// 4 (q >> 1).  tr_base() is the lane's part; kg and d0 add the immediate 16 kg P + 32 d0
+// (lds_row moves rows only within their block of 16).
 template <int P>
 __device__ __forceinline__ void tr_base(int lane, int off[2]) {
   const int q = lane & 3, m = (lane >> 2) & 3, g = lane >> 4;
   const int col = 16 * (q & 1) + 8 * (g & 1) + 4 * (q >> 1);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) off[u] = pi_key(8 * (g >> 1) + m + 4 * u) * P + col;
+  for (int u = 0; u < 2; ++u) off[u] = lds_row(pi_key(8 * (g >> 1) + m + 4 * u)) * P + col;
 }
 
 __device__ __forceinline__ u32x4 tr_frag(const uint16_t *tile, const int off[2], int imm) {
@@ -319,8 +334,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const int kk = i / (2 * NDB), d0 = (i >> 1) % NDB;
       fb[i] = tr_frag((i & 1) ? sQ : sDO, tro, 16 * kk * RP + 32 * d0);
     }
-    const uint16_t *qa = &sQ[l32 * RP + hf * 8];
-    const uint16_t *da = &sDO[l32 * RP + hf * 8];
+    const uint16_t *qa = &sQ[lds_row(l32) * RP + hf * 8];
+    const uint16_t *da = &sDO[lds_row(l32) * RP + hf * 8];
     auto frag = [&](int i) -> u32x4 {
       return *(const u32x4 *)(i < NKS ? qa + i * 16 : da + (i - NKS) * 16);
     };
@@ -432,7 +447,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 // The K and V tiles are double-buffered in LDS and filled by buffer-to-LDS loads
 // (buffer_load_dwordx4 ... lds): no VGPR staging, and the loads of tile t + 1 are in flight
 // while tile t is computed.  One LDS stage holds the K tile then the V tile, each 64
-// pi-permuted key rows of pitch KP, as 16-byte slots; a wave instruction fills 64 consecutive
+// pi-permuted key rows of pitch KP placed by lds_row, as 16-byte slots; a wave instruction fills 64 consecutive
 // slots, and a wave fills slot group j of both tiles (same offsets).  A pad slot repeats a real
 // chunk of its row; keys past N lie beyond the K and V resources and read as zero.
 // K^T, the A operand of dQ^T += K^T dS^T, is read from the same K tile with the transposing
@@ -512,7 +527,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int r = 0; r < NRK; ++r) {
     const int slot = 64 * (r * 8 + wave) + lane;
-    const int row = slot / KSPR, ch = slot % KSPR;
+    const int row = lds_row(slot / KSPR), ch = slot % KSPR;
     voff[r] = (pi_key(row) * D + (ch < D / 8 ? ch : D / 8 - 1) * 8) * 2;
   }
   auto fill = [&](int kt, int stage) {
@@ -533,7 +548,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     const int q = lane & 3, m = (lane >> 2) & 3, g = lane >> 4;
     const int col = 16 * (q & 1) + 8 * (g & 1) + 4 * (q >> 1);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) tr_off[u] = pi_key(8 * (g >> 1) + m + 4 * u) * KP + col;
+    for (int u = 0; u < 2; ++u) tr_off[u] = lds_row(pi_key(8 * (g >> 1) + m + 4 * u)) * KP + col;
   }
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -559,8 +574,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     f32x16 s[2] = {}, dp[2] = {};
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const uint16_t *ka = &sK[(32 * blk + l32) * KP + hf * 8];
-      const uint16_t *va = &sV[(32 * blk + l32) * KP + hf * 8];
+      const uint16_t *ka = &sK[(32 * blk + lds_row(l32)) * KP + hf * 8];
+      const uint16_t *va = &sV[(32 * blk + lds_row(l32)) * KP + hf * 8];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         s[blk] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4 *)(ka + ks * 16)), qf[ks], s[blk]);
