@@ -139,6 +139,37 @@ __device__ __forceinline__ void copy_tiles_to_lds(const void *x, const void *y, 
   }
 }
 
+// The same copies for a wave that fills whole tiles alone (NW = 1), with one LDS base (M0) per
+// group of 4 instructions instead of one per instruction: the immediate offset of a
+// buffer-to-LDS load is added to both the global and the LDS address, so instruction r takes
+// the group base plus (r % 4) KB as its immediate.  The resources start kGroupShift bytes before
+// x and y and the per-lane offsets are voffs[r] = voff + kGroupShift - (r % 4) KB (>= 0), so
+// every address, and the bound check, is what the plain copies compute.
+constexpr int kGroupShift = 3072;
+template <int NR, int NJ>
+__device__ __forceinline__ void copy_tiles_to_lds_grouped(const void *x, const void *y, int bytes,
+                                                          uint16_t *dst, const int *voffs) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  const auto rx = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)x - kGroupShift), 0,
+                                                    bytes + kGroupShift, kBufferWord3);
+  const auto ry = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)y - kGroupShift), 0,
+                                                    bytes + kGroupShift, kBufferWord3);
+#pragma unroll
+  for (int g = 0; g < (NR + 3) / 4; ++g) {
+    const int n = NR - 4 * g;  // instructions in this group (compile-time after unrolling)
+    lds_void *bx = (lds_void *)&dst[4 * g * 64 * 8], *by = (lds_void *)&dst[(NJ + 4 * g) * 64 * 8];
+    const int *v = &voffs[4 * g];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, bx, 16, v[0], 0, 0, 0);
+    if (n > 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, bx, 16, v[1], 0, 1024, 0);
+    if (n > 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, bx, 16, v[2], 0, 2048, 0);
+    if (n > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, bx, 16, v[3], 0, 3072, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, by, 16, v[0], 0, 0, 0);
+    if (n > 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, by, 16, v[1], 0, 1024, 0);
+    if (n > 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, by, 16, v[2], 0, 2048, 0);
+    if (n > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, by, 16, v[3], 0, 3072, 0);
+  }
+}
+
 // Buffer-to-LDS copy of two 4-byte-per-lane rows (bytes each, from x and y) into dst and
 // dst + 128 elements (64 floats each); loads past `bytes` read as zero.
 __device__ __forceinline__ void copy_rows4_to_lds(const float *x, const float *y, int bytes,
@@ -288,14 +319,20 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   int voff[NRR];
 #pragma unroll
   for (int r = 0; r < NRR; ++r)
-    voff[r] = tile_slot_offset<D, RP, QS>(64 * (r * (PRIV ? 1 : NW) + cw) + lane);
+    voff[r] = tile_slot_offset<D, RP, QS>(64 * (r * (PRIV ? 1 : NW) + cw) + lane) +
+              (PRIV ? kGroupShift - (r & 3) * 1024 : 0);
   auto fill = [&](int qs, int stage) {
     const int q0 = qs * QS;
-    const int rows_left = N - q0;  // >= 1
+    const int rows_left = max(N - q0, 0);  // 0 past the last step: the copies read nothing
     uint16_t *dst = &stages[stage * STAGE];
-    copy_tiles_to_lds<NRR, NJR, PRIV ? 1 : NW>(a.q + hbase + (size_t)q0 * D,
-                                               a.dout + hbase + (size_t)q0 * D, rows_left * D * 2,
-                                               dst, cw, voff);
+    if constexpr (PRIV)
+      copy_tiles_to_lds_grouped<NRR, NJR>(a.q + hbase + (size_t)q0 * D,
+                                          a.dout + hbase + (size_t)q0 * D, rows_left * D * 2, dst,
+                                          voff);
+    else
+      copy_tiles_to_lds<NRR, NJR, NW>(a.q + hbase + (size_t)q0 * D,
+                                      a.dout + hbase + (size_t)q0 * D, rows_left * D * 2, dst, cw,
+                                      voff);
     // L and D of the 32 queries: one 4-byte-per-lane copy each (lanes 32..63 land in the unused
     // upper half of the 64-float slot).
     if (PRIV || wave == 0)
@@ -304,63 +341,61 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   };
   int tro[2];
   tr_base<RP>(lane, tro);
-  // Settle the loads above and the zero fill before the first copy lands.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (qs_begin < qs_end) fill(qs_begin, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  if constexpr (!PRIV) __syncthreads();
-
-  for (int qs = qs_begin; qs < qs_end; ++qs) {
-    const int q0 = qs * QS, stage = (qs - qs_begin) & 1;
+  // A step's LDS operands: the A fragments of the score products S = Q K^T (k-step i, i < NKS)
+  // and dP = dO V^T (k-step i - NKS), the transposed A fragments of dV^T += dO^T P and
+  // dK^T += Q^T dS (16-query half kk, d block d0; dK when odd), and L and D.  They are read at
+  // the end of the step before, while its dK products run, so every MFMA of a step finds its
+  // operands in registers.
+  constexpr int NA = 2 * NKS, NB = 4 * NDB;
+  u32x4 fb[NB], fa[NA];
+  f32x4 l2v[4], dv4[4];
+  auto load_ops = [&](int stage) {
     const uint16_t *sQ = &stages[stage * STAGE];
     const uint16_t *sDO = sQ + TILE;
     const float *sL = (const float *)(sQ + 2 * TILE);
     const float *sDv = sL + 64;
-    // The step's 32 MFMAs each take one A fragment (16 bytes a lane) from LDS.  The transposed
-    // ones of dV^T += dO^T P and dK^T += Q^T dS (16-query half kk, d block d0; dK when odd) are
-    // all read first, before the copies of the next step are issued: a transposing read issued
-    // after those copies would be made to wait for them.  The score products S = Q K^T (k-step
-    // i, i < NKS) and dP = dO V^T (k-step i - NKS) read theirs kDepth MFMAs ahead.
-    // One wave runs per SIMD, so the step is ordered for the wave to overlap its own vector
-    // work with its own MFMAs: all of S first, then the dP products while the probabilities
-    // (which need only S) are formed; then the dV products (which need only P) while dS is
-    // formed, then the dK products.  sched_group_barrier pins that interleave.
-    constexpr int kDepth = 4;
-    constexpr int NA = 2 * NKS, NB = 4 * NDB;
-    u32x4 fb[NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      fa[i] = *(const u32x4 *)&(i < NKS ? sQ : sDO)[lds_row(l32) * RP + hf * 8 + (i % NKS) * 16];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int kk = i / (2 * NDB), d0 = (i >> 1) % NDB;
       fb[i] = tr_frag((i & 1) ? sQ : sDO, tro, 16 * kk * RP + 32 * d0);
     }
-    const uint16_t *qa = &sQ[lds_row(l32) * RP + hf * 8];
-    const uint16_t *da = &sDO[lds_row(l32) * RP + hf * 8];
-    auto frag = [&](int i) -> u32x4 {
-      return *(const u32x4 *)(i < NKS ? qa + i * 16 : da + (i - NKS) * 16);
-    };
-    u32x4 win[kDepth];
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) win[i] = frag(i);
-    f32x4 l2v[4], dv4[4];
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
       const int base = 16 * (aa >> 1) + 8 * hf + 4 * (aa & 1);
       l2v[aa] = *(const f32x4 *)&sL[base];
       dv4[aa] = *(const f32x4 *)&sDv[base];
     }
-    if (qs + 1 < qs_end) fill(qs + 1, stage ^ 1);  // in flight during this step's compute
+  };
+  // Settle the loads above and the zero fill before the first copy lands.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (qs_begin < qs_end) fill(qs_begin, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (!PRIV) __syncthreads();
+  load_ops(0);
+
+  for (int qs = qs_begin; qs < qs_end; ++qs) {
+    const int q0 = qs * QS, stage = (qs - qs_begin) & 1;
+    // One wave runs per SIMD, so the step is ordered for the wave to overlap its own vector
+    // work with its own MFMAs: all of S first (while the copies of the next step are issued),
+    // then the dP products while the probabilities (which need only S) are formed; then the dV
+    // products (which need only P) while dS is formed, then the dK products while the next
+    // step's operands are read.  sched_group_barrier pins that interleave.  The copies of the
+    // next step are issued between the score MFMAs (past the last step they read nothing and
+    // fill the unused stage with zeros).
+    fill(qs + 1, stage ^ 1);
     // S and dP: accumulator register r (row 8(r/4) + 4 hf + r%4 of the pi-permuted tile) is
     // query q0 + 16(r/8) + 8 hf + r%8, column = key j.
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const u32x4 cur = win[i % kDepth];
-      if (i + kDepth < NA) win[i % kDepth] = frag(i + kDepth);
       if (i < NKS)
-        s = mfma32(__builtin_bit_cast(bf16x8, cur), kf[i], s);
+        s = mfma32(__builtin_bit_cast(bf16x8, fa[i]), kf[i], s);
       else
-        dp = mfma32(__builtin_bit_cast(bf16x8, cur), vf[i - NKS], dp);
+        dp = mfma32(__builtin_bit_cast(bf16x8, fa[i]), vf[i - NKS], dp);
     }
     float p[16], ds[16], dc[16];
 #pragma unroll
@@ -374,7 +409,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      if (i + kDepth < NA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      if (i < NKS) __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);  // copy instructions
       if (i >= NKS) __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // vector ALU
     }
     // Element mask only when some key of this wave does not take all 32 queries of the step.
@@ -416,18 +451,24 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const int kk = i / (2 * NDB), d0 = (i >> 1) % NDB;
       dkt[d0] = mfma32(__builtin_bit_cast(bf16x8, fb[i]), db[kk], dkt[d0]);
     }
+    // The next step's operands: its copies (issued at the top of this step) have landed; with
+    // shared stages, after the barrier every wave's have, and every wave is done reading this
+    // stage (which the copies at the top of the next step overwrite).  After the last step the
+    // reads fetch unused data from the other stage.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if constexpr (!PRIV) __syncthreads();
+    load_ops(stage ^ 1);
     __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // the P conversions
 #pragma unroll
     for (int i = 0; i < NB / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NB / 2, 0);
-    // This wave's copies of step qs + 1 have landed, and its reads of this stage (which the
-    // copies of step qs + 2 overwrite) have returned; with shared stages, after the barrier
-    // every wave's have.
-    __builtin_amdgcn_s_waitcnt(0);
-    if constexpr (!PRIV) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NB / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, (NA + NB + 8) / (NB / 2) + 1, 0);
+    }
   }
 
   if (j_ok) {

@@ -208,6 +208,69 @@ __global__ __launch_bounds__(512) void pair_cycles(float *out, u64 *cyc, float s
   if (lane == 0) cyc[blockIdx.x * 8 + wave] = dt | ((u64)mat << 63);
 }
 
+// One wave per SIMD that interleaves its own MFMAs with independent vector work: each of the 4
+// MFMAs of an iteration (4 accumulator chains) is followed by NV independent v_fma_f32 (EXP:
+// v_exp_f32) on registers no MFMA touches.  If the wave overlaps the two, an iteration takes the
+// 4 MFMAs' 128 cycles until the vector instructions alone take longer.
+template <int NV, bool EXP>
+__global__ __launch_bounds__(256) void mixed_cycles(float *out, u64 *cyc, float seed) {
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(seed * (threadIdx.x + i));
+    b[i] = (__bf16)(seed * (i + 1));
+  }
+  f32x16 c[4] = {};
+  float y[4 * NV + 1];
+  for (int i = 0; i < 4 * NV + 1; ++i) y[i] = -seed * (threadIdx.x + 2 * i);
+  const u64 t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < kIters; ++it) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      c[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[m], 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        float &v = y[m * NV + k];
+        v = EXP ? __builtin_amdgcn_exp2f(v) : fmaf(v, 0.999f, 0.001f);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+    }
+  }
+  const u64 t1 = __builtin_amdgcn_s_memtime();
+  float s = 0.f;
+  for (int m = 0; m < 4; ++m)
+    for (int i = 0; i < 16; ++i) s += c[m][i];
+  for (int i = 0; i < 4 * NV + 1; ++i) s += y[i];
+  if (s == 1234.5f) out[threadIdx.x] = s;
+  if (threadIdx.x == 0) cyc[blockIdx.x] = (t1 - t0) / kIters;
+}
+
+// One wave per SIMD issuing 8 MFMAs per iteration into NC accumulator chains (NC = 1: every MFMA
+// takes the previous one's result as its accumulator).
+template <int NC>
+__global__ __launch_bounds__(256) void chain_cycles(float *out, u64 *cyc, float seed) {
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(seed * (threadIdx.x + i));
+    b[i] = (__bf16)(seed * (i + 1));
+  }
+  f32x16 c[NC] = {};
+  const u64 t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < kIters; ++it) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) c[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[m % NC], 0, 0, 0);
+  }
+  const u64 t1 = __builtin_amdgcn_s_memtime();
+  float s = 0.f;
+  for (int m = 0; m < NC; ++m)
+    for (int i = 0; i < 16; ++i) s += c[m][i];
+  if (s == 1234.5f) out[threadIdx.x] = s;
+  if (threadIdx.x == 0) cyc[blockIdx.x] = (t1 - t0) / kIters;
+}
+
 // ds_read_b128 from a 32 KB LDS array: each lane reads a 16-byte chunk of its own row (pitch
 // 272 bytes, the forward kernel's K layout), 8 reads per iteration at different offsets.
 __global__ __launch_bounds__(256) void lds_rate(float *out, float seed) {
@@ -380,6 +443,31 @@ int main() {
     const std::pair<double, double> fv = roles([&] { pair_cycles<2, 2><<<grid, 512>>>(out, cyc, seed); });
     printf("one mfma wave + one fma wave per SIMD, core cycles: together mfma %.0f, fma %.0f; "
            "alone mfma %.0f, fma %.0f\n", fb.first, fb.second, fm.first, fv.second);
+  }
+  // One wave per SIMD: a dependent MFMA chain against independent ones.
+  {
+    const int grid = cus;
+    auto per = [&](auto launch) { return median_cycles(launch, cyc, grid) / 8.0; };
+    printf("1 wave/SIMD, core cycles per MFMA with 1, 2, 4 accumulator chains: %.1f %.1f %.1f\n",
+           per([&] { chain_cycles<1><<<grid, 256>>>(out, cyc, seed); }),
+           per([&] { chain_cycles<2><<<grid, 256>>>(out, cyc, seed); }),
+           per([&] { chain_cycles<4><<<grid, 256>>>(out, cyc, seed); }));
+  }
+  // One wave per SIMD overlapping its own MFMAs with independent vector instructions.
+  {
+    const int grid = cus;
+    auto per = [&](auto launch) { return median_cycles(launch, cyc, grid) / 4.0; };
+    printf("1 wave/SIMD, core cycles per MFMA followed by n independent vector instructions:\n"
+           "  fma n=0..8: %.1f %.1f %.1f %.1f %.1f\n  exp n=1..4: %.1f %.1f %.1f %.1f\n",
+           per([&] { mixed_cycles<0, false><<<grid, 256>>>(out, cyc, seed); }),
+           per([&] { mixed_cycles<2, false><<<grid, 256>>>(out, cyc, seed); }),
+           per([&] { mixed_cycles<4, false><<<grid, 256>>>(out, cyc, seed); }),
+           per([&] { mixed_cycles<6, false><<<grid, 256>>>(out, cyc, seed); }),
+           per([&] { mixed_cycles<8, false><<<grid, 256>>>(out, cyc, seed); }),
+           per([&] { mixed_cycles<1, true><<<grid, 256>>>(out, cyc, seed); }),
+           per([&] { mixed_cycles<2, true><<<grid, 256>>>(out, cyc, seed); }),
+           per([&] { mixed_cycles<3, true><<<grid, 256>>>(out, cyc, seed); }),
+           per([&] { mixed_cycles<4, true><<<grid, 256>>>(out, cyc, seed); }));
   }
   {
     const int grid = cus * 2 * 8;
