@@ -240,14 +240,78 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   }
 }
 
+// The same merge for at most 64 splits, with one wave per (sequence, head, query row) and no
+// LDS: lane s holds split s's (m, l), the maximum and the normaliser are wave reductions, and
+// each lane sums its D / 64 columns over the splits with the weights broadcast from their lanes.
+// The partial outputs are loaded in chunks of 16 splits, each chunk's loads issued together; the
+// first chunk is loaded with (m, l), before the maximum is known.
+template <int D, int LQ, bool OUTF32>
+__global__ __launch_bounds__(64) void decode_merge_small_kernel(DecodeArgs a) {
+  constexpr int CPL = D / 64;  // columns per lane
+  constexpr int CH = 16;       // splits per chunk
+  const int bh = blockIdx.x, i = blockIdx.y, lane = threadIdx.x;
+  const int ns = a.nsplit;  // <= 64
+  const size_t pbase = (size_t)bh * ns;
+  const float *po = a.part_o + (pbase * LQ + i) * D + lane;
+  const size_t sstride = (size_t)LQ * D;  // between the partials of consecutive splits
+  float v[CH][CPL];
+  auto load_chunk = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) v[u][c] = s0 + u < ns ? po[(s0 + u) * sstride + 64 * c] : 0.f;
+  };
+  load_chunk(0);
+  float m = -INFINITY, l = 0.f;
+  if (lane < ns) {
+    m = a.part_m[(pbase + lane) * LQ + i];
+    l = a.part_l[(pbase + lane) * LQ + i];
+  }
+  float M = m;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  const float w = (lane < ns && M != -INFINITY) ? __builtin_amdgcn_exp2f(m - M) : 0.f;
+  float L = w * l;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
+  float acc[CPL][2] = {};
+  for (int s0 = 0; s0 < ns; s0 += CH) {
+    if (s0 > 0) load_chunk(s0);
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      // weight of split s0 + u (0 past ns: lanes >= ns hold w = 0)
+      const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(s0 + u, 63)));
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c][u & 1] = fmaf(ws, v[u][c], acc[c][u & 1]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const float val = L > 0.f ? (acc[c][0] + acc[c][1]) / L : 0.f;
+    const size_t oi = ((size_t)bh * a.Lq + i) * D + 64 * c + lane;
+    if constexpr (OUTF32)
+      ((float *)a.o)[oi] = val;
+    else
+      ((__bf16 *)a.o)[oi] = (__bf16)val;
+  }
+  if (lane == 0 && a.lse) a.lse[(size_t)bh * a.Lq + i] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
 template <int D, int LQ>
 hipError_t launch_decode_lq(const DecodeArgs &a, bool out_f32, hipStream_t s) {
   decode_split_kernel<D, LQ><<<dim3((unsigned)(a.B * a.H), (unsigned)a.nsplit), 256, 0, s>>>(a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  if (out_f32)
+  if (a.nsplit <= 64) {
+    const dim3 grid((unsigned)(a.B * a.H), (unsigned)a.Lq);
+    if (out_f32)
+      decode_merge_small_kernel<D, LQ, true><<<grid, 64, 0, s>>>(a);
+    else
+      decode_merge_small_kernel<D, LQ, false><<<grid, 64, 0, s>>>(a);
+  } else if (out_f32) {
     decode_merge_kernel<D, LQ, true><<<(unsigned)(a.B * a.H), 256, 0, s>>>(a);
-  else
+  } else {
     decode_merge_kernel<D, LQ, false><<<(unsigned)(a.B * a.H), 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
