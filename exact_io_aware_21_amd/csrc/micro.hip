@@ -3,7 +3,7 @@
 // kernels time themselves in core cycles (s_memtime inside the kernel, the median over the
 // workgroups) at a stated number of waves per SIMD: one 4-wave workgroup per CU places one wave
 // on each SIMD, so a grid of k workgroups per CU runs k waves per SIMD.  The bandwidth kernels
-// are timed with hipEvents.  Results feed the roofline figures used to judge the attention
+// are timed with hipEvents.  Results feed the roofline figures used to assess the attention
 // forward kernel: the MFMA rate and the core clock under it, the cost of transcendental and FMA
 // instructions alone and mixed, the forward kernel's per-score probability work, how matrix-core
 // and vector waves share a SIMD, LDS read bandwidth and HBM bandwidth.
