@@ -6,7 +6,8 @@
 // are timed with hipEvents.  Results feed the roofline figures used to assess the attention
 // forward kernel: the MFMA rate and the core clock under it, the cost of transcendental and FMA
 // instructions alone and mixed, the forward kernel's per-score probability work, how matrix-core
-// and vector waves share a SIMD, LDS read bandwidth and HBM bandwidth.
+// and vector waves share a SIMD, how far one wave overlaps its own MFMAs with vector work, the
+// rate of a dependent MFMA chain, LDS read bandwidth and HBM bandwidth.
 //
 //   make micro && ./micro_bench
 #include <hip/hip_runtime.h>
