@@ -47,6 +47,10 @@ int check_shape(int B, int H, int N, int d, uint32_t variant, Shape &s) {
   if (B < 1 || H < 1 || N < 1) return fail(ATTN_ERR_INVALID_ARG, "B, H and N must be >= 1");
   if (N > (1 << 24)) return fail(ATTN_ERR_INVALID_ARG, "N must be <= 2^24");
   if (d != 64 && d != 128 && d != 256) return fail(ATTN_ERR_INVALID_ARG, "d must be 64, 128 or 256");
+  // The kernels address a V^T tile with 32-bit per-lane offsets of up to (columns of O - 1) *
+  // Npad * 2 bytes: below 2^31 for 64 columns up to N = 2^24, for 128 up to N = 2^23.
+  if (d >= 128 && N > (1 << 23))
+    return fail(ATTN_ERR_INVALID_ARG, "N must be <= 2^23 for d 128 and 256");
   if (variant & ~kKnownBits) return fail(ATTN_ERR_INVALID_ARG, "unknown variant bits");
   s.kind = variant & 0xFu;
   if (s.kind > ATTN_MASK_DOCUMENT) return fail(ATTN_ERR_INVALID_ARG, "unknown mask kind");

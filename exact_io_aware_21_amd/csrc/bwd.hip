@@ -323,7 +323,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
               (PRIV ? kGroupShift - (r & 3) * 1024 : 0);
   auto fill = [&](int qs, int stage) {
     const int q0 = qs * QS;
-    const int rows_left = max(N - q0, 0);  // 0 past the last step: the copies read nothing
+    // rows of this step (0 past the last step: the copies read nothing), so that the tiles'
+    // byte count stays far below 2^31 for every N
+    const int rows_left = min(max(N - q0, 0), QS);
     uint16_t *dst = &stages[stage * STAGE];
     if constexpr (PRIV)
       copy_tiles_to_lds_grouped<NRR, NJR>(a.q + hbase + (size_t)q0 * D,
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     // L and D of the 32 queries: one 4-byte-per-lane copy each (lanes 32..63 land in the unused
     // upper half of the 64-float slot).
     if (PRIV || wave == 0)
-      copy_rows4_to_lds(a.lse + (size_t)bh * N + q0, a.dvec + (size_t)bh * N + q0, rows_left * 4,
+      copy_rows4_to_lds(a.lse + (size_t)bh * N + q0, a.dvec + (size_t)bh * N + q0, max(N - q0, 0) * 4,
                         &dst[2 * TILE], lane * 4);
   };
   int tro[2];
@@ -572,7 +574,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     voff[r] = (pi_key(row) * D + (ch < D / 8 ? ch : D / 8 - 1) * 8) * 2;
   }
   auto fill = [&](int kt, int stage) {
-    const int keys_left = N - kt * kBc;  // >= 1
+    const int keys_left = min(N - kt * kBc, kBc);  // keys of this tile, >= 1
     const size_t off = hbase + (size_t)kt * kBc * D;
     copy_tiles_to_lds<NRK, NJK, 8>(a.k + off, a.v + off, keys_left * D * 2, &lds[stage * STAGE],
                                 wave, voff);

@@ -662,7 +662,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs &a) {
         dvo[r] = pi_key(row) * KROW + min(ch, KCHR - 1) * 16;
       } else {
         const int sl = (g - NJK) * 64 + lane, row = sl / SPV, ch = sl % SPV;
-        dvo[r] = row * a.Npad * 2 + min(ch, VCH - 1) * 16;  // < 2^31: row < D, Npad <= 2^24
+        // < 2^31: row < DV, Npad <= 2^24 for DV = 64 and <= 2^23 for DV = 128 (attn_fwd's limits)
+        dvo[r] = row * a.Npad * 2 + min(ch, VCH - 1) * 16;
       }
     }
     // Copy item r of pair (K tile ktk, V^T tile ktv) into buffer buf; vzero: write zeros in

@@ -98,7 +98,7 @@ typedef struct {
  *   q, k, v : device, bf16, [B][H][N][d] row-major (d contiguous), 16-byte aligned.
  *   o       : device, [B][H][N][d], bf16 or fp32 per params->o_dtype, 16-byte aligned.
  *   lse     : device, fp32 [B][H][N], the natural-log L; NULL skips it.
- *   B, H, N : >= 1, N <= 2^24, B*H*ceil(N/Br) < 2^31.
+ *   B, H, N : >= 1, N <= 2^24 (2^23 for d 128 and 256), B*H*ceil(N/Br) < 2^31.
  *   d       : 64, 128 or 256 (ATTN_PREC_FP8: 64 or 128).
  *   scale   : finite (1/sqrt(d) for the standard scaling).
  *   variant : one mask kind, optionally OR-ed with ATTN_MOD_ALIBI and/or ATTN_MOD_SOFTCAP, or

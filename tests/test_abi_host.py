@@ -86,6 +86,8 @@ def _call_fwd(q=16, k=16, v=16, o=16, lse=None, B=1, H=1, N=64, d=64, scale=0.12
     ({"N": 0}, attn.ATTN_ERR_INVALID_ARG),
     ({"B": -1}, attn.ATTN_ERR_INVALID_ARG),
     ({"N": (1 << 24) + 1}, attn.ATTN_ERR_INVALID_ARG),
+    ({"N": (1 << 23) + 1, "d": 128}, attn.ATTN_ERR_INVALID_ARG),  # 32-bit V^T tile offsets
+    ({"N": (1 << 23) + 1, "d": 256}, attn.ATTN_ERR_INVALID_ARG),
     ({"d": 32}, attn.ATTN_ERR_INVALID_ARG),
     ({"scale": float("inf")}, attn.ATTN_ERR_INVALID_ARG),
     ({"scale": float("nan")}, attn.ATTN_ERR_INVALID_ARG),
