@@ -1,4 +1,5 @@
-"""Every row of every head of the four larger workloads against the fp64 oracle (C ABI, GPU).
+"""Every row of every head of the four larger workloads, and of one sanity shape, against the
+fp64 oracle (C ABI, GPU).
 
 The forward pass is run at full size in the launch the benchmark times (bf16 O) and with an fp32
 O (the same kernel up to the store).  Element by element, on every (batch, head, row):
@@ -52,10 +53,20 @@ def half_ulp_bf16(x):
     return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
 
 
-@pytest.mark.parametrize("name", ["causal_b4h16_n2048_d128", "window1024_alibi_b2h32_n8192_d128",
-                                  "doc_softcap30_h16_n16384_d64", "causal_h32_n16384_d128"])
+# The four larger benchmark workloads, and the causal B=1 H=32 N=4096 d=128 shape of the usage
+# example on page "FlashAttention-3 y torch.compile ..." (section 4: a transformer block calling
+# the fused kernel with 32 heads of dimension 128 on 4096 positions, causal) as a sanity shape.
+SHAPES = {n: inputs.WORKLOADS[n] for n in ("causal_b4h16_n2048_d128",
+                                           "window1024_alibi_b2h32_n8192_d128",
+                                           "doc_softcap30_h16_n16384_d64",
+                                           "causal_h32_n16384_d128")}
+SHAPES["causal_h32_n4096_d128"] = inputs.Workload("causal_h32_n4096_d128", B=1, H=32, N=4096,
+                                                  d=128, mask="causal", seed=6)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
 def test_every_row_every_head(name):
-    w = inputs.WORKLOADS[name]
+    w = SHAPES[name]
     inp = inputs.make_inputs(w)
     o16, l16 = run(w, inp, out_f32=False)  # the launch the benchmark times
     o32, l32 = run(w, inp, out_f32=True)
