@@ -60,6 +60,9 @@ CASES = [
     ("dec_lq8_d128_p128", 2, 4, 8, 128, 128, 8, 2000, True),
     ("dec_lq2_none_d128_p256", 2, 2, 2, 128, 256, 300, 5000, False),
     ("dec_long_d128_p64", 2, 2, 1, 128, 64, 30000, 40000, True),
+    # 64 splits per sequence-head (B*H = 128, 16k table): the single-wave merge at its largest,
+    # four chunks of 16 splits, with several query rows and one column per lane (d = 64)
+    ("dec_ns64_lq4_d64_p32", 8, 16, 4, 64, 32, 8000, 16384, True),
 ]
 
 
