@@ -139,37 +139,6 @@ __device__ __forceinline__ void copy_tiles_to_lds(const void *x, const void *y, 
   }
 }
 
-// The same copies for a wave that fills whole tiles alone (NW = 1), with one LDS base (M0) per
-// group of 4 instructions instead of one per instruction: the immediate offset of a
-// buffer-to-LDS load is added to both the global and the LDS address, so instruction r takes
-// the group base plus (r % 4) KB as its immediate.  The resources start kGroupShift bytes before
-// x and y and the per-lane offsets are voffs[r] = voff + kGroupShift - (r % 4) KB (>= 0), so
-// every address, and the bound check, is what the plain copies compute.
-constexpr int kGroupShift = 3072;
-template <int NR, int NJ>
-__device__ __forceinline__ void copy_tiles_to_lds_grouped(const void *x, const void *y, int bytes,
-                                                          uint16_t *dst, const int *voffs) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  const auto rx = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)x - kGroupShift), 0,
-                                                    bytes + kGroupShift, kBufferWord3);
-  const auto ry = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)y - kGroupShift), 0,
-                                                    bytes + kGroupShift, kBufferWord3);
-#pragma unroll
-  for (int g = 0; g < (NR + 3) / 4; ++g) {
-    const int n = NR - 4 * g;  // instructions in this group (compile-time after unrolling)
-    lds_void *bx = (lds_void *)&dst[4 * g * 64 * 8], *by = (lds_void *)&dst[(NJ + 4 * g) * 64 * 8];
-    const int *v = &voffs[4 * g];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, bx, 16, v[0], 0, 0, 0);
-    if (n > 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, bx, 16, v[1], 0, 1024, 0);
-    if (n > 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, bx, 16, v[2], 0, 2048, 0);
-    if (n > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, bx, 16, v[3], 0, 3072, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, by, 16, v[0], 0, 0, 0);
-    if (n > 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, by, 16, v[1], 0, 1024, 0);
-    if (n > 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, by, 16, v[2], 0, 2048, 0);
-    if (n > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, by, 16, v[3], 0, 3072, 0);
-  }
-}
-
 // Buffer-to-LDS copy of two 4-byte-per-lane rows (bytes each, from x and y) into dst and
 // dst + 128 elements (64 floats each); loads past `bytes` read as zero.
 __device__ __forceinline__ void copy_rows4_to_lds(const float *x, const float *y, int bytes,
@@ -247,16 +216,14 @@ __device__ __forceinline__ void block_place(int kind, int N, int d, int &pos, in
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV: one workgroup = 4 waves x 32 keys of one (batch, head); query steps of 32 rows.
+// dK, dV for d = 64: one workgroup = 4 waves x 32 keys of one (batch, head); query steps of 32
+// rows.
 //
 // Each query step's Q and dO rows (32 pi-permuted rows of pitch RP each) and its L and D are
-// copied straight into LDS (buffer-to-LDS loads) one step ahead, double-buffered; the
-// transposed operands Q^T and dO^T of the dK and dV products are read from the same row tiles
-// with ds_read_b64_tr_b16.  For d = 128 every wave stages the step's tiles into LDS buffers of
-// its own (four copies of each tile, 148 KB): the waves then never wait for one another.  They
-// run one per SIMD, and a workgroup barrier at the end of every step (shared buffers) made each
-// step wait for the slowest of the four.  For d = 64 the workgroup shares one copy (21 KB) and
-// two workgroups fit a CU (two waves per SIMD), whose interleaving hides that wait.
+// copied straight into LDS (buffer-to-LDS loads) one step ahead, double-buffered, one copy for
+// the workgroup (21 KB); the transposed operands Q^T and dO^T of the dK and dV products are read
+// from the same row tiles with ds_read_b64_tr_b16.  Two workgroups fit a CU (two waves per SIMD),
+// whose interleaving hides the wait at the barrier that ends every step.
 template <int D, bool ALIBI, bool SOFTCAP, bool OUTF32>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NT = 256, NW = 4, QS = 32, KPW = 32;
@@ -266,9 +233,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NJR = (RSLOT + 63) / 64;          // wave instructions per row tile
   constexpr int TILE = NJR * 64 * 8;              // elements per row tile (with the spill-over)
   constexpr int STAGE = 2 * TILE + 2 * 64 * 2;    // Q, dO, then L and D (64 floats each)
-  constexpr bool PRIV = D > 64;                   // stages of its own for every wave
-  constexpr int NRR = PRIV ? NJR : (NJR + NW - 1) / NW;  // copy instructions per wave and tile
-  __shared__ __attribute__((aligned(16))) uint16_t lds[(PRIV ? NW : 1) * 2 * STAGE];
+  constexpr int NRR = (NJR + NW - 1) / NW;        // copy instructions per wave and tile
+  static_assert(D == 64, "d = 128 runs bwd_dkdv2_kernel");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS copy targets
@@ -314,30 +281,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 
   // Zero every stage once, so that no LDS byte is ever read unwritten.
   for (int i = tid; i < (int)(sizeof(lds) / 16); i += NT) *(u32x4 *)&lds[i * 8] = u32x4{0u, 0u, 0u, 0u};
-  uint16_t *const stages = PRIV ? &lds[wave * 2 * STAGE] : lds;  // the two stages this wave reads
-  const int cw = PRIV ? 0 : wave;  // copy instruction r of a tile: r * (PRIV ? 1 : NW) + cw
-  int voff[NRR];
+  uint16_t *const stages = lds;
+  int voff[NRR];  // copy instruction r of a tile: r * NW + wave
 #pragma unroll
-  for (int r = 0; r < NRR; ++r)
-    voff[r] = tile_slot_offset<D, RP, QS>(64 * (r * (PRIV ? 1 : NW) + cw) + lane) +
-              (PRIV ? kGroupShift - (r & 3) * 1024 : 0);
+  for (int r = 0; r < NRR; ++r) voff[r] = tile_slot_offset<D, RP, QS>(64 * (r * NW + wave) + lane);
   auto fill = [&](int qs, int stage) {
     const int q0 = qs * QS;
     // rows of this step (0 past the last step: the copies read nothing), so that the tiles'
     // byte count stays far below 2^31 for every N
     const int rows_left = min(max(N - q0, 0), QS);
     uint16_t *dst = &stages[stage * STAGE];
-    if constexpr (PRIV)
-      copy_tiles_to_lds_grouped<NRR, NJR>(a.q + hbase + (size_t)q0 * D,
-                                          a.dout + hbase + (size_t)q0 * D, rows_left * D * 2, dst,
-                                          voff);
-    else
-      copy_tiles_to_lds<NRR, NJR, NW>(a.q + hbase + (size_t)q0 * D,
-                                      a.dout + hbase + (size_t)q0 * D, rows_left * D * 2, dst, cw,
-                                      voff);
+    copy_tiles_to_lds<NRR, NJR, NW>(a.q + hbase + (size_t)q0 * D, a.dout + hbase + (size_t)q0 * D,
+                                    rows_left * D * 2, dst, wave, voff);
     // L and D of the 32 queries: one 4-byte-per-lane copy each (lanes 32..63 land in the unused
     // upper half of the 64-float slot).
-    if (PRIV || wave == 0)
+    if (wave == 0)
       copy_rows4_to_lds(a.lse + (size_t)bh * N + q0, a.dvec + (size_t)bh * N + q0, max(N - q0, 0) * 4,
                         &dst[2 * TILE], lane * 4);
   };
@@ -376,7 +334,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   __syncthreads();
   if (qs_begin < qs_end) fill(qs_begin, 0);
   __builtin_amdgcn_s_waitcnt(0);
-  if constexpr (!PRIV) __syncthreads();
+  __syncthreads();
   load_ops(0);
 
   for (int qs = qs_begin; qs < qs_end; ++qs) {
@@ -453,12 +411,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const int kk = i / (2 * NDB), d0 = (i >> 1) % NDB;
       dkt[d0] = mfma32(__builtin_bit_cast(bf16x8, fb[i]), db[kk], dkt[d0]);
     }
-    // The next step's operands: its copies (issued at the top of this step) have landed; with
-    // shared stages, after the barrier every wave's have, and every wave is done reading this
-    // stage (which the copies at the top of the next step overwrite).  After the last step the
-    // reads fetch unused data from the other stage.
+    // The next step's operands: its copies (issued at the top of this step) have landed; after
+    // the barrier every wave's have, and every wave is done reading this stage (which the
+    // copies at the top of the next step overwrite).  After the last step the reads fetch unused
+    // data from the other stage.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    if constexpr (!PRIV) __syncthreads();
+    __syncthreads();
     load_ops(stage ^ 1);
     __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // the P conversions
 #pragma unroll
@@ -479,6 +437,267 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     for (int d0 = 0; d0 < NDB; ++d0) {
       store16<OUTF32>(a.dk, off + 32 * d0, dkt[d0] * a.scale);
       store16<OUTF32>(a.dv, off + 32 * d0, dvt[d0]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK, dV for d = 128 with two waves per SIMD: one workgroup = 8 waves = 4 pairs x 32 keys of one
+// (batch, head).  Waves w and w + 4 (pair w % 4) share the keys; per 32-query step, role 0 forms
+// S = Q K^T, P and dV^T += dO^T P, role 1 forms dP = dO V^T, dS and dK^T += Q^T dS: 16 MFMAs each.
+// P (with the soft-cap factor) goes from role 0 to role 1 through LDS.  In the single-wave form
+// (bwd_dkdv_kernel, d = 64) one wave issues all 32 MFMAs of a step and every vector and LDS
+// instruction itself; here two waves share a SIMD, so one issues while the other waits, and role
+// 0's exponentials run beside its own dV products of the step before and beside role 1's
+// products.  The products, and the order in which each accumulator sums them, are those of the
+// single-wave form.
+// The workgroup shares the steps' Q, dO, L, D tiles in three LDS stages (one array each, so the
+// compiler tracks the copies into each separately; one copy of each tile per workgroup, where
+// private stages per wave took four), filled two steps ahead; each stage also holds the P of its
+// step.  Each role runs its own loop with one barrier per step: role 0 after writing P, role 1
+// after its dP products, both after waiting for their own copies.  Barrier s therefore orders:
+// P of step s written before it is read; step s + 1's tiles landed before they are read; the last
+// reads of step s - 1's stage (the dV operands of role 0 and the dK operands of role 1, both
+// before barrier s) before the copies of step s + 2 (issued after barrier s) overwrite it.
+template <int D, bool ALIBI, bool SOFTCAP, bool OUTF32>
+__global__ __launch_bounds__(512) void bwd_dkdv2_kernel(BwdArgs a) {
+  constexpr int NT = 512, NPAIR = 4, QS = 32, KPW = 32;
+  constexpr int NKS = D / 16, NDB = D / 32;     // k-steps of the score products; d blocks
+  constexpr int RP = pitch(D);                  // LDS pitch of a Q / dO row
+  constexpr int RSLOT = QS * (RP / 8);          // 16-byte slots of a row tile
+  constexpr int NJR = (RSLOT + 63) / 64;        // wave instructions per row tile
+  constexpr int TILE = NJR * 64 * 8;            // elements per row tile (with the spill-over)
+  constexpr int NRR = (NJR + 7) / 8;            // copy instructions per wave and tile (at most)
+  constexpr int XF = SOFTCAP ? 2 : 1;           // vectors role 0 sends: P, the soft-cap factor
+  constexpr int XOFF = 2 * TILE + 2 * 64 * 2;   // Q, dO, then L and D (64 floats each), then P
+  constexpr int STAGE = XOFF + NPAIR * XF * 1024 * 2;  // P: [pair][vector][4 groups][64 lanes][4]
+  static_assert(D == 128, "the paired kernel is written for d = 128");
+  __shared__ __attribute__((aligned(16))) uint16_t st0[STAGE], st1[STAGE], st2[STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS copy targets
+  const int pair = wave & 3, role = wave >> 2;
+  int kx, bh;
+  block_place(a.kind, a.N, D, kx, bh);  // key blocks: the first ones see the most queries
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int N = a.N;
+  const int key0 = kx * (NPAIR * KPW);
+  const int j = key0 + pair * KPW + l32;  // this lane's key
+  const bool j_ok = j < N;
+  const MaskDesc md{a.kind, N, a.window, a.offs ? a.offs + (size_t)b * (a.max_docs + 1) : nullptr,
+                    a.max_docs};
+  int qlo = 1, qhi = 0;  // queries allowed to attend to key j (empty past N)
+  if (j_ok) {
+    qlo = col_lo(md, j);
+    qhi = col_hi(md, j);
+  }
+  const int jl = min(key0 + NPAIR * KPW, N) - 1;
+  const int qs_begin = __builtin_amdgcn_readfirstlane(col_lo(md, key0) / QS);
+  const int qs_end = __builtin_amdgcn_readfirstlane(col_hi(md, jl) / QS + 1);
+
+  const size_t hbase = (size_t)bh * N * D;
+  const float slopeL = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+  bf16x8 bop[NKS];  // B operand: K^T (role 0) or V^T (role 1) of this lane's key
+  {
+    const uint16_t *src = (role ? a.v : a.k) + hbase + (size_t)(j_ok ? j : 0) * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (j_ok) x = *(const u32x4 *)(src + ks * 16);
+      bop[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  f32x16 acc4[NDB];  // dV^T (role 0) or dK^T (role 1), column block d0
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc4[i] = f32x16{};
+
+  // Zero the stages once, so that no LDS byte is ever read unwritten.
+  for (int i = tid; i < STAGE / 8; i += NT) {
+    *(u32x4 *)&st0[i * 8] = u32x4{0u, 0u, 0u, 0u};
+    *(u32x4 *)&st1[i * 8] = u32x4{0u, 0u, 0u, 0u};
+    *(u32x4 *)&st2[i * 8] = u32x4{0u, 0u, 0u, 0u};
+  }
+  int voff[NRR];
+#pragma unroll
+  for (int r = 0; r < NRR; ++r) voff[r] = tile_slot_offset<D, RP, QS>(64 * (r * 8 + wave) + lane);
+  auto fill = [&](int qs, uint16_t *dst) __attribute__((always_inline)) {
+    const int q0 = qs * QS;
+    // rows of this step, so that the tiles' byte count stays far below 2^31 for every N
+    // (read into scalars: the buffer descriptors they enter must be wave-uniform)
+    const int rows = __builtin_amdgcn_readfirstlane(min(max(N - q0, 0), QS));
+    const int left = __builtin_amdgcn_readfirstlane(max(N - q0, 0));
+    copy_tiles_to_lds<NRR, NJR, 8>(a.q + hbase + (size_t)q0 * D, a.dout + hbase + (size_t)q0 * D,
+                                   rows * D * 2, dst, wave, voff);
+    // L and D of the 32 queries (lanes 32..63 land in the unused upper half of each slot)
+    if (wave == 0)
+      copy_rows4_to_lds(a.lse + (size_t)bh * N + q0, a.dvec + (size_t)bh * N + q0, left * 4,
+                        &dst[2 * TILE], lane * 4);
+  };
+  int tro[2];
+  tr_base<RP>(lane, tro);
+  auto stage = [&](auto sc) __attribute__((always_inline)) -> uint16_t * {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return st0;
+    else if constexpr (S == 1) return st1;
+    else return st2;
+  };
+  // This lane's slot of vector v of the pair's P block (conflict-free 16-byte writes and reads).
+  auto xslot = [&](uint16_t *st, int v, int g) __attribute__((always_inline)) -> float * {
+    return (float *)&st[XOFF] + ((pair * XF + v) * 4 + g) * 256 + lane * 4;
+  };
+  // The score-product operand rows (Q for role 0, dO for role 1) of a stage, k-step ks:
+  // accumulator register r (row 8(r/4) + 4 hf + r%4 of the pi-permuted tile) is query
+  // q0 + 16(r/8) + 8 hf + r%8, column = key j.
+  auto scores = [&](const uint16_t *rows) __attribute__((always_inline)) -> f32x16 {
+    const uint16_t *ra = rows + lds_row(l32) * RP + hf * 8;
+    u32x4 fa[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) fa[ks] = *(const u32x4 *)(ra + ks * 16);
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) acc = mfma32(__builtin_bit_cast(bf16x8, fa[ks]), bop[ks], acc);
+    return acc;
+  };
+  // acc4[d0] += X^T F over the 32 queries (two 16-row halves kk), X = dO (role 0) or Q (role 1).
+  auto accumulate = [&](const uint16_t *x, const bf16x8 (&f)[2]) __attribute__((always_inline)) {
+    u32x4 fb[2][NDB];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int d0 = 0; d0 < NDB; ++d0) fb[kk][d0] = tr_frag(x, tro, 16 * kk * RP + 32 * d0);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int d0 = 0; d0 < NDB; ++d0)
+        acc4[d0] = mfma32(__builtin_bit_cast(bf16x8, fb[kk][d0]), f[kk], acc4[d0]);
+  };
+  auto to_bf16 = [&](const float (&v)[16], bf16x8 (&o)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      f32x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = v[8 * kk + e];
+      o[kk] = __builtin_convertvector(x, bf16x8);
+    }
+  };
+  // Each wave's copies landed, then the barrier (with the workgroup fence: the P writes before
+  // it, the P reads after it); then the copies of step qs + 2.
+  auto sync_and_fill = [&](int qs, uint16_t *next) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (qs + 2 < qs_end) fill(qs + 2, next);
+  };
+
+  // Role 0, step qs from stage S: S, then dV of step qs - 1 (its stage, the one before S, is
+  // overwritten only by the copies after this step's barrier) while P is formed and written to
+  // the stage's P block.  pbp holds the previous step's P in bf16; before the first step it is
+  // zero and the stage before is the zero-filled st2, so that first product adds exact zeros.
+  bf16x8 pbp[2] = {};
+  auto step0 = [&](int qs, auto sc) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
+    uint16_t *st = stage(IntC<S>{});
+    const float *sL = (const float *)(st + 2 * TILE);
+    const int q0 = qs * QS;
+    const f32x16 acc = scores(st);
+    accumulate(stage(IntC<(S + 2) % 3>{}) + TILE, pbp);  // dV^T += dO^T P, step qs - 1
+    f32x4 l2v[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) l2v[aa] = *(const f32x4 *)&sL[16 * (aa >> 1) + 8 * hf + 4 * (aa & 1)];
+    float p[16], dc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int aa = r >> 2, bb = r & 3;
+      // key - query distance: the step's base plus this register's offset, exact in float
+      const float dji = (float)(j - q0 - 8 * hf) - (float)(16 * (aa >> 1) + 4 * (aa & 1) + bb);
+      const float t = score2f<ALIBI, SOFTCAP>(a, acc[r], slopeL, dji, dc[r]);
+      p[r] = __builtin_amdgcn_exp2f(fmaf(-kLog2e, l2v[aa][bb], t));  // L is natural-log
+    }
+    // Element mask only when some key of this wave does not take all 32 queries of the step.
+    if (__builtin_amdgcn_ballot_w64(!(qlo <= q0 && qhi >= q0 + QS - 1))) {
+      keep_branch();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int aa = r >> 2, bb = r & 3;
+        const int i = q0 + 16 * (aa >> 1) + 8 * hf + 4 * (aa & 1) + bb;
+        if (i < qlo || i > qhi) p[r] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      *(f32x4 *)xslot(st, 0, g) = f32x4{p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+      if constexpr (SOFTCAP)
+        *(f32x4 *)xslot(st, XF - 1, g) = f32x4{dc[4 * g], dc[4 * g + 1], dc[4 * g + 2], dc[4 * g + 3]};
+    }
+    to_bf16(p, pbp);
+    sync_and_fill(qs, stage(IntC<(S + 2) % 3>{}));
+  };
+  // Role 1, step qs from stage S: dP, the barrier, then dS (with the P role 0 wrote) and dK.
+  auto step1 = [&](int qs, auto sc) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
+    uint16_t *st = stage(IntC<S>{});
+    const float *sDv = (const float *)(st + 2 * TILE) + 64;
+    const f32x16 dp = scores(st + TILE);
+    sync_and_fill(qs, stage(IntC<(S + 2) % 3>{}));
+    float ds[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 pv = *(const f32x4 *)xslot(st, 0, g);
+      const f32x4 dv4 = *(const f32x4 *)&sDv[16 * (g >> 1) + 8 * hf + 4 * (g & 1)];
+      f32x4 dc = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (SOFTCAP) dc = *(const f32x4 *)xslot(st, XF - 1, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ds[4 * g + e] = pv[e] * (dp[4 * g + e] - dv4[e]) * dc[e];
+    }
+    bf16x8 db[2];
+    to_bf16(ds, db);
+    accumulate(st, db);  // dK^T += Q^T dS
+  };
+
+  // Settle the loads above and the zero fill before the first copies land.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (qs_begin < qs_end) fill(qs_begin, st0);
+  if (qs_begin + 1 < qs_end) fill(qs_begin + 1, st1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // Whole triples of steps in the loop (one exit, so the accumulators stay in place), then the
+  // last one or two steps.
+  int qs = qs_begin;
+  if (role == 0) {
+    for (; qs + 3 <= qs_end; qs += 3) {
+      step0(qs, IntC<0>{});
+      step0(qs + 1, IntC<1>{});
+      step0(qs + 2, IntC<2>{});
+    }
+    // dV of the last step, from its stage (no copies follow it)
+    if (qs + 1 < qs_end) {
+      step0(qs, IntC<0>{});
+      step0(qs + 1, IntC<1>{});
+      accumulate(st1 + TILE, pbp);
+    } else if (qs < qs_end) {
+      step0(qs, IntC<0>{});
+      accumulate(st0 + TILE, pbp);
+    } else if (qs_begin < qs_end) {
+      accumulate(st2 + TILE, pbp);
+    }
+  } else {
+    for (; qs + 3 <= qs_end; qs += 3) {
+      step1(qs, IntC<0>{});
+      step1(qs + 1, IntC<1>{});
+      step1(qs + 2, IntC<2>{});
+    }
+    if (qs < qs_end) step1(qs, IntC<0>{});
+    if (qs + 1 < qs_end) step1(qs + 1, IntC<1>{});
+  }
+
+  if (j_ok) {
+    const size_t off = hbase + (size_t)j * D + 16 * hf;
+#pragma unroll
+    for (int d0 = 0; d0 < NDB; ++d0) {
+      if (role)
+        store16<OUTF32>(a.dk, off + 32 * d0, acc4[d0] * a.scale);
+      else
+        store16<OUTF32>(a.dv, off + 32 * d0, acc4[d0]);
     }
   }
 }
@@ -687,8 +906,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
 template <int D, bool ALIBI, bool SOFTCAP, bool OUTF32>
 hipError_t launch_bwd_inst(const BwdArgs &a, hipStream_t s) {
   const unsigned BH = (unsigned)(a.B * a.H);
-  bwd_dkdv_kernel<D, ALIBI, SOFTCAP, OUTF32>
-      <<<dim3((unsigned)((a.N + 127) / 128), BH), 256, 0, s>>>(a);
+  if constexpr (D == 128)
+    bwd_dkdv2_kernel<D, ALIBI, SOFTCAP, OUTF32>
+        <<<dim3((unsigned)((a.N + 127) / 128), BH), 512, 0, s>>>(a);
+  else
+    bwd_dkdv_kernel<D, ALIBI, SOFTCAP, OUTF32>
+        <<<dim3((unsigned)((a.N + 127) / 128), BH), 256, 0, s>>>(a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   bwd_dq_kernel<D, ALIBI, SOFTCAP, OUTF32><<<dim3((unsigned)a.n_qt, BH), 512, 0, s>>>(a);
   return hipGetLastError();
