@@ -292,6 +292,45 @@ __global__ __launch_bounds__(256) void lds_rate(float *out, float seed) {
   if (acc[0] + acc[1] + acc[2] + acc[3] == 1234.5f) out[threadIdx.x] = acc[0];
 }
 
+// ds_read_b64_tr_b16 (the transposing 8-byte read) with the backward kernels' operand pattern:
+// a 32-row tile of pitch 272 bytes, rows placed with index bits 0-1 and 2-3 swapped; per
+// iteration 16 reads = the 8 transposed 32x16 fragments of a 32 x 128 tile (two 16-row halves x
+// four 32-column blocks), alternating between two tiles.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+__global__ __launch_bounds__(256) void lds_tr_rate(float *out, float seed) {
+  constexpr int P = 136;  // row pitch in 2-byte elements
+  __shared__ __attribute__((aligned(16))) unsigned short lds[2 * 32 * P];
+  for (int i = threadIdx.x; i < 2 * 32 * P; i += 256) lds[i] = (unsigned short)(seed * i);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 3, m = (lane >> 2) & 3, g = lane >> 4;
+  const int col = 16 * (q & 1) + 8 * (g & 1) + 4 * (q >> 1);
+  int off[2];
+  for (int u = 0; u < 2; ++u) {
+    int r = 8 * (g >> 1) + m + 4 * u;                  // row before the two placements
+    r = (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1);  // pi: bits 2 and 3 swapped
+    r = (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3);   // LDS placement: bit pairs 0-1, 2-3 swapped
+    off[u] = r * P + col;  // <= 15 * 136 + 28; with the offsets below < 32 * 136 per tile
+  }
+  int acc = 0;
+  for (int it = 0; it < 2 * kIters; ++it) {
+    asm volatile("" ::: "memory");  // the reads are loop-invariant: force them every iteration
+    const unsigned short *t = &lds[(it & 1) * 32 * P];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int d0 = 0; d0 < 4; ++d0)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16 *)&t[off[u] + 16 * kk * P + 32 * d0]);
+          acc += v[0] ^ v[1] ^ v[2] ^ v[3];
+        }
+  }
+  if (acc == 12345) out[threadIdx.x] = (float)acc;
+}
+
 // Read-only stream: 8 independent 16-byte loads in flight per lane, XOR-folded.
 __global__ __launch_bounds__(256) void read_kernel(const f32x4 *__restrict__ src, size_t n,
                                                    float *out) {
@@ -475,6 +514,13 @@ int main() {
     const float ms = time_ms([&] { lds_rate<<<grid, 256>>>(out, seed); }, 5);
     const double bytes = (double)grid * 256 * 2 * kIters * 8 * 16;
     printf("LDS ds_read_b128: %.1f TB/s = %.1f B/clk/CU at 2.4 GHz\n", bytes / ms / 1e9,
+           bytes / (ms * 1e-3) / 2.4e9 / cus);
+  }
+  {
+    const int grid = cus * 2 * 8;
+    const float ms = time_ms([&] { lds_tr_rate<<<grid, 256>>>(out, seed); }, 5);
+    const double bytes = (double)grid * 256 * 2 * kIters * 16 * 8;
+    printf("LDS ds_read_b64_tr_b16: %.1f TB/s = %.1f B/clk/CU at 2.4 GHz\n", bytes / ms / 1e9,
            bytes / (ms * 1e-3) / 2.4e9 / cus);
   }
   {
