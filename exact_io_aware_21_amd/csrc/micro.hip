@@ -297,6 +297,7 @@ __global__ __launch_bounds__(256) void lds_rate(float *out, float seed) {
 // iteration 16 reads = the 8 transposed 32x16 fragments of a 32 x 128 tile (two 16-row halves x
 // four 32-column blocks), alternating between two tiles.
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 __global__ __launch_bounds__(256) void lds_tr_rate(float *out, float seed) {
   constexpr int P = 136;  // row pitch in 2-byte elements
@@ -329,6 +330,75 @@ __global__ __launch_bounds__(256) void lds_tr_rate(float *out, float seed) {
         }
   }
   if (acc == 12345) out[threadIdx.x] = (float)acc;
+}
+
+// Do LDS reads and MFMAs overlap?  Eight waves per CU (two per SIMD), each iteration a wave
+// issues 8 MFMAs (4 accumulator chains; operands in registers) and/or 8 KB of LDS reads whose
+// results no MFMA uses: TR = 16 ds_read_b64_tr_b16 with the backward kernels' addresses, else
+// 8 ds_read_b128 of 16-byte row chunks.  MODE 1: MFMAs only, 2: reads only, 3: both, the
+// reads issued before the MFMAs of the iteration.  Core cycles per iteration: if the two
+// overlap, MODE 3 takes the longer of MODE 1 and 2; if not, their sum.
+template <int MODE, bool TR>
+__global__ __launch_bounds__(512) void lds_mfma_cycles(float *out, u64 *cyc, float seed) {
+  constexpr int P = 136;
+  __shared__ __attribute__((aligned(16))) unsigned short lds[2 * 32 * P];
+  for (int i = threadIdx.x; i < 2 * 32 * P; i += 512) lds[i] = (unsigned short)(seed * i);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane & 3, m = (lane >> 2) & 3, g = lane >> 4;
+  const int col = 16 * (q & 1) + 8 * (g & 1) + 4 * (q >> 1);
+  int off[2];
+  for (int u = 0; u < 2; ++u) {
+    int r = 8 * (g >> 1) + m + 4 * u;
+    r = (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1);
+    r = (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3);
+    off[u] = r * P + col;  // as in lds_tr_rate: every read stays inside its 32 x 136 tile
+  }
+  const int roff = (lane & 31) * P + (lane >> 5) * 8;  // row reads: <= 31 * 136 + 8 + 7 * 16 + 7
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(seed * (threadIdx.x + i));
+    b[i] = (__bf16)(seed * (i + 1));
+  }
+  f32x16 c[4] = {};
+  int acc = 0;
+  const u64 t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < kIters; ++it) {
+    asm volatile("" ::: "memory");
+    const unsigned short *t = &lds[(it & 1) * 32 * P];
+    if constexpr (MODE & 2) {
+      if constexpr (TR) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int d0 = 0; d0 < 4; ++d0)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_v4i16 *)&t[off[u] + 16 * kk * P + 32 * d0]);
+              acc += v[0] ^ v[1] ^ v[2] ^ v[3];
+            }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const v8i16 v = *(const v8i16 *)&t[roff + 16 * k];  // 16-byte aligned
+          acc += v[0] ^ v[1] ^ v[2] ^ v[3] ^ v[4] ^ v[5] ^ v[6] ^ v[7];
+        }
+      }
+    }
+    if constexpr (MODE & 1) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm)
+          c[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[mm], 0, 0, 0);
+    }
+  }
+  const u64 dt = __builtin_amdgcn_s_memtime() - t0;
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += c[0][i] + c[1][i] + c[2][i] + c[3][i];
+  if (s == 1234.5f || acc == 12345) out[threadIdx.x] = s;
+  if (lane == 0) cyc[blockIdx.x * 8 + wave] = dt;
 }
 
 // Read-only stream: 8 independent 16-byte loads in flight per lane, XOR-folded.
@@ -522,6 +592,18 @@ int main() {
     const double bytes = (double)grid * 256 * 2 * kIters * 16 * 8;
     printf("LDS ds_read_b64_tr_b16: %.1f TB/s = %.1f B/clk/CU at 2.4 GHz\n", bytes / ms / 1e9,
            bytes / (ms * 1e-3) / 2.4e9 / cus);
+  }
+  {
+    // one 8-wave workgroup per CU; cycles per iteration (median over the waves)
+    const int grid = cus;
+    auto per = [&](auto launch) { return median_cycles(launch, cyc, grid * 8) / kIters; };
+    printf("2 wave/SIMD, core cycles per iteration of 8 MFMAs and/or 8 KB of LDS reads per wave: "
+           "MFMA %.0f; ds_read_b64_tr_b16 %.0f, both %.0f; ds_read_b128 %.0f, both %.0f\n",
+           per([&] { lds_mfma_cycles<1, true><<<grid, 512>>>(out, cyc, seed); }),
+           per([&] { lds_mfma_cycles<2, true><<<grid, 512>>>(out, cyc, seed); }),
+           per([&] { lds_mfma_cycles<3, true><<<grid, 512>>>(out, cyc, seed); }),
+           per([&] { lds_mfma_cycles<2, false><<<grid, 512>>>(out, cyc, seed); }),
+           per([&] { lds_mfma_cycles<3, false><<<grid, 512>>>(out, cyc, seed); }));
   }
   {
     const size_t n = (size_t)1 << 26;  // 1 GiB of f32x4
