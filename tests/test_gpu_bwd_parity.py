@@ -99,6 +99,12 @@ CASES = [
     # shares that are not whole heads with a tail past the last multiple of 8 blocks
     ("b_place_grp2_causal_d64", 2, 8, 512, 64, "causal", 0, False, 0.0, 1.0),
     ("b_place_tail_causal_d128", 3, 5, 700, 128, "causal", 0, False, 0.0, 1.0),
+    # the d = 128 dK/dV kernel walks 32-query steps in whole triples (three LDS stages) and
+    # then one or two more: 2 steps (no triple), 3 (one triple, no tail), and up to 5 steps
+    # per key block under the causal mask (a triple and two more)
+    ("b_n64_none_d128", 1, 2, 64, 128, "none", 0, False, 0.0, 1.0),
+    ("b_n96_none_alibi_d128", 1, 2, 96, 128, "none", 0, True, 0.0, 1.0),
+    ("b_n160_causal_d128", 2, 2, 160, 128, "causal", 0, False, 0.0, 1.0),
 ]
 
 
