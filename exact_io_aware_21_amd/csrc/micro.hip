@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256) void lds_tr_rate(float *out, float seed) {
 // 8 ds_read_b128 of 16-byte row chunks.  MODE 1: MFMAs only, 2: reads only, 3: both, the
 // reads issued before the MFMAs of the iteration.  Core cycles per iteration: if the two
 // overlap, MODE 3 takes the longer of MODE 1 and 2; if not, their sum.
-template <int MODE, bool TR>
+template <int MODE, bool TR, bool AGPR = false>
 __global__ __launch_bounds__(512) void lds_mfma_cycles(float *out, u64 *cyc, float seed) {
   constexpr int P = 136;
   __shared__ __attribute__((aligned(16))) unsigned short lds[2 * 32 * P];
@@ -390,8 +390,12 @@ __global__ __launch_bounds__(512) void lds_mfma_cycles(float *out, u64 *cyc, flo
 #pragma unroll
       for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm)
-          c[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[mm], 0, 0, 0);
+        for (int mm = 0; mm < 4; ++mm) {
+          if constexpr (AGPR)  // accumulators held in AGPRs (the MFMA result form before gfx90a)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c[mm]) : "v"(a), "v"(b));
+          else
+            c[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[mm], 0, 0, 0);
+        }
     }
   }
   const u64 dt = __builtin_amdgcn_s_memtime() - t0;
@@ -604,6 +608,11 @@ int main() {
            per([&] { lds_mfma_cycles<3, true><<<grid, 512>>>(out, cyc, seed); }),
            per([&] { lds_mfma_cycles<2, false><<<grid, 512>>>(out, cyc, seed); }),
            per([&] { lds_mfma_cycles<3, false><<<grid, 512>>>(out, cyc, seed); }));
+    printf("  the same with the MFMA accumulators in AGPRs: MFMA %.0f; ds_read_b64_tr_b16 both %.0f; "
+           "ds_read_b128 both %.0f\n",
+           per([&] { lds_mfma_cycles<1, true, true><<<grid, 512>>>(out, cyc, seed); }),
+           per([&] { lds_mfma_cycles<3, true, true><<<grid, 512>>>(out, cyc, seed); }),
+           per([&] { lds_mfma_cycles<3, false, true><<<grid, 512>>>(out, cyc, seed); }));
   }
   {
     const size_t n = (size_t)1 << 26;  // 1 GiB of f32x4
